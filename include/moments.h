@@ -1,0 +1,114 @@
+/*
+ * moments.h - C ABI of the MI355X (gfx950) physical-frame state-moments library.
+ *
+ * The operation (burn-mamba "recalculated.rs" source page, moments_phys_fwd and
+ * the Mamba3MomentsBackendExt trait; "backward.rs" source page, module doc
+ * "Gradient math" and moments_phys_bwd):
+ *
+ *   per (b,h) chain, with V = min(valid_len, s), decays da <= 0 typical,
+ *     h~[t] = exp(da_t) h~[t-1] + sum_c xhat[t,c] (outer) bhat[t,c],  h~[-1] = h0
+ *   computed chunkwise: a = inclusive cumsum of da inside a chunk,
+ *     h~[t] = exp(a_t) h_- + sum_{j<=t,c} exp(a_t - a_j) xhat[j,c] (outer) bhat[j,c]
+ *   then de-rotated along the state-rank axis, c_t = M_t h~[t] row by row:
+ *     complex pairwise : pairs (2i, 2i+1), i < rope_dim/2, angle rot[b,t,h,i],
+ *                        (x, y) -> (cos x + sin y, -sin x + cos y)     (R(-theta))
+ *     complex half     : pairs (i, r/2 + i), same 2x2 block
+ *     quaternion       : 4-blocks 4j..4j+3, j < quat_blocks, left Hamilton
+ *                        product by Q = rot[b,t,h,j,:] = (w,x,y,z)
+ *     coordinates outside the rotated width pass through unchanged;
+ *   and the masked moments over t < V:
+ *     m2[b,h]     = sum_t c_t^T c_t                       ([r, r])
+ *     m1[b,h,p,:] = sum_t c_t[p, :]                       ([p, r], per state row)
+ *   The pages' pooled first moment m1[b,h,r] is m1.sum over p; its cotangent is
+ *   d_m1 broadcast over p.
+ *
+ * moments_bwd returns the vector-Jacobian product of (m2, m1) with cotangents
+ * (d_m2, d_m1) with respect to xhat, bhat, da, rot (the cumulative angles or
+ * quaternions, unconstrained) and h0. Gradients at positions t >= V are exactly
+ * zero. Nothing is kept between calls: the backward recomputes the states.
+ *
+ * Layouts: every tensor is dense row-major (C order), device memory, aligned to
+ * at least 16 bytes:
+ *   xhat[b,s,c,h,p]  bhat[b,s,c,h,r]  da[b,s,h]
+ *   rot[b,s,h,rope_dim/2] (complex) | rot[b,s,h,quat_blocks,4] (quaternion)
+ *   h0[b,h,p,r]  m2[b,h,r,r]  m1[b,h,p,r]  d_m2[b,h,r,r]  d_m1[b,h,p,r]
+ * The five float inputs share one dtype (desc->dtype); gradients are written in
+ * that dtype; m2, m1, d_m2 and d_m1 are float32. Arithmetic accumulates in fp32.
+ *
+ * Ownership: the caller allocates every buffer, including the workspace, and
+ * keeps them alive until the work queued on `stream` (a hipStream_t, NULL = the
+ * default stream) has finished. The library allocates no device memory, keeps
+ * no state between calls, and fully overwrites every output it is given.
+ *
+ * Errors: functions return 0 on success or a negative MOMENTS_E* code; nothing
+ * is launched when a call fails validation. moments_strerror() names a code;
+ * moments_last_hip_error() returns the hipError_t behind MOMENTS_EHIP.
+ */
+#ifndef MOMENTS_H
+#define MOMENTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOMENTS_OK = 0,
+  MOMENTS_EINVAL = -1,     /* bad descriptor, NULL required pointer, misalignment */
+  MOMENTS_ENOTSUP = -2,    /* shape outside what the compiled kernels cover */
+  MOMENTS_EWORKSPACE = -3, /* workspace_bytes below moments_workspace_size() */
+  MOMENTS_EHIP = -4        /* a HIP launch or runtime call failed */
+};
+
+typedef enum { MOMENTS_F32 = 0, MOMENTS_BF16 = 1 } moments_dtype;
+
+typedef enum {
+  MOMENTS_ROT_NONE = 0,
+  MOMENTS_ROT_COMPLEX_PAIRWISE = 1,
+  MOMENTS_ROT_COMPLEX_HALF = 2,
+  MOMENTS_ROT_QUATERNION = 3
+} moments_rot_kind;
+
+typedef struct {
+  int64_t b, s, c, h, p, r; /* batch, sequence, channels, heads, rows, state rank */
+  int64_t chunk_len;        /* the caller's chunk length l: 1 <= l, s % l == 0 */
+  int64_t valid_len;        /* positions >= valid_len are padding; >= s acts as s */
+  int32_t dtype;            /* moments_dtype */
+  int32_t rot_kind;         /* moments_rot_kind */
+  int64_t rope_dim;         /* complex modes: rotated coordinates, even, <= r */
+  int64_t quat_blocks;      /* quaternion mode: J, 4*J <= r */
+} moments_desc;
+
+/* Host-only check of a descriptor (no GPU needed). Returns 0, MOMENTS_EINVAL or
+ * MOMENTS_ENOTSUP. Supported: 1 <= r <= 128, 1 <= c <= 4, p >= 1, any s, b, h;
+ * half-split needs r even; rope_dim/2 <= r/2 there. */
+int moments_validate(const moments_desc* desc);
+
+/* Bytes of device workspace moments_fwd (is_bwd = 0) or moments_bwd (is_bwd = 1)
+ * needs for this descriptor, or a negative error code. */
+int64_t moments_workspace_size(const moments_desc* desc, int is_bwd);
+
+/* Forward: m2, m1 (float32) from the five inputs. rot may be NULL only for
+ * MOMENTS_ROT_NONE; h0 may be NULL (zero initial state). */
+int moments_fwd(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                const void* rot, const void* h0, float* m2, float* m1, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Backward: the VJP of (m2, m1) with cotangents d_m2 [b,h,r,r] (need not be
+ * symmetric; only d_m2 + d_m2^T enters) and d_m1 [b,h,p,r]. Any gradient
+ * pointer may be NULL (not wanted); d_rot must be NULL for MOMENTS_ROT_NONE. */
+int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                const void* rot, const void* h0, const float* d_m2, const float* d_m1,
+                void* d_xhat, void* d_bhat, void* d_da, void* d_rot, void* d_h0,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+const char* moments_strerror(int code);
+int moments_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOMENTS_H */

@@ -1,0 +1,73 @@
+"""ctypes binding of libmoments.so (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels; this module only builds
+the descriptor, allocates the workspace with torch and passes device pointers
+and torch's current HIP stream. It fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libmoments.so")
+
+OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+F32, BF16 = 0, 1
+ROT_NONE, ROT_PAIRWISE, ROT_HALF, ROT_QUAT = 0, 1, 2, 3
+
+EXPORTS = ("moments_validate", "moments_workspace_size", "moments_fwd", "moments_bwd",
+           "moments_strerror", "moments_last_hip_error")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("b", ctypes.c_int64), ("s", ctypes.c_int64), ("c", ctypes.c_int64),
+                ("h", ctypes.c_int64), ("p", ctypes.c_int64), ("r", ctypes.c_int64),
+                ("chunk_len", ctypes.c_int64), ("valid_len", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("rot_kind", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int64), ("quat_blocks", ctypes.c_int64)]
+
+
+class MomentsError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mamba_ssm_chunkwise_amd.build` (no CPU fallback exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        dp = ctypes.POINTER(Desc)
+        lib.moments_validate.argtypes = [dp]
+        lib.moments_validate.restype = ctypes.c_int
+        lib.moments_workspace_size.argtypes = [dp, ctypes.c_int]
+        lib.moments_workspace_size.restype = ctypes.c_int64
+        lib.moments_fwd.argtypes = [dp] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
+        lib.moments_fwd.restype = ctypes.c_int
+        lib.moments_bwd.argtypes = [dp] + [vp] * 12 + [vp, ctypes.c_size_t, vp]
+        lib.moments_bwd.restype = ctypes.c_int
+        lib.moments_strerror.argtypes = [ctypes.c_int]
+        lib.moments_strerror.restype = ctypes.c_char_p
+        lib.moments_last_hip_error.argtypes = []
+        lib.moments_last_hip_error.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def check(code):
+    if code != OK:
+        lib = load()
+        msg = lib.moments_strerror(code).decode()
+        if code == EHIP:
+            msg += f" [hipError {lib.moments_last_hip_error()}]"
+        raise MomentsError(code, msg)
+    return code

@@ -1,0 +1,146 @@
+// Shared device helpers for the state-moments kernels (gfx950 / CDNA4).
+//
+// Notation follows the burn-mamba moments pages ("recalculated.rs" and
+// "backward.rs" source pages): a kernel chunk holds ELL tokens t; inside it
+// a_t = inclusive cumsum of da, d_t = exp(a_t), L[t,j] = exp(a_t - a_j) for
+// j <= t (0 above the diagonal). The write axis (j,c) is folded into one index
+// k = j*c + c_i, as the pages fold it for chunk_states.
+//
+// MFMA tiles are 16x16 with fp32 accumulators. A lane l of a wave64 holds:
+//   A operand: row (l % 16), E consecutive K-slots starting at E*(l/16)
+//   B operand: col (l % 16), the same K-slots
+//   C/D      : col (l % 16), rows 4*(l/16) + i, i = 0..3
+// Only the row/col placement matters to this code: every operand of one MFMA
+// is loaded with the same slot -> k assignment, so any order of K inside an
+// instruction gives the same sum.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mom {
+
+constexpr int ELL = 32;   // tokens per kernel chunk (two 16-row MFMA tiles)
+constexpr int NW = 4;     // waves per workgroup
+constexpr int NTH = 256;  // threads per workgroup
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16;
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct MM;
+template <> struct MM<float> {
+  static constexpr int KS = 4;  // K per instruction
+  static constexpr int E = 1;   // K-slots per lane
+  using frag = float;
+  __device__ static inline f4 mma(frag a, frag b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct MM<bf16> {
+  static constexpr int KS = 32;
+  static constexpr int E = 8;
+  using frag = bf8;
+  __device__ static inline f4 mma(frag a, frag b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T to_t(float x);
+template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return (bf16)x; }
+
+// Load one operand fragment (E consecutive elements, 4 or 16 bytes aligned).
+__device__ __forceinline__ float ld_frag(const float* p) { return *p; }
+__device__ __forceinline__ bf8 ld_frag(const bf16* p) { return *reinterpret_cast<const bf8*>(p); }
+
+// Token of a K-slot when K runs over the ELL = 32 tokens of a chunk and the B
+// operand comes straight from accumulator registers (rows 4q+i of tile mt):
+//   bf16 (one K-step of 32): slot 8q+e -> t = 4q+e (e<4) or 16+4q+(e-4)
+//   fp32 (eight K-steps of 4): slot 4s+q -> t = 16*(s/4) + 4q + (s%4)
+template <typename T> __host__ __device__ __forceinline__ int tslot(int slot);
+template <> __host__ __device__ __forceinline__ int tslot<bf16>(int slot) {
+  const int q = slot >> 3, e = slot & 7;
+  return e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4);
+}
+template <> __host__ __device__ __forceinline__ int tslot<float>(int slot) {
+  const int s = slot >> 2, q = slot & 3;
+  return 16 * (s >> 2) + 4 * q + (s & 3);
+}
+
+// B fragment over the 32 tokens from accumulator registers v[mt] (one N tile).
+__device__ __forceinline__ bf8 pack_tslots(const f4 (&v)[2], int /*ks*/, bf16) {
+  bf8 f;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    f[e] = (bf16)v[0][e];
+    f[e + 4] = (bf16)v[1][e];
+  }
+  return f;
+}
+__device__ __forceinline__ float pack_tslots(const f4 (&v)[2], int ks, float) { return v[ks >> 2][ks & 3]; }
+
+// DPP lane exchange within a quad (row_mask/bank_mask all lanes).
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+  return __builtin_amdgcn_update_dpp(0.0f, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int QP_SWAP1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int QP_B0 = 0x00, QP_B1 = 0x55, QP_B2 = 0xAA, QP_B3 = 0xFF;  // broadcast lane k of quad
+
+// Sum over the 16 lanes of a row (lanes sharing l/16); every lane gets the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __shfl_xor(v, 1, 16);
+  v += __shfl_xor(v, 2, 16);
+  v += __shfl_xor(v, 4, 16);
+  v += __shfl_xor(v, 8, 16);
+  return v;
+}
+// Sum over the four lane groups (lanes sharing l%16).
+__device__ __forceinline__ float col4_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Order LDS traffic between lanes of one wave without a workgroup barrier.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Everything a kernel needs to know about the problem.
+struct Geo {
+  int b, s, c, h, p, r;
+  int V;         // min(valid_len, s)
+  int NK;        // processed kernel chunks: ceil(V / ELL)
+  int K;         // ELL * c (folded write axis)
+  int KP;        // LDS row length of K-contiguous tiles (elements)
+  int RP;        // LDS row length of R-contiguous tiles (elements)
+  int PP;        // LDS row length of P-contiguous tiles (elements)
+  int P16;       // p rounded up to 16
+  int rot_kind;  // 0 none, 1 pairwise, 2 half-split, 3 quaternion
+  int A;         // angles per token (complex modes)
+  int J;         // quaternion blocks
+  int RW;        // last dim of rot per token: A or 4*J
+  int G;         // chunks per workgroup (fwd/bwd main kernels)
+  int NGR;       // workgroups per (b,h) chain: ceil(NK / G)
+  int half;      // half-split: internal state column order interleaves the halves
+};
+
+// Internal state-column order. Half-split pairs (i, r/2+i) are stored next to
+// each other (internal 2i, 2i+1) so every complex mode rotates adjacent columns.
+__device__ __forceinline__ int perm_rc(const Geo& g, int rc) {
+  return g.half ? ((rc & 1) ? (g.r >> 1) + (rc >> 1) : (rc >> 1)) : rc;
+}
+__device__ __forceinline__ int inv_perm_rc(const Geo& g, int ra) {
+  if (!g.half) return ra;
+  const int hr = g.r >> 1;
+  return ra < hr ? 2 * ra : 2 * (ra - hr) + 1;
+}
+
+__host__ __device__ __forceinline__ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace mom

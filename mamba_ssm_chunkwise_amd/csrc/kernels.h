@@ -1,0 +1,406 @@
+// Kernels of the state-moments path. One workgroup = 4 waves (256 lanes).
+//
+// Dataflow (sources: burn-mamba "recalculated.rs" and "backward.rs" source pages):
+//   forward : k_carry (per-chunk decay-to-chunk-end GEMM, the pages' boundary
+//             carry) -> k_scan (serial carry recurrence over chunks)
+//             -> k_fwd (chunk states on MFMA, de-rotation, m2 on MFMA, m1)
+//             -> k_reduce (fixed-order sum of per-workgroup partials)
+//   backward: k_carry -> k_scan -> k_bwd (recompute states, d_c = c S + d_m1,
+//             rotation VJP, d_W = L^T G, d_xhat, d_bhat, d_da; every chunk
+//             independent because the carry cotangent enters only through
+//             G[l-1]) -> k_dscan (reverse carry-cotangent recurrence, d_h0)
+//             -> k_fix (the carry-cotangent terms of d_xhat, d_bhat, d_da)
+//             -> k_zero_tail (zeros past the processed chunks).
+#pragma once
+
+#include "chunk.h"
+
+namespace mom {
+
+// ---------------------------------------------------------------------------
+// LDS plans (shared by host sizing and device carving)
+// ---------------------------------------------------------------------------
+struct Lds {
+  size_t a, d, L, lx, bs, ltp, ltx, rot, xr, S, xg, xgw, red, m1s, total;
+};
+
+__host__ __device__ __forceinline__ size_t al16(size_t x) { return (x + 15) & ~size_t(15); }
+
+__host__ __device__ __forceinline__ size_t rot_bytes(const Geo& g) {
+  if (g.rot_kind == 1 || g.rot_kind == 2) return al16((size_t)2 * ELL * g.A * 4);
+  if (g.rot_kind == 3) return al16((size_t)ELL * g.J * 4 * 4);
+  return 16;
+}
+
+// Forward main kernel.
+__host__ __device__ __forceinline__ Lds lds_fwd(const Geo& g, int R, int tsz) {
+  Lds l{};
+  size_t o = 0;
+  l.a = o; o += al16(ELL * 4);
+  l.d = o; o += al16(ELL * 4);
+  l.L = o; o += al16(ELL * (ELL + 1) * 4);
+  l.lx = o; o += al16((size_t)ELL * g.KP * 4);
+  l.bs = o; o += al16((size_t)R * g.KP * tsz);
+  l.rot = o; o += rot_bytes(g);
+  l.xr = o; o += al16((size_t)NW * g.KP * tsz);
+  const int pp = ((g.p + 3) / 4) * 4;
+  l.m1s = o; o += al16((size_t)(pp > R ? pp : R) * R * 4);
+  l.total = o;
+  return l;
+}
+
+// Backward main kernel.
+__host__ __device__ __forceinline__ Lds lds_bwd(const Geo& g, int R, int tsz, int NT) {
+  Lds l{};
+  size_t o = 0;
+  l.a = o; o += al16(ELL * 4);
+  l.d = o; o += al16(ELL * 4);
+  l.L = o; o += al16(ELL * (ELL + 1) * 4);
+  l.lx = o; o += al16((size_t)ELL * g.KP * 4);
+  l.bs = o; o += al16((size_t)R * g.KP * tsz);
+  l.ltp = o; o += al16((size_t)ELL * SLOTP * tsz);
+  l.ltx = o; o += al16((size_t)g.K * SLOTP * tsz);
+  l.rot = o; o += rot_bytes(g);
+  l.xr = o; o += al16((size_t)NW * g.KP * tsz);
+  l.S = o; o += al16((size_t)R * g.RP * tsz);
+  const size_t xtile = (size_t)ELL * g.RP * tsz;
+  const size_t gb = tsz == 2 ? (size_t)NT * 64 * 16 : (size_t)NT * 8 * 64 * 4;
+  l.xgw = al16(xtile > gb ? xtile : gb);
+  size_t xg = l.xgw * NW;
+  const size_t rb = (size_t)ELL * R * 4;  // rotation-gradient reduction, aliases xg
+  if (xg < rb) xg = rb;
+  l.xg = o; o += al16(xg);
+  l.red = o; o += al16((size_t)(2 * NW * ELL + ELL) * 4);
+  l.total = o;
+  return l;
+}
+
+// Carry kernel: as [PK][KP] and bs [R][KP].
+__host__ __device__ __forceinline__ Lds lds_carry(const Geo& g, int R, int tsz, int PK) {
+  Lds l{};
+  size_t o = 0;
+  l.a = o; o += al16(ELL * 4);
+  l.d = o; o += al16(ELL * 4);
+  l.L = o; o += al16(ELL * (ELL + 1) * 4);
+  l.lx = o; o += al16((size_t)PK * g.KP * tsz);  // x^T scaled (A operand)
+  l.bs = o; o += al16((size_t)R * g.KP * tsz);
+  l.total = o;
+  return l;
+}
+
+// Correction kernel: dp [PK][RP], dpt [R][PP], bn [K][RP], xn [K][PP].
+__host__ __device__ __forceinline__ Lds lds_fix(const Geo& g, int R, int tsz, int PK) {
+  Lds l{};
+  size_t o = 0;
+  l.a = o; o += al16(ELL * 4);
+  l.d = o; o += al16(ELL * 4);
+  l.L = o; o += al16(ELL * (ELL + 1) * 4);
+  l.lx = o; o += al16((size_t)PK * g.RP * tsz);   // dp
+  l.ltx = o; o += al16((size_t)R * g.PP * tsz);   // dpt
+  l.bs = o; o += al16((size_t)g.K * g.RP * tsz);  // bn
+  l.xr = o; o += al16((size_t)g.K * g.PP * tsz);  // xn
+  l.red = o; o += al16((size_t)(g.K + NTH + ELL + 4) * 4);
+  l.total = o;
+  return l;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk states of one state row p0: acc[mt][nt] = h~[t = 16mt+4q+i][col 16nt+m]
+//   = d_t h_-[p0][col] + sum_{k=(j,c), j<=t} L[t,j] xhat[j,c,p0] bhat[j,c,col]
+// (chunk_states of the recalculated.rs source page, folded (j,c) write axis).
+// Rows at positions >= V are zeroed.
+// ---------------------------------------------------------------------------
+template <typename T, int NT>
+__device__ __forceinline__ void chunk_states_row(f4 (&acc)[2][NT], const Geo& g, int n, const float* s_d,
+                                        const float* lx, const T* bs, const T* xrow,
+                                        const float* hrow) {
+  constexpr int KS = MM<T>::KS, E = MM<T>::E;
+  const int lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; nt++) {
+    const int col = 16 * nt + m;
+    const float hv = (hrow != nullptr && col < g.r) ? hrow[col] : 0.0f;
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) acc[mt][nt][i] = s_d[16 * mt + 4 * q + i] * hv;
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++) {
+    const int kneed = (16 * mt + 16) * g.c;
+    const int kmax = kneed < g.K ? kneed : g.K;
+    const int nks = (kmax + KS - 1) / KS;
+    const int t = 16 * mt + m;
+    for (int ks = 0; ks < nks; ks++) {
+      const int k0 = ks * KS + E * q;
+      typename MM<T>::frag a;
+      if constexpr (E == 1) {
+        a = lx[t * g.KP + k0] * to_f(xrow[k0]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; e++) a[e] = to_t<T>(lx[t * g.KP + k0 + e] * to_f(xrow[k0 + e]));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        const auto b = ld_frag(bs + (16 * nt + m) * g.KP + k0);
+        acc[mt][nt] = MM<T>::mma(a, b, acc[mt][nt]);
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      if (n * ELL + 16 * mt + 4 * q + i >= g.V) {
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) acc[mt][nt][i] = 0.0f;
+      }
+    }
+}
+
+// Stage the x row block of one round (4 state rows, one per wave): xr[w][k].
+template <typename T>
+__device__ __forceinline__ void stage_xround(const Geo& g, const T* __restrict__ xhat, int bi, int hi, int n,
+                                    int round, T* xr) {
+  for (int idx = threadIdx.x; idx < 4 * g.K; idx += NTH) {
+    const int k = idx >> 2, ww = idx & 3;
+    const int p0 = 4 * round + ww;
+    const int j = k / g.c, ci = k - j * g.c;
+    const int pos = n * ELL + j;
+    float v = 0.0f;
+    if (p0 < g.p && pos < g.V)
+      v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + p0]);
+    xr[ww * g.KP + k] = to_t<T>(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_carry: U_n[p][col] = sum_{k=(j,c)} exp(a_last - a_j) xhat[j,c,p] bhat[j,c,col]
+// for chunks n < NK-1, and dec_n = exp(a_last) (boundary_carries, backward.rs
+// source page: the decay-to-chunk-end GEMM).
+// ---------------------------------------------------------------------------
+template <typename T, int NT>
+__global__ __launch_bounds__(NTH, 1) void k_carry(Geo g, int PK, const T* __restrict__ xhat,
+                                                   const T* __restrict__ bhat,
+                                                   const T* __restrict__ da, float* carry,
+                                                   float* dec) {
+  constexpr int R = 16 * NT, KS = MM<T>::KS, E = MM<T>::E;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Lds L = lds_carry(g, R, sizeof(T), PK);
+  float* s_a = (float*)(smem + L.a);
+  float* s_d = (float*)(smem + L.d);
+  float* s_L = (float*)(smem + L.L);
+  T* as = (T*)(smem + L.lx);
+  T* bs = (T*)(smem + L.bs);
+  const int per = g.NK - 1;
+  const int bh = blockIdx.x / per, n = blockIdx.x % per;
+  const int bi = bh / g.h, hi = bh % g.h;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+
+  stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
+  stage_bhat<T, R>(g, bhat, bi, hi, n, bs);
+  __syncthreads();
+  const float* wl = s_L + (ELL - 1) * (ELL + 1);  // L[l-1][j] = exp(a_last - a_j)
+  for (int idx = threadIdx.x; idx < g.K * PK; idx += NTH) {
+    const int k = idx / PK, pp = idx % PK;
+    const int j = k / g.c, ci = k - j * g.c;
+    const int pos = n * ELL + j;
+    float v = 0.0f;
+    if (pp < g.p) v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp]) * wl[j];
+    as[pp * g.KP + k] = to_t<T>(v);
+  }
+  __syncthreads();
+  const int MT = PK / 16;
+  const int nks = g.K / KS;
+#pragma unroll
+  for (int mi = 0; mi < 2; mi++) {
+    const int mt = w + 4 * mi;
+    if (mt >= MT) break;
+    f4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) acc[nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ks = 0; ks < nks; ks++) {
+      const int k0 = ks * KS + E * q;
+      const auto a = ld_frag(as + (16 * mt + m) * g.KP + k0);
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) acc[nt] = MM<T>::mma(a, ld_frag(bs + (16 * nt + m) * g.KP + k0), acc[nt]);
+    }
+    float* out = carry + ((size_t)bh * g.NK + n) * g.p * g.r;
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++) {
+      const int col = 16 * nt + m;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int pp = 16 * mt + 4 * q + i;
+        if (pp < g.p && col < g.r) out[(size_t)pp * g.r + col] = acc[nt][i];
+      }
+    }
+  }
+  if (threadIdx.x == 0) dec[(size_t)bh * g.NK + n] = s_d[ELL - 1];
+}
+
+// k_scan: h_-(0) = h0, h_-(n+1) = dec_n h_-(n) + U_n, written in place over U.
+template <typename T>
+__global__ __launch_bounds__(NTH) void k_scan(Geo g, const T* __restrict__ h0, float* carry,
+                                              const float* __restrict__ dec) {
+  const int bh = blockIdx.x;
+  const int e = blockIdx.y * NTH + threadIdx.x;
+  const int pr = g.p * g.r;
+  if (e >= pr) return;
+  const int p0 = e / g.r, rc = e % g.r;
+  float h = h0 ? to_f(h0[((size_t)bh * g.p + p0) * g.r + perm_rc(g, rc)]) : 0.0f;
+  float* C = carry + (size_t)bh * g.NK * pr + e;
+  const float* D = dec + (size_t)bh * g.NK;
+  const int last = g.NK - 1;
+  for (int n0 = 0; n0 < g.NK; n0 += 8) {
+    float u[8], dd[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int n = n0 + k;
+      u[k] = n < last ? C[(size_t)n * pr] : 0.0f;
+      dd[k] = n < last ? D[n] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int n = n0 + k;
+      if (n < g.NK) {
+        C[(size_t)n * pr] = h;
+        h = dd[k] * h + u[k];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_fwd: chunk states, de-rotation, m2 += c^T c (MFMA, K over tokens, operands
+// straight from the accumulators), m1 += sum_t c. One workgroup walks G chunks
+// of one (b,h) chain and writes one partial of m2 (upper tiles) and m1.
+// ---------------------------------------------------------------------------
+template <typename T, int NT>
+__global__ __launch_bounds__(NTH, 1) void k_fwd(Geo g, const T* __restrict__ xhat,
+                                                 const T* __restrict__ bhat,
+                                                 const T* __restrict__ da,
+                                                 const T* __restrict__ rot,
+                                                 const float* __restrict__ carry, float* m2part,
+                                                 float* m1part) {
+  constexpr int R = 16 * NT, KS = MM<T>::KS, NKT = ELL / KS;
+  constexpr int NU = NT * (NT + 1) / 2;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Lds L = lds_fwd(g, R, sizeof(T));
+  float* s_a = (float*)(smem + L.a);
+  float* s_d = (float*)(smem + L.d);
+  float* s_L = (float*)(smem + L.L);
+  float* lx = (float*)(smem + L.lx);
+  T* bs = (T*)(smem + L.bs);
+  float* cs = (float*)(smem + L.rot);
+  float* sn = cs + ELL * g.A;
+  float* qv = cs;
+  T* xr = (T*)(smem + L.xr);
+  float* m1s = (float*)(smem + L.m1s);
+
+  const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
+  const int bi = bh / g.h, hi = bh % g.h;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+  const int nrounds = (g.p + 3) / 4;
+  for (int idx = threadIdx.x; idx < nrounds * 4 * R; idx += NTH) m1s[idx] = 0.0f;
+  f4 m2acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; u++) m2acc[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int n0 = gi * g.G;
+  const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
+  for (int n = n0; n < n1; n++) {
+    __syncthreads();
+    stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
+    stage_bhat<T, R>(g, bhat, bi, hi, n, bs);
+    stage_rot(g, rot, bi, hi, n, cs, sn, qv);
+    __syncthreads();
+    stage_lx(g, s_L, lx);
+    for (int round = 0; round < nrounds; round++) {
+      stage_xround(g, xhat, bi, hi, n, round, xr);
+      __syncthreads();
+      const int p0 = 4 * round + w;
+      const bool valid = p0 < g.p;
+      const float* hrow = valid ? carry + (((size_t)bh * g.NK + n) * g.p + p0) * g.r : nullptr;
+      f4 acc[2][NT];
+      chunk_states_row<T, NT>(acc, g, n, s_d, lx, bs, xr + w * g.KP, hrow);
+      rotate_tiles<false, NT>(acc, g, cs, sn, qv);
+      // m1[p0][col] += sum over the chunk's tokens
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) sum += acc[mt][nt][i];
+        sum = col4_sum(sum);
+        if (q == 0 && valid) m1s[p0 * R + 16 * nt + m] += sum;
+      }
+      // m2 tile (R1 <= R2) += sum_t c[t][R1 cols]^T c[t][R2 cols]
+      int u = 0;
+#pragma unroll
+      for (int r1 = 0; r1 < NT; r1++) {
+        f4 a1[2] = {acc[0][r1], acc[1][r1]};
+#pragma unroll
+        for (int r2 = r1; r2 < NT; r2++) {
+          f4 a2[2] = {acc[0][r2], acc[1][r2]};
+#pragma unroll
+          for (int ks = 0; ks < NKT; ks++)
+            m2acc[u] = MM<T>::mma(pack_tslots(a1, ks, T{}), pack_tslots(a2, ks, T{}), m2acc[u]);
+          u++;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // partial m1 (internal column order)
+  __syncthreads();
+  float* m1o = m1part + ((size_t)bh * g.NGR + gi) * g.p * R;
+  for (int idx = threadIdx.x; idx < g.p * R; idx += NTH) m1o[idx] = m1s[idx];
+  __syncthreads();
+  // partial m2: fixed-order sum of the four waves' tiles
+  float* M = m1s;
+  for (int idx = threadIdx.x; idx < R * R; idx += NTH) M[idx] = 0.0f;
+  __syncthreads();
+  for (int ww = 0; ww < NW; ww++) {
+    if (w == ww) {
+      int u = 0;
+#pragma unroll
+      for (int r1 = 0; r1 < NT; r1++)
+#pragma unroll
+        for (int r2 = r1; r2 < NT; r2++) {
+#pragma unroll
+          for (int i = 0; i < 4; i++) M[(16 * r1 + 4 * q + i) * R + 16 * r2 + m] += m2acc[u][i];
+          u++;
+        }
+    }
+    __syncthreads();
+  }
+  float* m2o = m2part + ((size_t)bh * g.NGR + gi) * R * R;
+  for (int idx = threadIdx.x; idx < R * R; idx += NTH) m2o[idx] = M[idx];
+}
+
+// k_reduce: m2 = sum over partials (mirrored from upper tiles), m1 likewise;
+// both written in the caller's column order.
+__global__ __launch_bounds__(NTH) void k_reduce(Geo g, int R, const float* __restrict__ m2part,
+                                                const float* __restrict__ m1part, float* m2,
+                                                float* m1) {
+  const int bh = blockIdx.x;
+  const int e = blockIdx.y * NTH + threadIdx.x;
+  const int n2 = g.r * g.r, n1 = g.p * g.r;
+  if (e < n2) {
+    const int a = inv_perm_rc(g, e / g.r), b = inv_perm_rc(g, e % g.r);
+    const int x = (a >> 4) <= (b >> 4) ? a : b, y = (a >> 4) <= (b >> 4) ? b : a;
+    float s = 0.0f;
+    for (int gi = 0; gi < g.NGR; gi++) s += m2part[((size_t)bh * g.NGR + gi) * R * R + x * R + y];
+    m2[(size_t)bh * n2 + e] = s;
+  } else if (e < n2 + n1) {
+    const int f = e - n2;
+    const int p0 = f / g.r, rc = inv_perm_rc(g, f % g.r);
+    float s = 0.0f;
+    for (int gi = 0; gi < g.NGR; gi++) s += m1part[((size_t)bh * g.NGR + gi) * g.p * R + p0 * R + rc];
+    m1[(size_t)bh * n1 + f] = s;
+  }
+}
+
+}  // namespace mom

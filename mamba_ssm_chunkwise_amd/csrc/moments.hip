@@ -1,0 +1,315 @@
+// C ABI of the state-moments library: validation, planning, dispatch.
+// The operation and its conventions are stated in include/moments.h.
+#include "moments.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "kernels_bwd.h"
+
+using namespace mom;
+
+namespace {
+
+std::atomic<int> g_last_hip{0};
+
+constexpr size_t kLdsLimit = 160 * 1024;
+
+struct Plan {
+  Geo g;
+  bool bf;      // bf16 inputs
+  int NT, R;    // state columns padded to R = 16*NT
+  int PK;       // state rows padded for MFMA K over rows
+  size_t carry, dec, m2p, m1p, db;  // workspace offsets
+  size_t ws_fwd, ws_bwd;
+};
+
+int round_nt(int r, bool bf) {
+  int nt = (r + 15) / 16;
+  if (nt <= 1) nt = bf ? 2 : 1;
+  else if (nt <= 2) nt = 2;
+  else if (nt <= 4) nt = 4;
+  else nt = 8;
+  return nt;
+}
+
+int make_plan(const moments_desc* d, Plan* P) {
+  if (d == nullptr) return MOMENTS_EINVAL;
+  if (d->b < 1 || d->s < 1 || d->c < 1 || d->h < 1 || d->p < 1 || d->r < 1) return MOMENTS_EINVAL;
+  if (d->chunk_len < 1 || d->s % d->chunk_len != 0) return MOMENTS_EINVAL;
+  if (d->valid_len < 0) return MOMENTS_EINVAL;
+  if (d->dtype != MOMENTS_F32 && d->dtype != MOMENTS_BF16) return MOMENTS_EINVAL;
+  int A = 0, J = 0, RW = 0;
+  switch (d->rot_kind) {
+    case MOMENTS_ROT_NONE:
+      break;
+    case MOMENTS_ROT_COMPLEX_PAIRWISE:
+    case MOMENTS_ROT_COMPLEX_HALF:
+      if (d->rope_dim < 0 || d->rope_dim % 2 != 0 || d->rope_dim > d->r) return MOMENTS_EINVAL;
+      if (d->rot_kind == MOMENTS_ROT_COMPLEX_HALF && d->r % 2 != 0) return MOMENTS_EINVAL;
+      A = (int)(d->rope_dim / 2);
+      RW = A;
+      break;
+    case MOMENTS_ROT_QUATERNION:
+      if (d->quat_blocks < 0 || 4 * d->quat_blocks > d->r) return MOMENTS_EINVAL;
+      J = (int)d->quat_blocks;
+      RW = 4 * J;
+      break;
+    default:
+      return MOMENTS_EINVAL;
+  }
+  if (d->r > 128 || d->c > 4) return MOMENTS_ENOTSUP;
+  if (d->s > (int64_t)1 << 30 || d->p > 4096 || d->b * d->h > ((int64_t)1 << 30)) return MOMENTS_ENOTSUP;
+
+  const bool bf = d->dtype == MOMENTS_BF16;
+  const int tsz = bf ? 2 : 4, pad = 16 / tsz;
+  Geo& g = P->g;
+  g = Geo{};
+  g.b = (int)d->b; g.s = (int)d->s; g.c = (int)d->c; g.h = (int)d->h; g.p = (int)d->p; g.r = (int)d->r;
+  g.V = (int)(d->valid_len < d->s ? d->valid_len : d->s);
+  g.NK = (g.V + ELL - 1) / ELL;
+  g.K = ELL * g.c;
+  P->bf = bf;
+  P->NT = round_nt(g.r, bf);
+  P->R = 16 * P->NT;
+  const int kq = bf ? 32 : 16;
+  P->PK = ((g.p + kq - 1) / kq) * kq;
+  g.KP = g.K + pad;
+  g.RP = P->R + pad;
+  g.PP = P->PK + pad;
+  g.P16 = P->PK;
+  g.rot_kind = d->rot_kind;
+  g.A = A; g.J = J; g.RW = RW;
+  g.half = d->rot_kind == MOMENTS_ROT_COMPLEX_HALF;
+  const int64_t chains = (int64_t)g.b * g.h;
+  const int64_t total = chains * g.NK;
+  int G = (int)((total + 2047) / 2048);
+  if (G < 1) G = 1;
+  if (g.NK > 0 && G > g.NK) G = g.NK;
+  g.G = G;
+  g.NGR = g.NK > 0 ? (g.NK + G - 1) / G : 0;
+
+  if (lds_fwd(g, P->R, tsz).total > kLdsLimit || lds_bwd(g, P->R, tsz, P->NT).total > kLdsLimit ||
+      lds_carry(g, P->R, tsz, P->PK).total > kLdsLimit || lds_fix(g, P->R, tsz, P->PK).total > kLdsLimit)
+    return MOMENTS_ENOTSUP;
+
+  const size_t pr = (size_t)g.p * g.r;
+  size_t o = 0;
+  P->carry = o; o = align256(o + chains * (size_t)g.NK * pr * 4);
+  P->dec = o; o = align256(o + chains * (size_t)g.NK * 4);
+  const size_t base = o;
+  P->m2p = o; o = align256(o + chains * (size_t)g.NGR * P->R * P->R * 4);
+  P->m1p = o; o = align256(o + chains * (size_t)g.NGR * g.p * P->R * 4);
+  P->ws_fwd = o;
+  P->db = base;
+  P->ws_bwd = align256(base + chains * (size_t)g.NK * pr * 4);
+  return MOMENTS_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+int hip_fail(hipError_t e) {
+  g_last_hip.store((int)e);
+  return MOMENTS_EHIP;
+}
+
+template <typename K>
+int set_lds(K kernel, size_t bytes) {
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+int check_launch() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : hip_fail(e);
+}
+
+#define MOM_TRY(x)          \
+  do {                      \
+    const int _rc = (x);    \
+    if (_rc != 0) return _rc; \
+  } while (0)
+
+template <typename T, int NT>
+int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, const T* h0,
+                      unsigned char* ws, hipStream_t st) {
+  const Geo& g = P.g;
+  float* carry = (float*)(ws + P.carry);
+  float* dec = (float*)(ws + P.dec);
+  const int chains = g.b * g.h;
+  if (g.NK >= 2) {
+    const size_t lds = lds_carry(g, P.R, sizeof(T), P.PK).total;
+    MOM_TRY(set_lds(k_carry<T, NT>, lds));
+    hipLaunchKernelGGL((k_carry<T, NT>), dim3(chains * (g.NK - 1)), dim3(NTH), lds, st, g, P.PK, xhat,
+                       bhat, da, carry, dec);
+    MOM_TRY(check_launch());
+  }
+  if (g.NK >= 1) {
+    const int pr = g.p * g.r;
+    hipLaunchKernelGGL((k_scan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, h0, carry,
+                       dec);
+    MOM_TRY(check_launch());
+  }
+  return 0;
+}
+
+template <typename T, int NT>
+int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, const void* rot,
+            const void* h0, float* m2, float* m1, unsigned char* ws, hipStream_t st) {
+  const Geo& g = P.g;
+  const T* X = (const T*)xhat;
+  const T* B = (const T*)bhat;
+  const T* D = (const T*)da;
+  const T* Rt = (const T*)rot;
+  MOM_TRY((launch_carry_scan<T, NT>(P, X, B, D, (const T*)h0, ws, st)));
+  float* m2p = (float*)(ws + P.m2p);
+  float* m1p = (float*)(ws + P.m1p);
+  const int chains = g.b * g.h;
+  if (g.NK >= 1) {
+    const size_t lds = lds_fwd(g, P.R, sizeof(T)).total;
+    MOM_TRY(set_lds(k_fwd<T, NT>, lds));
+    hipLaunchKernelGGL((k_fwd<T, NT>), dim3(chains * g.NGR), dim3(NTH), lds, st, g, X, B, D, Rt,
+                       (const float*)(ws + P.carry), m2p, m1p);
+    MOM_TRY(check_launch());
+  }
+  const int nout = g.r * g.r + g.p * g.r;
+  hipLaunchKernelGGL(k_reduce, dim3(chains, (nout + NTH - 1) / NTH), dim3(NTH), 0, st, g, P.R,
+                     (const float*)m2p, (const float*)m1p, m2, m1);
+  return check_launch();
+}
+
+template <typename T, int NT>
+int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, const void* rot,
+            const void* h0, const float* dm2, const float* dm1, void* dx, void* db, void* dda,
+            void* drot, void* dh0, unsigned char* ws, hipStream_t st) {
+  const Geo& g = P.g;
+  const T* X = (const T*)xhat;
+  const T* B = (const T*)bhat;
+  const T* D = (const T*)da;
+  const T* Rt = (const T*)rot;
+  MOM_TRY((launch_carry_scan<T, NT>(P, X, B, D, (const T*)h0, ws, st)));
+  float* carry = (float*)(ws + P.carry);
+  float* dec = (float*)(ws + P.dec);
+  float* Db = (float*)(ws + P.db);
+  const int chains = g.b * g.h;
+  if (g.NK >= 1) {
+    const size_t lds = lds_bwd(g, P.R, sizeof(T), P.NT).total;
+    MOM_TRY(set_lds(k_bwd<T, NT>, lds));
+    hipLaunchKernelGGL((k_bwd<T, NT>), dim3(chains * g.NGR), dim3(NTH), lds, st, g, X, B, D, Rt,
+                       (const float*)carry, dm2, dm1, Db, (T*)dx, (T*)db, (T*)dda, (T*)drot);
+    MOM_TRY(check_launch());
+  }
+  const int pr = g.p * g.r;
+  hipLaunchKernelGGL((k_dscan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, Db,
+                     (const float*)dec, (T*)dh0);
+  MOM_TRY(check_launch());
+  if (g.NK >= 2 && (dx != nullptr || db != nullptr || dda != nullptr)) {
+    const size_t lds = lds_fix(g, P.R, sizeof(T), P.PK).total;
+    MOM_TRY(set_lds(k_fix<T, NT>, lds));
+    hipLaunchKernelGGL((k_fix<T, NT>), dim3(chains * (g.NK - 1)), dim3(NTH), lds, st, g, P.PK, X, B, D,
+                       (const float*)carry, (const float*)Db, (T*)dx, (T*)db, (T*)dda);
+    MOM_TRY(check_launch());
+  }
+  const int z0 = g.NK * ELL;
+  if (z0 < g.s) {
+    hipLaunchKernelGGL((k_zero_tail<T>), dim3(1024), dim3(NTH), 0, st, g, z0, (T*)dx, (T*)db, (T*)dda,
+                       (T*)drot);
+    MOM_TRY(check_launch());
+  }
+  return 0;
+}
+
+template <typename T>
+int fwd_nt(const Plan& P, const void* x, const void* b, const void* da, const void* rot,
+           const void* h0, float* m2, float* m1, unsigned char* ws, hipStream_t st) {
+  switch (P.NT) {
+    case 1: if constexpr (sizeof(T) == 4) return run_fwd<T, 1>(P, x, b, da, rot, h0, m2, m1, ws, st); break;
+    case 2: return run_fwd<T, 2>(P, x, b, da, rot, h0, m2, m1, ws, st);
+    case 4: return run_fwd<T, 4>(P, x, b, da, rot, h0, m2, m1, ws, st);
+    case 8: return run_fwd<T, 8>(P, x, b, da, rot, h0, m2, m1, ws, st);
+  }
+  return MOMENTS_ENOTSUP;
+}
+
+template <typename T>
+int bwd_nt(const Plan& P, const void* x, const void* b, const void* da, const void* rot,
+           const void* h0, const float* dm2, const float* dm1, void* dx, void* db, void* dda,
+           void* drot, void* dh0, unsigned char* ws, hipStream_t st) {
+  switch (P.NT) {
+    case 1: if constexpr (sizeof(T) == 4) return run_bwd<T, 1>(P, x, b, da, rot, h0, dm2, dm1, dx, db, dda, drot, dh0, ws, st); break;
+    case 2: return run_bwd<T, 2>(P, x, b, da, rot, h0, dm2, dm1, dx, db, dda, drot, dh0, ws, st);
+    case 4: return run_bwd<T, 4>(P, x, b, da, rot, h0, dm2, dm1, dx, db, dda, drot, dh0, ws, st);
+    case 8: return run_bwd<T, 8>(P, x, b, da, rot, h0, dm2, dm1, dx, db, dda, drot, dh0, ws, st);
+  }
+  return MOMENTS_ENOTSUP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moments_validate(const moments_desc* desc) {
+  Plan P;
+  return make_plan(desc, &P);
+}
+
+int64_t moments_workspace_size(const moments_desc* desc, int is_bwd) {
+  Plan P;
+  const int rc = make_plan(desc, &P);
+  if (rc != 0) return rc;
+  return (int64_t)(is_bwd ? P.ws_bwd : P.ws_fwd);
+}
+
+int moments_fwd(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                const void* rot, const void* h0, float* m2, float* m1, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Plan P;
+  MOM_TRY(make_plan(desc, &P));
+  if (!xhat || !bhat || !da || !m2 || !m1) return MOMENTS_EINVAL;
+  if (desc->rot_kind != MOMENTS_ROT_NONE && rot == nullptr) return MOMENTS_EINVAL;
+  const void* ptrs[] = {xhat, bhat, da, rot, h0, m2, m1, workspace};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return MOMENTS_EINVAL;
+  if (workspace_bytes < P.ws_fwd || (P.ws_fwd > 0 && workspace == nullptr)) return MOMENTS_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  if (P.bf) return fwd_nt<bf16>(P, xhat, bhat, da, rot, h0, m2, m1, ws, st);
+  return fwd_nt<float>(P, xhat, bhat, da, rot, h0, m2, m1, ws, st);
+}
+
+int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                const void* rot, const void* h0, const float* d_m2, const float* d_m1, void* d_xhat,
+                void* d_bhat, void* d_da, void* d_rot, void* d_h0, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Plan P;
+  MOM_TRY(make_plan(desc, &P));
+  if (!xhat || !bhat || !da || !d_m2 || !d_m1) return MOMENTS_EINVAL;
+  if (desc->rot_kind != MOMENTS_ROT_NONE && rot == nullptr) return MOMENTS_EINVAL;
+  if (desc->rot_kind == MOMENTS_ROT_NONE && d_rot != nullptr) return MOMENTS_EINVAL;
+  const void* ptrs[] = {xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, workspace};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return MOMENTS_EINVAL;
+  if (workspace_bytes < P.ws_bwd || (P.ws_bwd > 0 && workspace == nullptr)) return MOMENTS_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  if (P.bf)
+    return bwd_nt<bf16>(P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, st);
+  return bwd_nt<float>(P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, st);
+}
+
+const char* moments_strerror(int code) {
+  switch (code) {
+    case MOMENTS_OK: return "ok";
+    case MOMENTS_EINVAL: return "invalid argument (descriptor, NULL pointer or misalignment)";
+    case MOMENTS_ENOTSUP: return "shape not covered by the compiled kernels";
+    case MOMENTS_EWORKSPACE: return "workspace too small";
+    case MOMENTS_EHIP: return "HIP runtime error (see moments_last_hip_error)";
+  }
+  return "unknown error";
+}
+
+int moments_last_hip_error(void) { return g_last_hip.load(); }
+
+}  // extern "C"

@@ -131,7 +131,7 @@ def generate(w: Workload, device="cpu", with_cotangents=True):
         v = torch.randn(w.b, w.s, w.h, w.quat_blocks, 3, **f32).double() * w.quat_sd
         phi = v.norm(dim=-1, keepdim=True).clamp_min(1e-30)
         q = torch.cat([torch.cos(phi / 2), torch.sin(phi / 2) * v / phi], dim=-1)
-        out["rot"] = _quat_prefix(q, dim=1).to(dt)
+        out["rot"] = _quat_prefix(q, dim=1).to(dt).contiguous()
     else:
         out["rot"] = None
     if w.h0_sd is None:
