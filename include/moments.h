@@ -107,6 +107,18 @@ int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, co
 const char* moments_strerror(int code);
 int moments_last_hip_error(void);
 
+/* Diagnostics: per-kernel timing. While enabled (on != 0), each kernel launch
+ * of moments_fwd / moments_bwd is bracketed by two HIP events recorded on the
+ * caller's stream (the stream the kernel runs on); disabled by default.
+ * moments_profile_read() waits for the recorded events, folds them into
+ * per-kernel totals and reports kernel `id` (0 <= id < the returned count):
+ * its name, number of timed launches and summed milliseconds. It returns the
+ * number of kernel ids, or a negative error code. Not thread-safe with
+ * concurrent fwd/bwd calls from other host threads. */
+int moments_profile_enable(int on);
+int moments_profile_read(int id, const char** name, int64_t* launches, double* total_ms);
+void moments_profile_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

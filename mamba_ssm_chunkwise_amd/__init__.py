@@ -95,3 +95,27 @@ def moments_bwd(desc: Desc, xhat, bhat, da, rot, h0, d_m2, d_m1, want=("xhat", "
                                  _ptr(out["d_h0"]), _ptr(ws), ws.numel(), _stream(dev))
     _lib.check(rc)
     return out
+
+
+def profile_enable(on: bool) -> bool:
+    """Turn per-kernel HIP-event timing on or off; returns the previous state."""
+    return bool(_lib.load().moments_profile_enable(int(bool(on))))
+
+
+def profile_reset() -> None:
+    _lib.load().moments_profile_reset()
+
+
+def profile_read() -> dict:
+    """{kernel name: (timed launches, summed ms)} of the launches timed so far."""
+    lib = _lib.load()
+    out = {}
+    name = ctypes.c_char_p()
+    n = ctypes.c_int64()
+    ms = ctypes.c_double()
+    count = lib.moments_profile_read(0, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms))
+    _lib.check(min(count, 0))
+    for i in range(count):
+        lib.moments_profile_read(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms))
+        out[name.value.decode()] = (int(n.value), float(ms.value))
+    return out

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
+#include <vector>
 
 #include "kernels_bwd.h"
 
@@ -15,6 +17,55 @@ namespace {
 std::atomic<int> g_last_hip{0};
 
 constexpr size_t kLdsLimit = 160 * 1024;
+
+// ---- optional per-kernel event timing (moments_profile_*) -------------------
+enum KernelId { KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_N };
+const char* const kKernelNames[KID_N] = {"k_carry", "k_scan", "k_fwd", "k_reduce",
+                                         "k_bwd", "k_dscan", "k_fix", "k_zero_tail"};
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  struct Rec { int kid; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  double ms[KID_N] = {};
+  int64_t n[KID_N] = {};
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+hipEvent_t prof_event() {
+  Prof& P = prof();
+  if (!P.pool.empty()) {
+    hipEvent_t e = P.pool.back();
+    P.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+// Brackets one launch with events when profiling is on.
+struct ProfScope {
+  int kid;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  ProfScope(int k, hipStream_t s) : kid(k), st(s) {
+    Prof& P = prof();
+    std::lock_guard<std::mutex> g(P.mu);
+    if (P.on && (a = prof_event()) != nullptr) (void)hipEventRecord(a, st);
+  }
+  ~ProfScope() {
+    if (a == nullptr) return;
+    Prof& P = prof();
+    std::lock_guard<std::mutex> g(P.mu);
+    hipEvent_t b = prof_event();
+    if (b == nullptr) return;
+    (void)hipEventRecord(b, st);
+    P.pending.push_back({kid, a, b});
+  }
+};
 
 struct Plan {
   Geo g;
@@ -142,12 +193,14 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   if (g.NK >= 2) {
     const size_t lds = lds_carry(g, P.R, sizeof(T), P.PK).total;
     MOM_TRY(set_lds(k_carry<T, NT>, lds));
+    ProfScope ps(KID_CARRY, st);
     hipLaunchKernelGGL((k_carry<T, NT>), dim3(chains * (g.NK - 1)), dim3(NTH), lds, st, g, P.PK, xhat,
                        bhat, da, carry, dec);
     MOM_TRY(check_launch());
   }
   if (g.NK >= 1) {
     const int pr = g.p * g.r;
+    ProfScope ps(KID_SCAN, st);
     hipLaunchKernelGGL((k_scan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, h0, carry,
                        dec);
     MOM_TRY(check_launch());
@@ -170,13 +223,17 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   if (g.NK >= 1) {
     const size_t lds = lds_fwd(g, P.R, sizeof(T)).total;
     MOM_TRY(set_lds(k_fwd<T, NT>, lds));
+    ProfScope ps(KID_FWD, st);
     hipLaunchKernelGGL((k_fwd<T, NT>), dim3(chains * g.NGR), dim3(NTH), lds, st, g, X, B, D, Rt,
                        (const float*)(ws + P.carry), m2p, m1p);
     MOM_TRY(check_launch());
   }
-  const int nout = g.r * g.r + g.p * g.r;
-  hipLaunchKernelGGL(k_reduce, dim3(chains, (nout + NTH - 1) / NTH), dim3(NTH), 0, st, g, P.R,
-                     (const float*)m2p, (const float*)m1p, m2, m1);
+  {
+    const int nout = g.r * g.r + g.p * g.r;
+    ProfScope ps(KID_REDUCE, st);
+    hipLaunchKernelGGL(k_reduce, dim3(chains, (nout + NTH - 1) / NTH), dim3(NTH), 0, st, g, P.R,
+                       (const float*)m2p, (const float*)m1p, m2, m1);
+  }
   return check_launch();
 }
 
@@ -197,23 +254,29 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   if (g.NK >= 1) {
     const size_t lds = lds_bwd(g, P.R, sizeof(T), P.NT).total;
     MOM_TRY(set_lds(k_bwd<T, NT>, lds));
+    ProfScope ps(KID_BWD, st);
     hipLaunchKernelGGL((k_bwd<T, NT>), dim3(chains * g.NGR), dim3(NTH), lds, st, g, X, B, D, Rt,
                        (const float*)carry, dm2, dm1, Db, (T*)dx, (T*)db, (T*)dda, (T*)drot);
     MOM_TRY(check_launch());
   }
-  const int pr = g.p * g.r;
-  hipLaunchKernelGGL((k_dscan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, Db,
-                     (const float*)dec, (T*)dh0);
+  {
+    const int pr = g.p * g.r;
+    ProfScope ps(KID_DSCAN, st);
+    hipLaunchKernelGGL((k_dscan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, Db,
+                       (const float*)dec, (T*)dh0);
+  }
   MOM_TRY(check_launch());
   if (g.NK >= 2 && (dx != nullptr || db != nullptr || dda != nullptr)) {
     const size_t lds = lds_fix(g, P.R, sizeof(T), P.PK).total;
     MOM_TRY(set_lds(k_fix<T, NT>, lds));
+    ProfScope ps(KID_FIX, st);
     hipLaunchKernelGGL((k_fix<T, NT>), dim3(chains * (g.NK - 1)), dim3(NTH), lds, st, g, P.PK, X, B, D,
                        (const float*)carry, (const float*)Db, (T*)dx, (T*)db, (T*)dda);
     MOM_TRY(check_launch());
   }
   const int z0 = g.NK * ELL;
   if (z0 < g.s) {
+    ProfScope ps(KID_ZERO, st);
     hipLaunchKernelGGL((k_zero_tail<T>), dim3(1024), dim3(NTH), 0, st, g, z0, (T*)dx, (T*)db, (T*)dda,
                        (T*)drot);
     MOM_TRY(check_launch());
@@ -311,5 +374,49 @@ const char* moments_strerror(int code) {
 }
 
 int moments_last_hip_error(void) { return g_last_hip.load(); }
+
+int moments_profile_enable(int on) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  const int was = P.on ? 1 : 0;
+  P.on = on != 0;
+  return was;
+}
+
+int moments_profile_read(int id, const char** name, int64_t* launches, double* total_ms) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  for (const auto& r : P.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess) return hip_fail(hipGetLastError());
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      P.ms[r.kid] += ms;
+      P.n[r.kid] += 1;
+    }
+    P.pool.push_back(r.a);
+    P.pool.push_back(r.b);
+  }
+  P.pending.clear();
+  if (id < 0 || id >= KID_N) return MOMENTS_EINVAL;
+  if (name) *name = kKernelNames[id];
+  if (launches) *launches = P.n[id];
+  if (total_ms) *total_ms = P.ms[id];
+  return KID_N;
+}
+
+void moments_profile_reset(void) {
+  Prof& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  for (auto& r : P.pending) {
+    (void)hipEventSynchronize(r.b);
+    P.pool.push_back(r.a);
+    P.pool.push_back(r.b);
+  }
+  P.pending.clear();
+  for (int i = 0; i < KID_N; i++) {
+    P.ms[i] = 0.0;
+    P.n[i] = 0;
+  }
+}
 
 }  // extern "C"
