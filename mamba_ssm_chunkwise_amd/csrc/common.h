@@ -21,8 +21,10 @@
 namespace mom {
 
 constexpr int ELL = 32;   // tokens per kernel chunk (two 16-row MFMA tiles)
-constexpr int NW = 4;     // waves per workgroup
-constexpr int NTH = 256;  // threads per workgroup
+constexpr int NW = 4;     // waves per workgroup (forward, carry, correction kernels)
+constexpr int NTH = 256;  // threads per workgroup (forward, carry, correction kernels)
+constexpr int NTHB = 1024; // threads per workgroup of the backward main kernel (16 waves)
+constexpr int NCW = 4;     // backward: waves sharing one state row (column quarters)
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16;
@@ -86,15 +88,21 @@ __device__ __forceinline__ float pack_tslots(const f4 (&v)[2], int ks, float) { 
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
   return __builtin_amdgcn_update_dpp(0.0f, v, CTRL, 0xF, 0xF, false);
 }
-constexpr int QP_SWAP1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int QP_SWAP1 = 0xB1;  // quad_perm [1,0,3,2]: lane k gets lane k^1
+constexpr int QP_X2 = 0x4E;     // quad_perm [2,3,0,1]: lane k gets lane k^2
+constexpr int QP_X3 = 0x1B;     // quad_perm [3,2,1,0]: lane k gets lane k^3
 constexpr int QP_B0 = 0x00, QP_B1 = 0x55, QP_B2 = 0xAA, QP_B3 = 0xFF;  // broadcast lane k of quad
 
+constexpr int DPP_ROW_MIRROR = 0x140;       // lane i of a row <- lane 15 - i
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;  // lane i of a half row <- lane 7 - i
+
 // Sum over the 16 lanes of a row (lanes sharing l/16); every lane gets the sum.
+// Quad sums first, then the two quads of each half row, then the two halves.
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 1, 16);
-  v += __shfl_xor(v, 2, 16);
-  v += __shfl_xor(v, 4, 16);
-  v += __shfl_xor(v, 8, 16);
+  v += dpp<QP_SWAP1>(v);
+  v += dpp<QP_X2>(v);
+  v += dpp<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp<DPP_ROW_MIRROR>(v);
   return v;
 }
 // Sum over the four lane groups (lanes sharing l%16).
@@ -128,6 +136,7 @@ struct Geo {
   int G;         // chunks per workgroup (fwd/bwd main kernels)
   int NGR;       // workgroups per (b,h) chain: ceil(NK / G)
   int half;      // half-split: internal state column order interleaves the halves
+  int cinv;      // ceil(65536 / c): j = (k * cinv) >> 16 for the folded index k < 65536 / c
 };
 
 // Internal state-column order. Half-split pairs (i, r/2+i) are stored next to

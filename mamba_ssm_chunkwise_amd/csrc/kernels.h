@@ -32,45 +32,52 @@ __host__ __device__ __forceinline__ size_t rot_bytes(const Geo& g) {
   return 16;
 }
 
-// Forward main kernel.
-__host__ __device__ __forceinline__ Lds lds_fwd(const Geo& g, int R, int tsz) {
+// Forward main kernel: c exchange cx holds, per wave, the state-row tile as
+// MFMA B fragments (K over tokens) for all NT column tiles.
+__host__ __device__ __forceinline__ size_t frag_tile_bytes(int NT, int tsz) {
+  return tsz == 2 ? (size_t)NT * 64 * 16 : (size_t)NT * 8 * 64 * 4;
+}
+__host__ __device__ __forceinline__ Lds lds_fwd(const Geo& g, int R, int tsz, int NT) {
   Lds l{};
   size_t o = 0;
   l.a = o; o += al16(ELL * 4);
   l.d = o; o += al16(ELL * 4);
   l.L = o; o += al16(ELL * (ELL + 1) * 4);
-  l.lx = o; o += al16((size_t)ELL * g.KP * 4);
   l.bs = o; o += al16((size_t)R * g.KP * tsz);
   l.rot = o; o += rot_bytes(g);
   l.xr = o; o += al16((size_t)NW * g.KP * tsz);
-  const int pp = ((g.p + 3) / 4) * 4;
-  l.m1s = o; o += al16((size_t)(pp > R ? pp : R) * R * 4);
+  l.xgw = al16(frag_tile_bytes(NT, tsz));
+  l.xg = o; o += l.xgw * NW;
   l.total = o;
   return l;
 }
 
-// Backward main kernel.
+// Backward main kernel (16 waves: 4 state-row slots x 4 column quarters).
 __host__ __device__ __forceinline__ Lds lds_bwd(const Geo& g, int R, int tsz, int NT) {
   Lds l{};
   size_t o = 0;
   l.a = o; o += al16(ELL * 4);
   l.d = o; o += al16(ELL * 4);
   l.L = o; o += al16(ELL * (ELL + 1) * 4);
-  l.lx = o; o += al16((size_t)ELL * g.KP * 4);
   l.bs = o; o += al16((size_t)R * g.KP * tsz);
   l.ltp = o; o += al16((size_t)ELL * SLOTP * tsz);
   l.ltx = o; o += al16((size_t)g.K * SLOTP * tsz);
   l.rot = o; o += rot_bytes(g);
   l.xr = o; o += al16((size_t)NW * g.KP * tsz);
   l.S = o; o += al16((size_t)R * g.RP * tsz);
+  // per state-row slot: the c tile [t][RP] for d_c, then (after a barrier) the
+  // G tile as B fragments for d_bhat; the rotation-gradient reduction reuses it.
   const size_t xtile = (size_t)ELL * g.RP * tsz;
-  const size_t gb = tsz == 2 ? (size_t)NT * 64 * 16 : (size_t)NT * 8 * 64 * 4;
+  const size_t gb = frag_tile_bytes(NT, tsz);
   l.xgw = al16(xtile > gb ? xtile : gb);
   size_t xg = l.xgw * NW;
-  const size_t rb = (size_t)ELL * R * 4;  // rotation-gradient reduction, aliases xg
+  const size_t rb = (size_t)2 * NT * 64 * 16;          // rotation-gradient reduction
+  const size_t dbt = (size_t)g.K * g.RP * tsz;          // d_bhat tile
   if (xg < rb) xg = rb;
+  if (xg < dbt) xg = dbt;
   l.xg = o; o += al16(xg);
-  l.red = o; o += al16((size_t)(2 * NW * ELL + ELL) * 4);
+  l.m1s = o; o += al16((size_t)NCW * NW * g.K * 4);     // d_xhat partials of the column quarters
+  l.red = o; o += al16((size_t)(4 * NCW * ELL + ELL) * 4);
   l.total = o;
   return l;
 }
@@ -105,20 +112,21 @@ __host__ __device__ __forceinline__ Lds lds_fix(const Geo& g, int R, int tsz, in
 }
 
 // ---------------------------------------------------------------------------
-// Chunk states of one state row p0: acc[mt][nt] = h~[t = 16mt+4q+i][col 16nt+m]
+// Chunk states of one state row p0 over NTC column tiles starting at col0:
+// acc[mt][nt] = h~[t = 16mt+4q+i][col0 + 16nt + m]
 //   = d_t h_-[p0][col] + sum_{k=(j,c), j<=t} L[t,j] xhat[j,c,p0] bhat[j,c,col]
 // (chunk_states of the recalculated.rs source page, folded (j,c) write axis).
 // Rows at positions >= V are zeroed.
 // ---------------------------------------------------------------------------
-template <typename T, int NT>
-__device__ __forceinline__ void chunk_states_row(f4 (&acc)[2][NT], const Geo& g, int n, const float* s_d,
-                                        const float* lx, const T* bs, const T* xrow,
-                                        const float* hrow) {
-  constexpr int KS = MM<T>::KS, E = MM<T>::E;
+template <typename T, int NTC, int CK>
+__device__ __forceinline__ void chunk_states_row(f4 (&acc)[2][NTC], const Geo& g, int n, const float* s_d,
+                                                 const float* s_L, const T* bs, const T* xrow,
+                                                 const float* hrow, int col0) {
+  constexpr int KS = MM<T>::KS, E = MM<T>::E, K = ELL * CK, KP = K + pad_of<T>();
   const int lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
 #pragma unroll
-  for (int nt = 0; nt < NT; nt++) {
-    const int col = 16 * nt + m;
+  for (int nt = 0; nt < NTC; nt++) {
+    const int col = col0 + 16 * nt + m;
     const float hv = (hrow != nullptr && col < g.r) ? hrow[col] : 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
@@ -127,22 +135,24 @@ __device__ __forceinline__ void chunk_states_row(f4 (&acc)[2][NT], const Geo& g,
   }
 #pragma unroll
   for (int mt = 0; mt < 2; mt++) {
-    const int kneed = (16 * mt + 16) * g.c;
-    const int kmax = kneed < g.K ? kneed : g.K;
-    const int nks = (kmax + KS - 1) / KS;
+    // writes k = (j, ci) with j <= 16mt + 15 only (L is zero above the diagonal)
+    constexpr int NKS0 = (16 * CK + KS - 1) / KS, NKS1 = (32 * CK + KS - 1) / KS;
     const int t = 16 * mt + m;
-    for (int ks = 0; ks < nks; ks++) {
+    const float* Lrow = s_L + t * (ELL + 1);
+#pragma unroll
+    for (int ks = 0; ks < (mt == 0 ? NKS0 : NKS1); ks++) {
       const int k0 = ks * KS + E * q;
       typename MM<T>::frag a;
       if constexpr (E == 1) {
-        a = lx[t * g.KP + k0] * to_f(xrow[k0]);
+        a = Lrow[k0 / CK] * to_f(xrow[k0]);
       } else {
+        const auto xv = ld_frag(xrow + k0);
 #pragma unroll
-        for (int e = 0; e < E; e++) a[e] = to_t<T>(lx[t * g.KP + k0 + e] * to_f(xrow[k0 + e]));
+        for (int e = 0; e < E; e++) a[e] = to_t<T>(Lrow[(k0 + e) / CK] * to_f(xv[e]));
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; nt++) {
-        const auto b = ld_frag(bs + (16 * nt + m) * g.KP + k0);
+      for (int nt = 0; nt < NTC; nt++) {
+        const auto b = ld_frag(bs + (col0 + 16 * nt + m) * KP + k0);
         acc[mt][nt] = MM<T>::mma(a, b, acc[mt][nt]);
       }
     }
@@ -153,24 +163,25 @@ __device__ __forceinline__ void chunk_states_row(f4 (&acc)[2][NT], const Geo& g,
     for (int i = 0; i < 4; i++) {
       if (n * ELL + 16 * mt + 4 * q + i >= g.V) {
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) acc[mt][nt][i] = 0.0f;
+        for (int nt = 0; nt < NTC; nt++) acc[mt][nt][i] = 0.0f;
       }
     }
 }
 
 // Stage the x row block of one round (4 state rows, one per wave): xr[w][k].
-template <typename T>
+template <typename T, int CK>
 __device__ __forceinline__ void stage_xround(const Geo& g, const T* __restrict__ xhat, int bi, int hi, int n,
                                     int round, T* xr) {
-  for (int idx = threadIdx.x; idx < 4 * g.K; idx += NTH) {
+  constexpr int K = ELL * CK, KP = K + pad_of<T>();
+  for (int idx = threadIdx.x; idx < 4 * K; idx += blockDim.x) {
     const int k = idx >> 2, ww = idx & 3;
     const int p0 = 4 * round + ww;
-    const int j = k / g.c, ci = k - j * g.c;
+    const int j = k / CK, ci = k % CK;
     const int pos = n * ELL + j;
     float v = 0.0f;
-    if (p0 < g.p && pos < g.V)
+    if (p0 < g.p && pos < g.V && ci < g.c)
       v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + p0]);
-    xr[ww * g.KP + k] = to_t<T>(v);
+    xr[ww * KP + k] = to_t<T>(v);
   }
 }
 
@@ -179,12 +190,12 @@ __device__ __forceinline__ void stage_xround(const Geo& g, const T* __restrict__
 // for chunks n < NK-1, and dec_n = exp(a_last) (boundary_carries, backward.rs
 // source page: the decay-to-chunk-end GEMM).
 // ---------------------------------------------------------------------------
-template <typename T, int NT>
+template <typename T, int NT, int CK>
 __global__ __launch_bounds__(NTH, 1) void k_carry(Geo g, int PK, const T* __restrict__ xhat,
                                                    const T* __restrict__ bhat,
                                                    const T* __restrict__ da, float* carry,
                                                    float* dec) {
-  constexpr int R = 16 * NT, KS = MM<T>::KS, E = MM<T>::E;
+  constexpr int R = 16 * NT, KS = MM<T>::KS, E = MM<T>::E, K = ELL * CK, KP = K + pad_of<T>();
   extern __shared__ __align__(16) unsigned char smem[];
   const Lds L = lds_carry(g, R, sizeof(T), PK);
   float* s_a = (float*)(smem + L.a);
@@ -198,20 +209,20 @@ __global__ __launch_bounds__(NTH, 1) void k_carry(Geo g, int PK, const T* __rest
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
 
   stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
-  stage_bhat<T, R>(g, bhat, bi, hi, n, bs);
+  stage_bhat<T, R, CK>(g, bhat, bi, hi, n, bs);
   __syncthreads();
   const float* wl = s_L + (ELL - 1) * (ELL + 1);  // L[l-1][j] = exp(a_last - a_j)
-  for (int idx = threadIdx.x; idx < g.K * PK; idx += NTH) {
+  for (int idx = threadIdx.x; idx < K * PK; idx += NTH) {
     const int k = idx / PK, pp = idx % PK;
-    const int j = k / g.c, ci = k - j * g.c;
+    const int j = k / CK, ci = k % CK;
     const int pos = n * ELL + j;
     float v = 0.0f;
-    if (pp < g.p) v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp]) * wl[j];
-    as[pp * g.KP + k] = to_t<T>(v);
+    if (pp < g.p && ci < g.c) v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp]) * wl[j];
+    as[pp * KP + k] = to_t<T>(v);
   }
   __syncthreads();
   const int MT = PK / 16;
-  const int nks = g.K / KS;
+  constexpr int nks = K / KS;
 #pragma unroll
   for (int mi = 0; mi < 2; mi++) {
     const int mt = w + 4 * mi;
@@ -219,11 +230,12 @@ __global__ __launch_bounds__(NTH, 1) void k_carry(Geo g, int PK, const T* __rest
     f4 acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) acc[nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
     for (int ks = 0; ks < nks; ks++) {
       const int k0 = ks * KS + E * q;
-      const auto a = ld_frag(as + (16 * mt + m) * g.KP + k0);
+      const auto a = ld_frag(as + (16 * mt + m) * KP + k0);
 #pragma unroll
-      for (int nt = 0; nt < NT; nt++) acc[nt] = MM<T>::mma(a, ld_frag(bs + (16 * nt + m) * g.KP + k0), acc[nt]);
+      for (int nt = 0; nt < NT; nt++) acc[nt] = MM<T>::mma(a, ld_frag(bs + (16 * nt + m) * KP + k0), acc[nt]);
     }
     float* out = carry + ((size_t)bh * g.NK + n) * g.p * g.r;
 #pragma unroll
@@ -272,60 +284,62 @@ __global__ __launch_bounds__(NTH) void k_scan(Geo g, const T* __restrict__ h0, f
 }
 
 // ---------------------------------------------------------------------------
-// k_fwd: chunk states, de-rotation, m2 += c^T c (MFMA, K over tokens, operands
-// straight from the accumulators), m1 += sum_t c. One workgroup walks G chunks
-// of one (b,h) chain and writes one partial of m2 (upper tiles) and m1.
+// k_fwd: chunk states, de-rotation, m2 += c^T c and m1 += sum_t c. One workgroup
+// walks G chunks of one (b,h) chain; each round, wave w computes state row
+// 4*round + w and publishes c as MFMA B fragments (K over tokens); the four
+// waves then own a 2x2 tiling of m2 and accumulate the round's four rows.
+// Each workgroup writes one m2 partial and owns one m1 partial.
 // ---------------------------------------------------------------------------
-template <typename T, int NT>
+template <typename T, int NT, int ROT, int CK>
 __global__ __launch_bounds__(NTH, 1) void k_fwd(Geo g, const T* __restrict__ xhat,
                                                  const T* __restrict__ bhat,
                                                  const T* __restrict__ da,
                                                  const T* __restrict__ rot,
                                                  const float* __restrict__ carry, float* m2part,
                                                  float* m1part) {
-  constexpr int R = 16 * NT, KS = MM<T>::KS, NKT = ELL / KS;
-  constexpr int NU = NT * (NT + 1) / 2;
+  static_assert(NT >= 2, "column tiles are split in halves");
+  constexpr int R = 16 * NT, NKT = ELL / MM<T>::KS, NH = NT / 2, KP = ELL * CK + pad_of<T>();
   extern __shared__ __align__(16) unsigned char smem[];
-  const Lds L = lds_fwd(g, R, sizeof(T));
+  const Lds L = lds_fwd(g, R, sizeof(T), NT);
   float* s_a = (float*)(smem + L.a);
   float* s_d = (float*)(smem + L.d);
   float* s_L = (float*)(smem + L.L);
-  float* lx = (float*)(smem + L.lx);
   T* bs = (T*)(smem + L.bs);
   float* cs = (float*)(smem + L.rot);
   float* sn = cs + ELL * g.A;
   float* qv = cs;
   T* xr = (T*)(smem + L.xr);
-  float* m1s = (float*)(smem + L.m1s);
+  unsigned char* cx = smem + L.xg;
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+  const int wi = w >> 1, wj = w & 1;  // this wave's m2 tiles: rows half wi, cols half wj
   const int nrounds = (g.p + 3) / 4;
-  for (int idx = threadIdx.x; idx < nrounds * 4 * R; idx += NTH) m1s[idx] = 0.0f;
-  f4 m2acc[NU];
+  float* m1o = m1part + ((size_t)bh * g.NGR + gi) * g.p * R;
+  f4 m2acc[NH][NH];
 #pragma unroll
-  for (int u = 0; u < NU; u++) m2acc[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int a = 0; a < NH; a++)
+#pragma unroll
+    for (int b = 0; b < NH; b++) m2acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
   for (int n = n0; n < n1; n++) {
     __syncthreads();
     stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
-    stage_bhat<T, R>(g, bhat, bi, hi, n, bs);
+    stage_bhat<T, R, CK>(g, bhat, bi, hi, n, bs);
     stage_rot(g, rot, bi, hi, n, cs, sn, qv);
-    __syncthreads();
-    stage_lx(g, s_L, lx);
     for (int round = 0; round < nrounds; round++) {
-      stage_xround(g, xhat, bi, hi, n, round, xr);
+      stage_xround<T, CK>(g, xhat, bi, hi, n, round, xr);
       __syncthreads();
       const int p0 = 4 * round + w;
       const bool valid = p0 < g.p;
       const float* hrow = valid ? carry + (((size_t)bh * g.NK + n) * g.p + p0) * g.r : nullptr;
       f4 acc[2][NT];
-      chunk_states_row<T, NT>(acc, g, n, s_d, lx, bs, xr + w * g.KP, hrow);
-      rotate_tiles<false, NT>(acc, g, cs, sn, qv);
-      // m1[p0][col] += sum over the chunk's tokens
+      chunk_states_row<T, NT, CK>(acc, g, n, s_d, s_L, bs, xr + w * KP, hrow, 0);
+      rotate_tiles<false, NT, ROT>(acc, g, cs, sn, qv);
+      // m1[p0][col] += sum over the chunk's tokens (this wave owns row p0)
 #pragma unroll
       for (int nt = 0; nt < NT; nt++) {
         float sum = 0.0f;
@@ -334,54 +348,63 @@ __global__ __launch_bounds__(NTH, 1) void k_fwd(Geo g, const T* __restrict__ xha
 #pragma unroll
           for (int i = 0; i < 4; i++) sum += acc[mt][nt][i];
         sum = col4_sum(sum);
-        if (q == 0 && valid) m1s[p0 * R + 16 * nt + m] += sum;
+        if (q == 0 && valid) {
+          float* dst = m1o + (size_t)p0 * R + 16 * nt + m;
+          *dst = (n == n0 ? 0.0f : *dst) + sum;
+        }
       }
-      // m2 tile (R1 <= R2) += sum_t c[t][R1 cols]^T c[t][R2 cols]
-      int u = 0;
+      // publish c as B fragments: K = tokens (slot order), one tile per column block
+      unsigned char* mine = cx + (size_t)w * L.xgw;
 #pragma unroll
-      for (int r1 = 0; r1 < NT; r1++) {
-        f4 a1[2] = {acc[0][r1], acc[1][r1]};
+      for (int nt = 0; nt < NT; nt++) {
+        const f4 v2[2] = {acc[0][nt], acc[1][nt]};
+        if constexpr (NKT == 1) {
+          ((bf8*)mine)[nt * 64 + lane] = pack_tslots(v2, 0, T{});
+        } else {
 #pragma unroll
-        for (int r2 = r1; r2 < NT; r2++) {
-          f4 a2[2] = {acc[0][r2], acc[1][r2]};
-#pragma unroll
-          for (int ks = 0; ks < NKT; ks++)
-            m2acc[u] = MM<T>::mma(pack_tslots(a1, ks, T{}), pack_tslots(a2, ks, T{}), m2acc[u]);
-          u++;
+          for (int ks = 0; ks < NKT; ks++) ((float*)mine)[(nt * NKT + ks) * 64 + lane] = pack_tslots(v2, ks, T{});
         }
       }
       __syncthreads();
-    }
-  }
-  // partial m1 (internal column order)
-  __syncthreads();
-  float* m1o = m1part + ((size_t)bh * g.NGR + gi) * g.p * R;
-  for (int idx = threadIdx.x; idx < g.p * R; idx += NTH) m1o[idx] = m1s[idx];
-  __syncthreads();
-  // partial m2: fixed-order sum of the four waves' tiles
-  float* M = m1s;
-  for (int idx = threadIdx.x; idx < R * R; idx += NTH) M[idx] = 0.0f;
-  __syncthreads();
-  for (int ww = 0; ww < NW; ww++) {
-    if (w == ww) {
-      int u = 0;
+      // m2 tile (16(wi*NH+a), 16(wj*NH+b)) += sum over the round's rows and tokens
 #pragma unroll
-      for (int r1 = 0; r1 < NT; r1++)
+      for (int src = 0; src < NW; src++) {
+        const unsigned char* fr = cx + (size_t)src * L.xgw;
 #pragma unroll
-        for (int r2 = r1; r2 < NT; r2++) {
+        for (int ks = 0; ks < NKT; ks++) {
+          typename MM<T>::frag fa[NH], fb[NH];
 #pragma unroll
-          for (int i = 0; i < 4; i++) M[(16 * r1 + 4 * q + i) * R + 16 * r2 + m] += m2acc[u][i];
-          u++;
+          for (int a = 0; a < NH; a++) {
+            const int ta = wi * NH + a, tb = wj * NH + a;
+            if constexpr (NKT == 1) {
+              fa[a] = ((const bf8*)fr)[ta * 64 + lane];
+              fb[a] = ((const bf8*)fr)[tb * 64 + lane];
+            } else {
+              fa[a] = ((const float*)fr)[(ta * NKT + ks) * 64 + lane];
+              fb[a] = ((const float*)fr)[(tb * NKT + ks) * 64 + lane];
+            }
+          }
+#pragma unroll
+          for (int a = 0; a < NH; a++)
+#pragma unroll
+            for (int b = 0; b < NH; b++) m2acc[a][b] = MM<T>::mma(fa[a], fb[b], m2acc[a][b]);
         }
+      }
     }
-    __syncthreads();
   }
+  // m2 partial: this wave's (NH x NH) tiles, written straight out
   float* m2o = m2part + ((size_t)bh * g.NGR + gi) * R * R;
-  for (int idx = threadIdx.x; idx < R * R; idx += NTH) m2o[idx] = M[idx];
+#pragma unroll
+  for (int a = 0; a < NH; a++)
+#pragma unroll
+    for (int b = 0; b < NH; b++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        m2o[(16 * (wi * NH + a) + 4 * q + i) * R + 16 * (wj * NH + b) + m] = m2acc[a][b][i];
 }
 
-// k_reduce: m2 = sum over partials (mirrored from upper tiles), m1 likewise;
-// both written in the caller's column order.
+// k_reduce: m2 = sum over the per-workgroup partials, m1 likewise; both
+// written in the caller's column order.
 __global__ __launch_bounds__(NTH) void k_reduce(Geo g, int R, const float* __restrict__ m2part,
                                                 const float* __restrict__ m1part, float* m2,
                                                 float* m1) {
@@ -390,9 +413,8 @@ __global__ __launch_bounds__(NTH) void k_reduce(Geo g, int R, const float* __res
   const int n2 = g.r * g.r, n1 = g.p * g.r;
   if (e < n2) {
     const int a = inv_perm_rc(g, e / g.r), b = inv_perm_rc(g, e % g.r);
-    const int x = (a >> 4) <= (b >> 4) ? a : b, y = (a >> 4) <= (b >> 4) ? b : a;
     float s = 0.0f;
-    for (int gi = 0; gi < g.NGR; gi++) s += m2part[((size_t)bh * g.NGR + gi) * R * R + x * R + y];
+    for (int gi = 0; gi < g.NGR; gi++) s += m2part[((size_t)bh * g.NGR + gi) * R * R + a * R + b];
     m2[(size_t)bh * n2 + e] = s;
   } else if (e < n2 + n1) {
     const int f = e - n2;

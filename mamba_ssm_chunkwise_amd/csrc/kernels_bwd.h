@@ -20,18 +20,23 @@
 
 namespace mom {
 
-template <typename T, int NT>
-__global__ __launch_bounds__(NTH, 1) void k_bwd(
+// Waves: w = 0..15, state-row slot u = w & 3 (row 4*round + u), column
+// quarter v = w >> 2 (column tiles [v*NQ, v*NQ + NQ)). A row's four waves
+// share the state A operand, exchange c through LDS for d_c (K over all
+// columns), and combine their quarters of the d_xhat dot products.
+template <typename T, int NT, int ROT, int CK>
+__global__ __launch_bounds__(NTHB, 1) void k_bwd(
     Geo g, const T* __restrict__ xhat, const T* __restrict__ bhat, const T* __restrict__ da,
     const T* __restrict__ rot, const float* __restrict__ carry, const float* __restrict__ dm2,
     const float* __restrict__ dm1, float* Db, T* d_xhat, T* d_bhat, T* d_da, T* d_rot) {
-  constexpr int R = 16 * NT, KS = MM<T>::KS, E = MM<T>::E, NKT = ELL / KS;
+  static_assert(NT >= NCW, "column tiles are split in quarters");
+  constexpr int R = 16 * NT, KS = MM<T>::KS, E = MM<T>::E, NKT = ELL / KS, NH = NT / NCW;
+  constexpr int K = ELL * CK, KP = K + pad_of<T>(), RP = R + pad_of<T>(), MTB = K / 16;
   extern __shared__ __align__(16) unsigned char smem[];
   const Lds L = lds_bwd(g, R, sizeof(T), NT);
   float* s_a = (float*)(smem + L.a);
   float* s_d = (float*)(smem + L.d);
   float* s_L = (float*)(smem + L.L);
-  float* lx = (float*)(smem + L.lx);
   T* bs = (T*)(smem + L.bs);
   T* ltp = (T*)(smem + L.ltp);
   T* ltx = (T*)(smem + L.ltx);
@@ -41,27 +46,29 @@ __global__ __launch_bounds__(NTH, 1) void k_bwd(
   T* xr = (T*)(smem + L.xr);
   T* S = (T*)(smem + L.S);
   unsigned char* xg = smem + L.xg;
-  float* rsum = (float*)(smem + L.red);
-  float* csum = rsum + NW * ELL;
-  float* ddv = csum + NW * ELL;
+  float* xpart = (float*)(smem + L.m1s);
+  float* rsum = (float*)(smem + L.red);   // [16 waves][ELL]
+  float* ddv = rsum + 4 * NCW * ELL;      // [ELL]
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+  const int u = w & 3, v = w >> 2;
+  const int col0 = 16 * NH * v;
   const int nrounds = (g.p + 3) / 4;
-  const bool cplx = g.rot_kind == 1 || g.rot_kind == 2;
+  constexpr bool cplx = ROT == 1;
 
   // S = d_m2 + d_m2^T in internal column order (symmetric, so it serves as the
   // K-contiguous B operand of d_c = c S).
-  for (int idx = threadIdx.x; idx < R * R; idx += NTH) {
+  for (int idx = threadIdx.x; idx < R * R; idx += NTHB) {
     const int a = idx / R, b = idx % R;
-    float v = 0.0f;
+    float val = 0.0f;
     if (a < g.r && b < g.r) {
       const int pa = perm_rc(g, a), pb = perm_rc(g, b);
       const float* D2 = dm2 + (size_t)bh * g.r * g.r;
-      v = D2[pa * g.r + pb] + D2[pb * g.r + pa];
+      val = D2[pa * g.r + pb] + D2[pb * g.r + pa];
     }
-    S[a * g.RP + b] = to_t<T>(v);
+    S[a * RP + b] = to_t<T>(val);
   }
 
   const int n0 = gi * g.G;
@@ -69,74 +76,75 @@ __global__ __launch_bounds__(NTH, 1) void k_bwd(
   for (int n = n0; n < n1; n++) {
     __syncthreads();
     stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
-    stage_bhat<T, R>(g, bhat, bi, hi, n, bs);
+    stage_bhat<T, R, CK>(g, bhat, bi, hi, n, bs);
     stage_rot(g, rot, bi, hi, n, cs, sn, qv);
-    __syncthreads();
-    stage_lx(g, s_L, lx);
-    stage_lt<T>(g, s_L, ltp, ltx);
+    stage_lt<T, CK>(s_L, ltp, ltx);
 
-    f4 racc[2][NT], dbacc[2][NT];
-    f4 gacc[2], cacc[2];
+    f4 racc[2][NH], dbacc[2][NH];
+    f4 gacc[2];
+    float ccol = 0.0f;
 #pragma unroll
     for (int mt = 0; mt < 2; mt++) {
       gacc[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-      cacc[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int nt = 0; nt < NT; nt++) {
+      for (int nt = 0; nt < NH; nt++) {
         racc[mt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
         dbacc[mt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
       }
     }
 
     for (int round = 0; round < nrounds; round++) {
-      stage_xround(g, xhat, bi, hi, n, round, xr);
-      __syncthreads();
-      const int p0 = 4 * round + w;
+      stage_xround<T, CK>(g, xhat, bi, hi, n, round, xr);
+      __syncthreads();  // (A) xr, and on the first round all chunk staging
+      const int p0 = 4 * round + u;
       const bool valid = p0 < g.p;
       const float* hrow = valid ? carry + (((size_t)bh * g.NK + n) * g.p + p0) * g.r : nullptr;
-      T* X = (T*)(xg + (size_t)w * L.xgw);
+      T* X = (T*)(xg + (size_t)u * L.xgw);
 
-      // states h~ and c
-      f4 keep[2][NT];
-      chunk_states_row<T, NT>(keep, g, n, s_d, lx, bs, xr + w * g.KP, hrow);
-      f4 dc[2][NT];
+      // states h~ and c for this wave's column half
+      f4 keep[2][NH];
+      chunk_states_row<T, NH, CK>(keep, g, n, s_d, s_L, bs, xr + u * KP, hrow, col0);
+      f4 dc[2][NH];
 #pragma unroll
       for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) dc[mt][nt] = keep[mt][nt];
-      rotate_tiles<false, NT>(dc, g, cs, sn, qv);  // dc holds c for now
-      if (cplx) {
+        for (int nt = 0; nt < NH; nt++) dc[mt][nt] = keep[mt][nt];
+      rotate_tiles<false, NH, ROT>(dc, g, cs, sn, qv, col0);  // dc holds c for now
+      if constexpr (cplx) {
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-          for (int nt = 0; nt < NT; nt++) keep[mt][nt] = dc[mt][nt];
+          for (int nt = 0; nt < NH; nt++) keep[mt][nt] = dc[mt][nt];
       }
-      // c -> LDS rows [t][col] for the A operand of d_c (K over columns)
+      // c -> X[u] rows [t][col] (A operand of d_c, K over all columns)
 #pragma unroll
       for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++)
+        for (int nt = 0; nt < NH; nt++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) X[(16 * mt + 4 * q + i) * g.RP + 16 * nt + m] = to_t<T>(dc[mt][nt][i]);
-      wave_lds_sync();
-      // d_c = c S + d_m1, masked
+          for (int i = 0; i < 4; i++)
+            X[(16 * mt + 4 * q + i) * RP + col0 + 16 * nt + m] = to_t<T>(dc[mt][nt][i]);
+      __syncthreads();  // (B) every quarter of every c row is in X
+      // d_c = c S + d_m1 on this wave's columns, masked past V
 #pragma unroll
       for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) dc[mt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int nt = 0; nt < NH; nt++) dc[mt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
       for (int ks = 0; ks < R / KS; ks++) {
         const int k0 = ks * KS + E * q;
+        const auto a0 = ld_frag(X + m * RP + k0);
+        const auto a1 = ld_frag(X + (16 + m) * RP + k0);
 #pragma unroll
-        for (int mt = 0; mt < 2; mt++) {
-          const auto a = ld_frag(X + (16 * mt + m) * g.RP + k0);
-#pragma unroll
-          for (int nt = 0; nt < NT; nt++)
-            dc[mt][nt] = MM<T>::mma(a, ld_frag(S + (16 * nt + m) * g.RP + k0), dc[mt][nt]);
+        for (int nt = 0; nt < NH; nt++) {
+          const auto b = ld_frag(S + (col0 + 16 * nt + m) * RP + k0);
+          dc[0][nt] = MM<T>::mma(a0, b, dc[0][nt]);
+          dc[1][nt] = MM<T>::mma(a1, b, dc[1][nt]);
         }
       }
 #pragma unroll
-      for (int nt = 0; nt < NT; nt++) {
-        const int col = 16 * nt + m;
+      for (int nt = 0; nt < NH; nt++) {
+        const int col = col0 + 16 * nt + m;
         const float dv = (valid && col < g.r) ? dm1[((size_t)bh * g.p + p0) * g.r + perm_rc(g, col)] : 0.0f;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
@@ -147,192 +155,209 @@ __global__ __launch_bounds__(NTH, 1) void k_bwd(
           }
       }
       // rotation gradient; <d_c, c> = <G, h~> (row term of d_da)
-      accum_drot<NT>(racc, dc, keep, g);
-      if (g.rot_kind != 3) {
+      accum_drot<NH, ROT>(racc, dc, keep, g);
+      if constexpr (ROT != 3) {
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-          for (int nt = 0; nt < NT; nt++)
+          for (int nt = 0; nt < NH; nt++)
 #pragma unroll
             for (int i = 0; i < 4; i++) gacc[mt][i] += dc[mt][nt][i] * keep[mt][nt][i];
       }
-      rotate_tiles<true, NT>(dc, g, cs, sn, qv);  // dc now holds G
-      if (g.rot_kind == 3) {
+      rotate_tiles<true, NH, ROT>(dc, g, cs, sn, qv, col0);  // dc now holds G
+      if constexpr (ROT == 3) {
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-          for (int nt = 0; nt < NT; nt++)
+          for (int nt = 0; nt < NH; nt++)
 #pragma unroll
             for (int i = 0; i < 4; i++) gacc[mt][i] += dc[mt][nt][i] * keep[mt][nt][i];
       }
       // local(n)[p0][col] = sum_t d_t G[t][col]
 #pragma unroll
-      for (int nt = 0; nt < NT; nt++) {
+      for (int nt = 0; nt < NH; nt++) {
         float sum = 0.0f;
 #pragma unroll
         for (int mt = 0; mt < 2; mt++)
 #pragma unroll
           for (int i = 0; i < 4; i++) sum += s_d[16 * mt + 4 * q + i] * dc[mt][nt][i];
         sum = col4_sum(sum);
-        const int col = 16 * nt + m;
+        const int col = col0 + 16 * nt + m;
         if (q == 0 && valid && col < g.r) Db[(((size_t)bh * g.NK + n) * g.p + p0) * g.r + col] = sum;
       }
       // d_W[j][col] = sum_t L[t][j] G[t][col] (K over tokens, B from registers)
-      f4 dw[2][NT];
+      f4 dw[2][NH];
 #pragma unroll
       for (int jt = 0; jt < 2; jt++)
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) dw[jt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int nt = 0; nt < NH; nt++) dw[jt][nt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < NKT; ks++) {
 #pragma unroll
         for (int jt = 0; jt < 2; jt++) {
           const auto a = ld_frag(ltp + (16 * jt + m) * SLOTP + ks * KS + E * q);
 #pragma unroll
-          for (int nt = 0; nt < NT; nt++) {
+          for (int nt = 0; nt < NH; nt++) {
             const f4 gv[2] = {dc[0][nt], dc[1][nt]};
             dw[jt][nt] = MM<T>::mma(a, pack_tslots(gv, ks, T{}), dw[jt][nt]);
           }
         }
       }
-      // G as B fragments (K over tokens) for d_bhat, in this wave's exchange slot
-      wave_lds_sync();
-#pragma unroll
-      for (int nt = 0; nt < NT; nt++) {
-        const f4 gv[2] = {dc[0][nt], dc[1][nt]};
-        if constexpr (E == 1) {
-#pragma unroll
-          for (int ks = 0; ks < NKT; ks++) ((float*)X)[(nt * NKT + ks) * 64 + lane] = pack_tslots(gv, ks, T{});
-        } else {
-          ((bf8*)X)[nt * 64 + lane] = pack_tslots(gv, 0, T{});
-        }
-      }
-      // d_xhat[j,c,p0] = sum_col d_W[j][col] bhat[j,c,col]; col term <xhat, d_xhat>
+      // this quarter's share of d_xhat[j,c,p0] = sum_col d_W[j][col] bhat[j,c,col],
+      // dropped into LDS; the quarters are added in a flat pass below
+      float* xp = xpart + (v * NW + u) * K;
 #pragma unroll
       for (int jt = 0; jt < 2; jt++)
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int j = 16 * jt + 4 * q + i;
-          const int pos = n * ELL + j;
-          for (int ci = 0; ci < g.c; ci++) {
-            const int k = j * g.c + ci;
-            float part = 0.0f;
 #pragma unroll
-            for (int nt = 0; nt < NT; nt++) part += dw[jt][nt][i] * to_f(bs[(16 * nt + m) * g.KP + k]);
-            const float val = row16_sum(part);
-            cacc[jt][i] += val * to_f(xr[w * g.KP + k]);
-            if (d_xhat != nullptr && valid && m == ((i * g.c + ci) & 15) && pos < g.s)
-              d_xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + p0] = to_t<T>(val);
+          for (int ci = 0; ci < CK; ci++) {
+            if (ci < g.c) {
+              float part = 0.0f;
+#pragma unroll
+              for (int nt = 0; nt < NH; nt++)
+                part += dw[jt][nt][i] * to_f(bs[(col0 + 16 * nt + m) * KP + j * CK + ci]);
+              part = row16_sum(part);
+              if (m == 0) xp[j * CK + ci] = part;
+            }
           }
         }
-      __syncthreads();
+      __syncthreads();  // (C) X reads done; every quarter's partials visible
+      // G as B fragments (K over tokens) for d_bhat, into this row's slot
+#pragma unroll
+      for (int nt = 0; nt < NH; nt++) {
+        const f4 gv[2] = {dc[0][nt], dc[1][nt]};
+        const int tile = NH * v + nt;
+        if constexpr (NKT == 1) {
+          ((bf8*)X)[tile * 64 + lane] = pack_tslots(gv, 0, T{});
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < NKT; ks++) ((float*)X)[(tile * NKT + ks) * 64 + lane] = pack_tslots(gv, ks, T{});
+        }
+      }
+      // d_xhat of the round's rows; thread (uu, k) also keeps its share of the
+      // d_da column term sum_c <xhat[j,c], d_xhat[j,c]>
+      if (threadIdx.x < NW * K) {
+        const int uu = threadIdx.x / K, k = threadIdx.x % K;
+        const int pr0 = 4 * round + uu;
+        const int j = k / CK, ci = k % CK;
+        float val = 0.0f;
+        if (ci < g.c) {
+#pragma unroll
+          for (int vv = 0; vv < NCW; vv++) val += xpart[(vv * NW + uu) * K + k];
+        }
+        ccol += val * to_f(xr[uu * KP + k]);
+        const int pos = n * ELL + j;
+        if (d_xhat != nullptr && ci < g.c && pr0 < g.p && pos < g.s)
+          d_xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pr0] = to_t<T>(val);
+      }
+      __syncthreads();  // (D) every row's G fragments are published
       // d_bhat[(j,c)][col] += sum over (t, this round's rows) L[t,j] xhat[j,c,p] G[t][col]
 #pragma unroll
       for (int mi = 0; mi < 2; mi++) {
-        const int mtb = w + 4 * mi;
-        if (16 * mtb < g.K) {
+        const int mtb = u + 4 * mi;
+        if (mtb < MTB) {
           const int k = 16 * mtb + m;
-          for (int ww = 0; ww < NW; ww++) {
-            const float xs = to_f(xr[ww * g.KP + k]);
-            const unsigned char* gb = xg + (size_t)ww * L.xgw;
+#pragma unroll
+          for (int src = 0; src < NW; src++) {
+            const float xs = to_f(xr[src * KP + k]);
+            const unsigned char* gb = xg + (size_t)src * L.xgw;
 #pragma unroll
             for (int ks = 0; ks < NKT; ks++) {
               typename MM<T>::frag a;
               const T* lt = ltx + k * SLOTP + ks * KS + E * q;
               if constexpr (E == 1) {
-                a = lt[0] * xs;
+                a = to_f(lt[0]) * xs;
               } else {
+                const auto lv = ld_frag(lt);
 #pragma unroll
-                for (int e = 0; e < E; e++) a[e] = to_t<T>(to_f(lt[e]) * xs);
+                for (int e = 0; e < E; e++) a[e] = to_t<T>(to_f(lv[e]) * xs);
               }
 #pragma unroll
-              for (int nt = 0; nt < NT; nt++) {
+              for (int nt = 0; nt < NH; nt++) {
+                const int tile = NH * v + nt;
                 typename MM<T>::frag b;
-                if constexpr (E == 1) b = ((const float*)gb)[(nt * NKT + ks) * 64 + lane];
-                else b = ((const bf8*)gb)[nt * 64 + lane];
+                if constexpr (NKT == 1) b = ((const bf8*)gb)[tile * 64 + lane];
+                else b = ((const float*)gb)[(tile * NKT + ks) * 64 + lane];
                 dbacc[mi][nt] = MM<T>::mma(a, b, dbacc[mi][nt]);
               }
             }
           }
         }
       }
-      __syncthreads();
+      __syncthreads();  // (E) before the next round overwrites xr and the slots
     }
 
-    // ---- chunk end: d_bhat --------------------------------------------------
+    // ---- chunk end: d_bhat, staged through LDS and written row by row --------
+    if (d_bhat != nullptr) {
+      T* DBs = (T*)xg;  // [K][RP]
 #pragma unroll
-    for (int mi = 0; mi < 2; mi++) {
-      const int mtb = w + 4 * mi;
-      if (16 * mtb < g.K && d_bhat != nullptr) {
+      for (int mi = 0; mi < 2; mi++) {
+        const int mtb = u + 4 * mi;
+        if (mtb < MTB) {
 #pragma unroll
-        for (int nt = 0; nt < NT; nt++) {
-          const int col = 16 * nt + m;
+          for (int nt = 0; nt < NH; nt++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int k = 16 * mtb + 4 * q + i;
-            const int j = k / g.c, ci = k - j * g.c;
-            const int pos = n * ELL + j;
-            if (k < g.K && col < g.r && pos < g.s)
-              d_bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, col)] =
-                  to_t<T>(dbacc[mi][nt][i]);
-          }
+            for (int i = 0; i < 4; i++)
+              DBs[(16 * mtb + 4 * q + i) * RP + col0 + 16 * nt + m] = to_t<T>(dbacc[mi][nt][i]);
         }
       }
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < K * g.r; idx += NTHB) {
+        const int k = idx / g.r, ra = idx - k * g.r;
+        const int j = k / CK, ci = k % CK;
+        const int pos = n * ELL + j;
+        if (pos < g.s && ci < g.c)
+          d_bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + ra] = DBs[k * RP + inv_perm_rc(g, ra)];
+      }
+      __syncthreads();
     }
-    // ---- rotation gradient: fixed-order sum over the four waves --------------
-    if (g.rot_kind != 0 && d_rot != nullptr) {
-      float* RB = (float*)xg;
-      const int rwi = cplx ? g.A : 4 * g.J;
-      for (int ww = 0; ww < NW; ww++) {
-        if (w == ww) {
+    // ---- rotation gradient: fixed-order sum over the four row slots, in the
+    // accumulator layout (one vector per lane and tile), then gathered --------
+    if (ROT != 0 && d_rot != nullptr) {
+      f4* RB = (f4*)xg;  // [2][NT][64]
+      for (int uu = 0; uu < NW; uu++) {
+        if (u == uu) {
 #pragma unroll
           for (int mt = 0; mt < 2; mt++)
 #pragma unroll
-            for (int nt = 0; nt < NT; nt++) {
-              const int col = 16 * nt + m;
-              int idx = -1;
-              if (cplx) {
-                if ((col & 1) == 0 && (col >> 1) < g.A) idx = col >> 1;
-              } else if (col < 4 * g.J) {
-                idx = col;
-              }
-              if (idx >= 0) {
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                  float* dst = RB + (16 * mt + 4 * q + i) * rwi + idx;
-                  *dst = (ww == 0 ? 0.0f : *dst) + racc[mt][nt][i];
-                }
-              }
+            for (int nt = 0; nt < NH; nt++) {
+              f4* dst = RB + (mt * NT + NH * v + nt) * 64 + lane;
+              *dst = (uu == 0 ? f4{0.0f, 0.0f, 0.0f, 0.0f} : *dst) + racc[mt][nt];
             }
         }
         __syncthreads();
       }
-      for (int idx = threadIdx.x; idx < ELL * rwi; idx += NTH) {
+      const int rwi = cplx ? g.A : 4 * g.J;
+      const float* RBf = (const float*)RB;
+      for (int idx = threadIdx.x; idx < ELL * rwi; idx += NTHB) {
         const int t = idx / rwi, e = idx % rwi;
+        const int col = cplx ? 2 * e : e;  // complex: the even column holds d_theta
+        const int tl = ((col >> 4) + (t >> 4) * NT) * 64 + 16 * ((t & 15) >> 2) + (col & 15);
         const int pos = n * ELL + t;
-        if (pos < g.s) d_rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e] = to_t<T>(RB[idx]);
+        if (pos < g.s) d_rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e] = to_t<T>(RBf[tl * 4 + (t & 3)]);
       }
     }
     // ---- d_da (without the carry-cotangent terms) ---------------------------
+    // row term per token from every wave; column term per (j,c) from the flat pass
 #pragma unroll
     for (int mt = 0; mt < 2; mt++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const float gs = row16_sum(gacc[mt][i]);
-        if (m == 0) {
-          rsum[w * ELL + 16 * mt + 4 * q + i] = gs;
-          csum[w * ELL + 16 * mt + 4 * q + i] = cacc[mt][i];
-        }
+        if (m == 0) rsum[w * ELL + 16 * mt + 4 * q + i] = gs;
       }
+    float* cw = xpart;  // reuse: [NW][K] column-term shares
+    if (threadIdx.x < NW * K) cw[threadIdx.x] = ccol;
     __syncthreads();
     if (threadIdx.x == 0) {
       float acc = 0.0f;
       for (int t = ELL - 1; t >= 0; t--) {
         float rt = 0.0f, ct = 0.0f;
-        for (int ww = 0; ww < NW; ww++) {
-          rt += rsum[ww * ELL + t];
-          ct += csum[ww * ELL + t];
-        }
+        for (int ww = 0; ww < 4 * NCW; ww++) rt += rsum[ww * ELL + t];
+        for (int uu = 0; uu < NW; uu++)
+          for (int ci = 0; ci < g.c; ci++) ct += cw[uu * K + t * CK + ci];
         acc += rt - ct;
         ddv[t] = acc;
       }
@@ -384,16 +409,17 @@ __global__ __launch_bounds__(NTH) void k_dscan(Geo g, float* Db, const float* __
 //   v[p][(j,c)] = sum_col D+[p][col] bhat[j,c,col]   d_xhat += L[l-1,j] v
 //   y[col][(j,c)] = sum_p D+[p][col] xhat[j,c,p]     d_bhat += L[l-1,j] y
 //   d_da_s += <D+, h_-(n+1)> - sum_{j>=s} L[l-1,j] sum_c <xhat[j,c], v[:, (j,c)]>
-template <typename T, int NT>
+template <typename T, int NT, int CK>
 __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restrict__ xhat,
                                                  const T* __restrict__ bhat,
                                                  const T* __restrict__ da,
                                                  const float* __restrict__ carry,
                                                  const float* __restrict__ Db, T* d_xhat,
                                                  T* d_bhat, T* d_da) {
-  constexpr int R = 16 * NT, KS = MM<T>::KS, E = MM<T>::E;
+  constexpr int R = 16 * NT, KS = MM<T>::KS, E = MM<T>::E, K = ELL * CK, RP = R + pad_of<T>();
   extern __shared__ __align__(16) unsigned char smem[];
   const Lds L = lds_fix(g, R, sizeof(T), PK);
+  const int PP = g.PP;
   float* s_a = (float*)(smem + L.a);
   float* s_d = (float*)(smem + L.d);
   float* s_L = (float*)(smem + L.L);
@@ -402,7 +428,7 @@ __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restri
   T* bn = (T*)(smem + L.bs);
   T* xn = (T*)(smem + L.xr);
   float* xv = (float*)(smem + L.red);
-  float* red = xv + g.K;
+  float* red = xv + K;
   float* ddv = red + NTH;
 
   const int per = g.NK - 1;
@@ -417,24 +443,24 @@ __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restri
   for (int idx = threadIdx.x; idx < PK * R; idx += NTH) {
     const int pp = idx / R, rc = idx % R;
     const float v = (pp < g.p && rc < g.r) ? Dp[pp * g.r + rc] : 0.0f;
-    dp[pp * g.RP + rc] = to_t<T>(v);
-    dpt[rc * g.PP + pp] = to_t<T>(v);
+    dp[pp * RP + rc] = to_t<T>(v);
+    dpt[rc * PP + pp] = to_t<T>(v);
   }
-  for (int idx = threadIdx.x; idx < g.K * R; idx += NTH) {
+  for (int idx = threadIdx.x; idx < K * R; idx += NTH) {
     const int k = idx / R, rc = idx % R;
-    const int j = k / g.c, ci = k - j * g.c;
+    const int j = k / CK, ci = k % CK;
     const int pos = n * ELL + j;
     float v = 0.0f;
-    if (rc < g.r) v = to_f(bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, rc)]);
-    bn[k * g.RP + rc] = to_t<T>(v);
+    if (rc < g.r && ci < g.c) v = to_f(bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, rc)]);
+    bn[k * RP + rc] = to_t<T>(v);
   }
-  for (int idx = threadIdx.x; idx < g.K * PK; idx += NTH) {
+  for (int idx = threadIdx.x; idx < K * PK; idx += NTH) {
     const int k = idx / PK, pp = idx % PK;
-    const int j = k / g.c, ci = k - j * g.c;
+    const int j = k / CK, ci = k % CK;
     const int pos = n * ELL + j;
     float v = 0.0f;
-    if (pp < g.p) v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp]);
-    xn[k * g.PP + pp] = to_t<T>(v);
+    if (pp < g.p && ci < g.c) v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp]);
+    xn[k * PP + pp] = to_t<T>(v);
   }
   float hd = 0.0f;
   for (int e = threadIdx.x; e < pr; e += NTH) hd += Dp[e] * Hn[e];
@@ -448,11 +474,11 @@ __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restri
   __syncthreads();
   hd = red[0];
   const float* ll = s_L + (ELL - 1) * (ELL + 1);
-  const int NTK = g.K / 16;
+  constexpr int NTK = K / 16;
   // v = D+ bhat^T: rows p (PK), cols (j,c), K over state columns
   for (int nt = w; nt < NTK; nt += NW) {
     const int k = 16 * nt + m;
-    const int j = k / g.c, ci = k - j * g.c;
+    const int j = k / CK, ci = k % CK;
     const int pos = n * ELL + j;
     const float lj = ll[j];
     float xsum = 0.0f;
@@ -460,13 +486,13 @@ __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restri
       f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
       for (int ks = 0; ks < R / KS; ks++) {
         const int k0 = ks * KS + E * q;
-        acc = MM<T>::mma(ld_frag(dp + (16 * mt + m) * g.RP + k0), ld_frag(bn + (16 * nt + m) * g.RP + k0), acc);
+        acc = MM<T>::mma(ld_frag(dp + (16 * mt + m) * RP + k0), ld_frag(bn + (16 * nt + m) * RP + k0), acc);
       }
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int pp = 16 * mt + 4 * q + i;
-        if (pp < g.p) {
-          xsum += to_f(xn[k * g.PP + pp]) * acc[i];
+        if (pp < g.p && ci < g.c) {
+          xsum += to_f(xn[k * PP + pp]) * acc[i];
           if (d_xhat != nullptr) {
             T* dst = d_xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp;
             *dst = to_t<T>(to_f(*dst) + lj * acc[i]);
@@ -481,19 +507,19 @@ __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restri
   if (d_bhat != nullptr) {
     for (int nt = w; nt < NTK; nt += NW) {
       const int k = 16 * nt + m;
-      const int j = k / g.c, ci = k - j * g.c;
+      const int j = k / CK, ci = k % CK;
       const int pos = n * ELL + j;
       const float lj = ll[j];
       for (int mt = 0; mt < NT; mt++) {
         f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
         for (int ks = 0; ks < PK / KS; ks++) {
           const int k0 = ks * KS + E * q;
-          acc = MM<T>::mma(ld_frag(dpt + (16 * mt + m) * g.PP + k0), ld_frag(xn + (16 * nt + m) * g.PP + k0), acc);
+          acc = MM<T>::mma(ld_frag(dpt + (16 * mt + m) * PP + k0), ld_frag(xn + (16 * nt + m) * PP + k0), acc);
         }
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const int rc = 16 * mt + 4 * q + i;
-          if (rc < g.r) {
+          if (rc < g.r && ci < g.c) {
             T* dst = d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, rc);
             *dst = to_t<T>(to_f(*dst) + lj * acc[i]);
           }
@@ -506,7 +532,7 @@ __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restri
     float acc = 0.0f;
     for (int j = ELL - 1; j >= 0; j--) {
       float cj = 0.0f;
-      for (int ci = 0; ci < g.c; ci++) cj += xv[j * g.c + ci];
+      for (int ci = 0; ci < g.c; ci++) cj += xv[j * CK + ci];
       acc += ll[j] * cj;
       ddv[j] = hd - acc;
     }

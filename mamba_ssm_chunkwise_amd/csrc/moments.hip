@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <type_traits>
 #include <mutex>
 #include <vector>
 
@@ -70,17 +71,16 @@ struct ProfScope {
 struct Plan {
   Geo g;
   bool bf;      // bf16 inputs
+  int CK;       // channel slots of the folded write axis (c padded to 1, 2 or 4)
   int NT, R;    // state columns padded to R = 16*NT
   int PK;       // state rows padded for MFMA K over rows
   size_t carry, dec, m2p, m1p, db;  // workspace offsets
   size_t ws_fwd, ws_bwd;
 };
 
-int round_nt(int r, bool bf) {
+int round_nt(int r, bool /*bf*/) {
   int nt = (r + 15) / 16;
-  if (nt <= 1) nt = bf ? 2 : 1;
-  else if (nt <= 2) nt = 2;
-  else if (nt <= 4) nt = 4;
+  if (nt <= 4) nt = 4;
   else nt = 8;
   return nt;
 }
@@ -120,9 +120,11 @@ int make_plan(const moments_desc* d, Plan* P) {
   g.b = (int)d->b; g.s = (int)d->s; g.c = (int)d->c; g.h = (int)d->h; g.p = (int)d->p; g.r = (int)d->r;
   g.V = (int)(d->valid_len < d->s ? d->valid_len : d->s);
   g.NK = (g.V + ELL - 1) / ELL;
-  g.K = ELL * g.c;
   P->bf = bf;
+  P->CK = g.c <= 1 ? 1 : g.c <= 2 ? 2 : 4;
+  g.K = ELL * P->CK;
   P->NT = round_nt(g.r, bf);
+  if (!bf && P->NT > 4) return MOMENTS_ENOTSUP;  // float32 kernels cover r <= 64
   P->R = 16 * P->NT;
   const int kq = bf ? 32 : 16;
   P->PK = ((g.p + kq - 1) / kq) * kq;
@@ -133,6 +135,7 @@ int make_plan(const moments_desc* d, Plan* P) {
   g.rot_kind = d->rot_kind;
   g.A = A; g.J = J; g.RW = RW;
   g.half = d->rot_kind == MOMENTS_ROT_COMPLEX_HALF;
+  g.cinv = (65536 + g.c - 1) / g.c;
   const int64_t chains = (int64_t)g.b * g.h;
   const int64_t total = chains * g.NK;
   int G = (int)((total + 2047) / 2048);
@@ -141,7 +144,7 @@ int make_plan(const moments_desc* d, Plan* P) {
   g.G = G;
   g.NGR = g.NK > 0 ? (g.NK + G - 1) / G : 0;
 
-  if (lds_fwd(g, P->R, tsz).total > kLdsLimit || lds_bwd(g, P->R, tsz, P->NT).total > kLdsLimit ||
+  if (lds_fwd(g, P->R, tsz, P->NT).total > kLdsLimit || lds_bwd(g, P->R, tsz, P->NT).total > kLdsLimit ||
       lds_carry(g, P->R, tsz, P->PK).total > kLdsLimit || lds_fix(g, P->R, tsz, P->PK).total > kLdsLimit)
     return MOMENTS_ENOTSUP;
 
@@ -183,7 +186,7 @@ int check_launch() {
     if (_rc != 0) return _rc; \
   } while (0)
 
-template <typename T, int NT>
+template <typename T, int NT, int CK>
 int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, const T* h0,
                       unsigned char* ws, hipStream_t st) {
   const Geo& g = P.g;
@@ -192,9 +195,9 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   const int chains = g.b * g.h;
   if (g.NK >= 2) {
     const size_t lds = lds_carry(g, P.R, sizeof(T), P.PK).total;
-    MOM_TRY(set_lds(k_carry<T, NT>, lds));
+    MOM_TRY(set_lds(k_carry<T, NT, CK>, lds));
     ProfScope ps(KID_CARRY, st);
-    hipLaunchKernelGGL((k_carry<T, NT>), dim3(chains * (g.NK - 1)), dim3(NTH), lds, st, g, P.PK, xhat,
+    hipLaunchKernelGGL((k_carry<T, NT, CK>), dim3(chains * (g.NK - 1)), dim3(NTH), lds, st, g, P.PK, xhat,
                        bhat, da, carry, dec);
     MOM_TRY(check_launch());
   }
@@ -208,7 +211,7 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   return 0;
 }
 
-template <typename T, int NT>
+template <typename T, int NT, int ROT, int CK>
 int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, const void* rot,
             const void* h0, float* m2, float* m1, unsigned char* ws, hipStream_t st) {
   const Geo& g = P.g;
@@ -216,15 +219,15 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   const T* B = (const T*)bhat;
   const T* D = (const T*)da;
   const T* Rt = (const T*)rot;
-  MOM_TRY((launch_carry_scan<T, NT>(P, X, B, D, (const T*)h0, ws, st)));
+  MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
   float* m2p = (float*)(ws + P.m2p);
   float* m1p = (float*)(ws + P.m1p);
   const int chains = g.b * g.h;
   if (g.NK >= 1) {
-    const size_t lds = lds_fwd(g, P.R, sizeof(T)).total;
-    MOM_TRY(set_lds(k_fwd<T, NT>, lds));
+    const size_t lds = lds_fwd(g, P.R, sizeof(T), P.NT).total;
+    MOM_TRY(set_lds(k_fwd<T, NT, ROT, CK>, lds));
     ProfScope ps(KID_FWD, st);
-    hipLaunchKernelGGL((k_fwd<T, NT>), dim3(chains * g.NGR), dim3(NTH), lds, st, g, X, B, D, Rt,
+    hipLaunchKernelGGL((k_fwd<T, NT, ROT, CK>), dim3(chains * g.NGR), dim3(NTH), lds, st, g, X, B, D, Rt,
                        (const float*)(ws + P.carry), m2p, m1p);
     MOM_TRY(check_launch());
   }
@@ -237,7 +240,7 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   return check_launch();
 }
 
-template <typename T, int NT>
+template <typename T, int NT, int ROT, int CK>
 int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, const void* rot,
             const void* h0, const float* dm2, const float* dm1, void* dx, void* db, void* dda,
             void* drot, void* dh0, unsigned char* ws, hipStream_t st) {
@@ -246,16 +249,16 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   const T* B = (const T*)bhat;
   const T* D = (const T*)da;
   const T* Rt = (const T*)rot;
-  MOM_TRY((launch_carry_scan<T, NT>(P, X, B, D, (const T*)h0, ws, st)));
+  MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
   float* carry = (float*)(ws + P.carry);
   float* dec = (float*)(ws + P.dec);
   float* Db = (float*)(ws + P.db);
   const int chains = g.b * g.h;
   if (g.NK >= 1) {
     const size_t lds = lds_bwd(g, P.R, sizeof(T), P.NT).total;
-    MOM_TRY(set_lds(k_bwd<T, NT>, lds));
+    MOM_TRY(set_lds(k_bwd<T, NT, ROT, CK>, lds));
     ProfScope ps(KID_BWD, st);
-    hipLaunchKernelGGL((k_bwd<T, NT>), dim3(chains * g.NGR), dim3(NTH), lds, st, g, X, B, D, Rt,
+    hipLaunchKernelGGL((k_bwd<T, NT, ROT, CK>), dim3(chains * g.NGR), dim3(NTHB), lds, st, g, X, B, D, Rt,
                        (const float*)carry, dm2, dm1, Db, (T*)dx, (T*)db, (T*)dda, (T*)drot);
     MOM_TRY(check_launch());
   }
@@ -268,9 +271,9 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   MOM_TRY(check_launch());
   if (g.NK >= 2 && (dx != nullptr || db != nullptr || dda != nullptr)) {
     const size_t lds = lds_fix(g, P.R, sizeof(T), P.PK).total;
-    MOM_TRY(set_lds(k_fix<T, NT>, lds));
+    MOM_TRY(set_lds(k_fix<T, NT, CK>, lds));
     ProfScope ps(KID_FIX, st);
-    hipLaunchKernelGGL((k_fix<T, NT>), dim3(chains * (g.NK - 1)), dim3(NTH), lds, st, g, P.PK, X, B, D,
+    hipLaunchKernelGGL((k_fix<T, NT, CK>), dim3(chains * (g.NK - 1)), dim3(NTH), lds, st, g, P.PK, X, B, D,
                        (const float*)carry, (const float*)Db, (T*)dx, (T*)db, (T*)dda);
     MOM_TRY(check_launch());
   }
@@ -284,27 +287,34 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   return 0;
 }
 
-template <typename T>
-int fwd_nt(const Plan& P, const void* x, const void* b, const void* da, const void* rot,
-           const void* h0, float* m2, float* m1, unsigned char* ws, hipStream_t st) {
-  switch (P.NT) {
-    case 1: if constexpr (sizeof(T) == 4) return run_fwd<T, 1>(P, x, b, da, rot, h0, m2, m1, ws, st); break;
-    case 2: return run_fwd<T, 2>(P, x, b, da, rot, h0, m2, m1, ws, st);
-    case 4: return run_fwd<T, 4>(P, x, b, da, rot, h0, m2, m1, ws, st);
-    case 8: return run_fwd<T, 8>(P, x, b, da, rot, h0, m2, m1, ws, st);
-  }
-  return MOMENTS_ENOTSUP;
-}
+template <int V> using IC = std::integral_constant<int, V>;
+template <typename T> struct TT { using type = T; };
 
-template <typename T>
-int bwd_nt(const Plan& P, const void* x, const void* b, const void* da, const void* rot,
-           const void* h0, const float* dm2, const float* dm1, void* dx, void* db, void* dda,
-           void* drot, void* dh0, unsigned char* ws, hipStream_t st) {
-  switch (P.NT) {
-    case 1: if constexpr (sizeof(T) == 4) return run_bwd<T, 1>(P, x, b, da, rot, h0, dm2, dm1, dx, db, dda, drot, dh0, ws, st); break;
-    case 2: return run_bwd<T, 2>(P, x, b, da, rot, h0, dm2, dm1, dx, db, dda, drot, dh0, ws, st);
-    case 4: return run_bwd<T, 4>(P, x, b, da, rot, h0, dm2, dm1, dx, db, dda, drot, dh0, ws, st);
-    case 8: return run_bwd<T, 8>(P, x, b, da, rot, h0, dm2, dm1, dx, db, dda, drot, dh0, ws, st);
+// Calls f(TT<T>, IC<NT>, IC<ROT>, IC<CK>) for the compiled variant matching the plan.
+template <class F>
+int with_variant(const Plan& P, F&& f) {
+  auto by_ck = [&](auto tt, auto nt, auto rot) -> int {
+    switch (P.CK) {
+      case 1: return f(tt, nt, rot, IC<1>{});
+      case 2: return f(tt, nt, rot, IC<2>{});
+      case 4: return f(tt, nt, rot, IC<4>{});
+    }
+    return MOMENTS_ENOTSUP;
+  };
+  auto by_rot = [&](auto tt, auto nt) -> int {
+    switch (P.g.rot_kind) {
+      case MOMENTS_ROT_NONE: return by_ck(tt, nt, IC<0>{});
+      case MOMENTS_ROT_COMPLEX_PAIRWISE:
+      case MOMENTS_ROT_COMPLEX_HALF: return by_ck(tt, nt, IC<1>{});
+      case MOMENTS_ROT_QUATERNION: return by_ck(tt, nt, IC<3>{});
+    }
+    return MOMENTS_EINVAL;
+  };
+  if (P.bf) {
+    if (P.NT == 4) return by_rot(TT<bf16>{}, IC<4>{});
+    if (P.NT == 8) return by_rot(TT<bf16>{}, IC<8>{});
+  } else {
+    if (P.NT == 4) return by_rot(TT<float>{}, IC<4>{});
   }
   return MOMENTS_ENOTSUP;
 }
@@ -338,8 +348,11 @@ int moments_fwd(const moments_desc* desc, const void* xhat, const void* bhat, co
   if (workspace_bytes < P.ws_fwd || (P.ws_fwd > 0 && workspace == nullptr)) return MOMENTS_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
-  if (P.bf) return fwd_nt<bf16>(P, xhat, bhat, da, rot, h0, m2, m1, ws, st);
-  return fwd_nt<float>(P, xhat, bhat, da, rot, h0, m2, m1, ws, st);
+  return with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
+    using T = typename decltype(tt)::type;
+    return run_fwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
+        P, xhat, bhat, da, rot, h0, m2, m1, ws, st);
+  });
 }
 
 int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
@@ -357,9 +370,11 @@ int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, co
   if (workspace_bytes < P.ws_bwd || (P.ws_bwd > 0 && workspace == nullptr)) return MOMENTS_EWORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
-  if (P.bf)
-    return bwd_nt<bf16>(P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, st);
-  return bwd_nt<float>(P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, st);
+  return with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
+    using T = typename decltype(tt)::type;
+    return run_bwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
+        P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, st);
+  });
 }
 
 const char* moments_strerror(int code) {
