@@ -54,6 +54,19 @@ template <typename T> __device__ __forceinline__ T to_t(float x);
 template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return (bf16)x; }
 
+// Two floats -> one register of two bf16 (round to nearest even), as an opaque
+// instruction so the compiler keeps the packed value instead of re-deriving it
+// from the float sources at every use.
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
+  unsigned r;
+  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
+  return r;
+}
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ bf8 as_bf8(u4 v) { return __builtin_bit_cast(bf8, v); }
+
 // Load one operand fragment (E consecutive elements, 4 or 16 bytes aligned).
 __device__ __forceinline__ float ld_frag(const float* p) { return *p; }
 __device__ __forceinline__ bf8 ld_frag(const bf16* p) { return *reinterpret_cast<const bf8*>(p); }

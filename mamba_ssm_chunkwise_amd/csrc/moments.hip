@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "kernels_bwd.h"
+#include "kernels_bwdt.h"
 
 using namespace mom;
 
@@ -20,9 +21,9 @@ std::atomic<int> g_last_hip{0};
 constexpr size_t kLdsLimit = 160 * 1024;
 
 // ---- optional per-kernel event timing (moments_profile_*) -------------------
-enum KernelId { KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_N };
+enum KernelId { KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_PREP, KID_N };
 const char* const kKernelNames[KID_N] = {"k_carry", "k_scan", "k_fwd", "k_reduce",
-                                         "k_bwd", "k_dscan", "k_fix", "k_zero_tail"};
+                                         "k_bwd", "k_dscan", "k_fix", "k_zero_tail", "k_prep_dm1"};
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -74,7 +75,8 @@ struct Plan {
   int CK;       // channel slots of the folded write axis (c padded to 1, 2 or 4)
   int NT, R;    // state columns padded to R = 16*NT
   int PK;       // state rows padded for MFMA K over rows
-  size_t carry, dec, m2p, m1p, db;  // workspace offsets
+  bool bwdt;    // backward main kernel in the transposed layout (bf16, c <= 2)
+  size_t carry, dec, m2p, m1p, db, dm1i;  // workspace offsets
   size_t ws_fwd, ws_bwd;
 };
 
@@ -157,7 +159,11 @@ int make_plan(const moments_desc* d, Plan* P) {
   P->m1p = o; o = align256(o + chains * (size_t)g.NGR * g.p * P->R * 4);
   P->ws_fwd = o;
   P->db = base;
-  P->ws_bwd = align256(base + chains * (size_t)g.NK * pr * 4);
+  o = align256(base + chains * (size_t)g.NK * pr * 4);
+  P->bwdt = bf && P->CK <= 2 && lds_bwdt(g, P->NT, P->CK).total <= kLdsLimit;
+  P->dm1i = o;
+  if (P->bwdt) o = align256(o + chains * (size_t)g.p * P->R * 4);
+  P->ws_bwd = o;
   return MOMENTS_OK;
 }
 
@@ -254,7 +260,27 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   float* dec = (float*)(ws + P.dec);
   float* Db = (float*)(ws + P.db);
   const int chains = g.b * g.h;
-  if (g.NK >= 1) {
+  bool done = false;
+  if constexpr (std::is_same<T, bf16>::value && CK <= 2) {
+    if (P.bwdt && g.NK >= 1) {
+      float* dm1i = (float*)(ws + P.dm1i);
+      {
+        const size_t total = (size_t)chains * g.p * P.R;
+        ProfScope ps(KID_PREP, st);
+        hipLaunchKernelGGL(k_prep_dm1, dim3((unsigned)((total + NTH - 1) / NTH)), dim3(NTH), 0, st, g, P.R, dm1,
+                           dm1i);
+        MOM_TRY(check_launch());
+      }
+      const size_t lds = lds_bwdt(g, NT, CK).total;
+      MOM_TRY(set_lds(k_bwdt<NT, ROT, CK>, lds));
+      ProfScope ps(KID_BWD, st);
+      hipLaunchKernelGGL((k_bwdt<NT, ROT, CK>), dim3(chains * g.NGR), dim3(NTT), lds, st, g, X, B, D, Rt,
+                         (const float*)carry, dm2, (const float*)dm1i, Db, (T*)dx, (T*)db, (T*)dda, (T*)drot);
+      MOM_TRY(check_launch());
+      done = true;
+    }
+  }
+  if (!done && g.NK >= 1) {
     const size_t lds = lds_bwd(g, P.R, sizeof(T), P.NT).total;
     MOM_TRY(set_lds(k_bwd<T, NT, ROT, CK>, lds));
     ProfScope ps(KID_BWD, st);
