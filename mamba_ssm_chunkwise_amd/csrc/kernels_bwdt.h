@@ -31,7 +31,7 @@ constexpr int NWT = 4;          // waves of k_bwdt
 constexpr int NTT = 64 * NWT;   // threads of k_bwdt
 constexpr int GSP = 40;         // G transpose: bf16 per state column (32 tokens + pad)
 constexpr int LTP = 36;         // row pitch of LT[j][t] (floats)
-constexpr int XPB = 64;         // state rows per staged xhat block
+constexpr int XPB = 32;         // state rows per staged xhat block
 
 // Column-contracting fragments built from accumulator registers: K-slot
 // 32ks + 8q + e holds state column 32ks + 16(e/4) + 4q + e%4, i.e. register
@@ -45,53 +45,55 @@ __host__ __device__ __forceinline__ int slot_of_col(int c) {
   return 32 * ks + 8 * q + 4 * h + e;
 }
 
-// Rotation tables of k_bwdt, padded with the identity so whole column tiles
-// can be rotated: complex -> [t][AP][cos, sin] with AP = A rounded up to 8;
-// quaternion -> [t][JP][4] with JP = J rounded up to 4.
-__host__ __device__ __forceinline__ int rot_ap(const Geo& g) { return (g.A + 7) & ~7; }
-__host__ __device__ __forceinline__ int rot_jp(const Geo& g) { return (g.J + 3) & ~3; }
-__host__ __device__ __forceinline__ size_t rott_bytes(const Geo& g) {
-  if (g.rot_kind == 1 || g.rot_kind == 2) return al16((size_t)ELL * rot_ap(g) * 2 * 4);
-  if (g.rot_kind == 3) return al16((size_t)ELL * rot_jp(g) * 4 * 4);
-  return 16;
+// Column tiles of 16 internal state columns that carry a rotation, rounded up
+// to a power of two (0: no rotation). Complex pairs 8 per tile, quaternion
+// blocks 4 per tile. The rotation tables of k_bwdt hold RT tiles per token,
+// padded with the identity: complex [t][8RT][cos, sin], quaternion [t][4RT][4],
+// each token row padded by 4 floats so consecutive tokens start in different
+// banks.
+__host__ __device__ __forceinline__ int rot_tiles(const Geo& g) {
+  const int need = (g.rot_kind == 1 || g.rot_kind == 2) ? (g.A + 7) / 8 : g.rot_kind == 3 ? (g.J + 3) / 4 : 0;
+  if (need == 0) return 0;
+  int rt = 1;
+  while (rt < need) rt *= 2;
+  return rt;
 }
 
-struct LdsT {
-  size_t Ss, bsT, bsY, xs, LT, a, d, rot, Gs, dXs, red, lw, total;
-};
-
-// Per-lane chunk constants kept in LDS as float4 rows interleaved by lane
-// ([entry][lane] of 16 bytes, conflict-free): 4 entries of W factors, 2*NKT
-// of d_xhat factors.
+// LDS plan: every region at a compile-time offset (so LDS addresses fold into
+// instruction offsets); the rotation table, sized at run time, comes last.
+// Per-lane chunk constants are float4 rows interleaved by lane ([entry][lane]
+// of 16 bytes, conflict-free): LWE entries of W factors, 2*NKT of d_xhat
+// factors.
 constexpr int LWE = 4;
-
-__host__ __device__ __forceinline__ LdsT lds_bwdt(const Geo& g, int NT, int CK) {
-  const int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8;
-  LdsT l{};
-  size_t o = 0;
-  l.Ss = o; o += al16((size_t)R * SP * 2);     // S rows, K-slot order
-  l.bsT = o; o += al16((size_t)R * KP * 2);    // bhat^T [col][(j,c)]
-  l.bsY = o; o += al16((size_t)K * SP * 2);    // bhat [(j,c)][col slot]
-  l.xs = o; o += al16((size_t)XPB * KP * 2);   // xhat block [p][(j,c)]
-  l.LT = o; o += al16((size_t)ELL * LTP * 4);  // L^T [j][t]
-  l.a = o; o += al16(ELL * 4);
-  l.d = o; o += al16(ELL * 4);
-  l.rot = o; o += rott_bytes(g);
+template <int NT, int CK>
+struct LdsT {
+  static constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8;
+  static constexpr size_t Ss = 0;                                     // S rows, K-slot order
+  static constexpr size_t bsT = Ss + (size_t)R * SP * 2;              // bhat^T [col][(j,c)]
+  static constexpr size_t bsY = bsT + (size_t)R * KP * 2;             // bhat [(j,c)][col slot]
+  static constexpr size_t xs = bsY + (size_t)K * SP * 2;              // xhat block [p][(j,c)]
+  static constexpr size_t dXs = xs + (size_t)XPB * KP * 2;            // d_xhat block [p][(j,c)]
+  static constexpr size_t LT = dXs + (size_t)XPB * KP * 2;            // L^T [j][t]
+  static constexpr size_t a = LT + (size_t)ELL * LTP * 4;
+  static constexpr size_t d = a + ELL * 4;
+  static constexpr size_t lw = d + ELL * 4;
+  static constexpr size_t cst = lw + (size_t)(LWE + 2 * (K / 16)) * 64 * 16;  // carry, d_m1 rows [2][4][R]
+  static constexpr size_t red = cst + (size_t)2 * 4 * R * 4;
   // G transposes of the round's rows; at chunk end the d_bhat tile and the
   // rotation-gradient reduction reuse the space
-  size_t gs = (size_t)NWT * R * GSP * 2;
-  const size_t dbt = (size_t)K * SP * 2;
-  const size_t rw = g.rot_kind == 3 ? (size_t)4 * rot_jp(g) : (size_t)rot_ap(g);
-  const size_t rb = (size_t)NWT * ELL * rw * 4;
-  if (gs < dbt) gs = dbt;
-  if (gs < rb) gs = rb;
-  l.Gs = o; o += al16(gs);
-  l.dXs = o; o += al16((size_t)XPB * KP * 2);  // d_xhat block [p][(j,c)]
-  l.red = o; o += al16((size_t)(NWT * 4 * ELL + NWT * K + ELL) * 4);
-  l.lw = o; o += (size_t)(LWE + 2 * (K / 16)) * 64 * 16;
-  l.total = o;
-  return l;
-}
+  static constexpr size_t gsb = (size_t)NWT * R * GSP * 2 > (size_t)K * SP * 2 ? (size_t)NWT * R * GSP * 2
+                                                                                : (size_t)K * SP * 2;
+  static constexpr size_t Gs = red + (size_t)(NWT * 4 * ELL + NWT * K + ELL) * 4;
+  static constexpr size_t rot = Gs + gsb;
+  static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0, "aligned regions");
+  // rotation table (RT rotated tiles): 16*RT + 4 floats per token
+  __host__ __device__ static size_t total(int RT) { return rot + (size_t)ELL * (16 * RT + 4) * 4; }
+  // the rotation-gradient reduction [wave][t][8RT or 16RT] must fit the G space
+  __host__ __device__ static bool fits(int rot_kind, int RT) {
+    const size_t rw = rot_kind == 3 ? (size_t)16 * RT : (size_t)8 * RT;
+    return (size_t)NWT * ELL * rw * 4 <= gsb;
+  }
+};
 
 // d_m1 in the internal column order, rows padded to R: dm1i[bh][p][R].
 __global__ __launch_bounds__(NTH) void k_prep_dm1(Geo g, int R, const float* __restrict__ dm1, float* dm1i) {
@@ -115,7 +117,9 @@ __device__ __forceinline__ f4 load_cols4(const float* row, int r, int col) {
   return v;
 }
 
-template <int NT, int ROT, int CK>
+// RT: column tiles carrying a rotation (compile time; the tables are padded
+// with the identity up to 8*RT complex pairs or 4*RT quaternion blocks).
+template <int NT, int ROT, int CK, int RT>
 __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     Geo g, const bf16* __restrict__ xhat, const bf16* __restrict__ bhat, const bf16* __restrict__ da,
     const bf16* __restrict__ rot, const float* __restrict__ carry, const float* __restrict__ dm2,
@@ -125,28 +129,31 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   constexpr int KSR = NT / 2;     // K-steps over state columns
   constexpr int KH = NKT / 2;     // d_bhat (j,c) tiles per wave
   constexpr int CH = NT / 2;      // d_bhat column tiles per wave
-  constexpr int NRC = ROT == 3 ? 4 : (ROT == 1 ? 2 : 1);  // rotation-gradient values per (t, tile)
+  constexpr int NRC = ROT == 3 ? 4 : 2;  // rotation-gradient values per (t, rotated tile)
+  constexpr int RTA = RT > 0 ? RT : 1;
+  static_assert((ROT == 0) == (RT == 0) && RT <= NT, "rotated tiles");
   extern __shared__ __align__(16) unsigned char smem[];
-  const LdsT L = lds_bwdt(g, NT, CK);
-  bf16* Ss = (bf16*)(smem + L.Ss);
-  bf16* bsT = (bf16*)(smem + L.bsT);
-  bf16* bsY = (bf16*)(smem + L.bsY);
-  bf16* xs = (bf16*)(smem + L.xs);
-  float* LT = (float*)(smem + L.LT);
-  float* s_a = (float*)(smem + L.a);
-  float* s_d = (float*)(smem + L.d);
-  float* rt = (float*)(smem + L.rot);
-  bf16* Gs = (bf16*)(smem + L.Gs);
-  bf16* dXs = (bf16*)(smem + L.dXs);
-  float* red = (float*)(smem + L.red);
-  f4* LWt = (f4*)(smem + L.lw);           // [LWE][64]
+  using L = LdsT<NT, CK>;
+  bf16* Ss = (bf16*)(smem + L::Ss);
+  bf16* bsT = (bf16*)(smem + L::bsT);
+  bf16* bsY = (bf16*)(smem + L::bsY);
+  bf16* xs = (bf16*)(smem + L::xs);
+  float* LT = (float*)(smem + L::LT);
+  float* s_a = (float*)(smem + L::a);
+  float* s_d = (float*)(smem + L::d);
+  float* rt = (float*)(smem + L::rot);
+  bf16* Gs = (bf16*)(smem + L::Gs);
+  bf16* dXs = (bf16*)(smem + L::dXs);
+  float* red = (float*)(smem + L::red);
+  f4* LWt = (f4*)(smem + L::lw);           // [LWE][64]
   f4* LYt = LWt + LWE * 64;               // [2*NKT][64]
+  float* cst = (float*)(smem + L::cst);   // [carry | d_m1][row of the round][R]
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
-  const int AP = rot_ap(g), JP = rot_jp(g);
+  constexpr int RTP = 16 * RT + 4;  // rotation table floats per token (padded)
   const int kh = w >> 1, ch = w & 1;  // this wave's d_bhat tiles: (j,c) half kh, column half ch
 
   // S = d_m2 + d_m2^T: rows internal columns, K-slots in col_of_slot order.
@@ -187,6 +194,27 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
   };
 
+  // The carry rows h_-(n)[p][:] and the d_m1 rows of a round (4 state rows)
+  // travel through LDS: every thread fetches one float4 of them a round ahead
+  // and stores it after the round's d_bhat work, off the rows' critical path.
+  constexpr int CQ = 2 * 4 * R / 4;  // float4 pieces per round
+  auto fetch_round = [&](int nc, int pr0) -> f4 {
+    f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (tid < CQ) {
+      const int arr = tid / (4 * R / 4), rest = tid % (4 * R / 4);
+      const int rr = rest / (R / 4), col = 4 * (rest % (R / 4));
+      const int pp = pr0 + rr;
+      if (pp < g.p) {
+        if (arr == 0) v = load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col);
+        else v = *reinterpret_cast<const f4*>(dm1i + ((size_t)bh * g.p + pp) * R + col);
+      }
+    }
+    return v;
+  };
+  auto store_round = [&](f4 v) {
+    if (tid < CQ) reinterpret_cast<f4*>(cst)[tid] = v;
+  };
+
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
   const int nrounds = (g.p + 3) / 4;
@@ -219,26 +247,27 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       bsY[k * SP + slot_of_col(col)] = v;
     }
     if constexpr (ROT == 1) {
-      for (int idx = tid; idx < ELL * AP; idx += NTT) {
-        const int t = idx / AP, a = idx % AP;
+      for (int idx = tid; idx < ELL * 8 * RT; idx += NTT) {
+        const int t = idx / (8 * RT), a = idx % (8 * RT);
         const int pos = nc * ELL + t;
         float th = 0.0f;
         if (a < g.A && pos < g.V) th = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + a];
         float sv, cv;
         sincosf(th, &sv, &cv);
-        rt[(t * AP + a) * 2] = cv;
-        rt[(t * AP + a) * 2 + 1] = sv;
+        rt[t * RTP + 2 * a] = cv;
+        rt[t * RTP + 2 * a + 1] = sv;
       }
     } else if constexpr (ROT == 3) {
-      for (int idx = tid; idx < ELL * JP * 4; idx += NTT) {
-        const int t = idx / (JP * 4), e = idx % (JP * 4);
+      for (int idx = tid; idx < ELL * 16 * RT; idx += NTT) {
+        const int t = idx / (16 * RT), e = idx % (16 * RT);
         const int pos = nc * ELL + t;
         float v = (e & 3) == 0 ? 1.0f : 0.0f;
         if ((e >> 2) < g.J && pos < g.V) v = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e];
-        rt[t * JP * 4 + e] = v;
+        rt[t * RTP + e] = v;
       }
     }
     stage_x(nc, 0);
+    store_round(fetch_round(nc, 0));
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, t = idx % ELL;
@@ -274,11 +303,11 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     for (int a = 0; a < KH; a++)
 #pragma unroll
       for (int b = 0; b < CH; b++) dbacc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    float racc[2][NT][NRC];
+    float racc[2][RTA][NRC];
 #pragma unroll
     for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-      for (int ct = 0; ct < NT; ct++)
+      for (int ct = 0; ct < RTA; ct++)
 #pragma unroll
         for (int u = 0; u < NRC; u++) racc[tt][ct][u] = 0.0f;
     float gacc[2] = {0.0f, 0.0f};
@@ -296,28 +325,30 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         __syncthreads();
       }
       const int p = pr0 + w;
-      if (p < g.p) {
+      const f4 pf = fetch_round(nc, pr0 + 4);  // next round's rows, stored after the d_bhat work
+      // One state row, all columns and tokens; MASK zeroes d_c at tokens >= tv
+      // (only the chunk holding valid_len needs it).
+      auto row = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int pl = p - pblk;
-        // ---- W fragments and the carry row -----------------------------------
-        float xv[CK][8];
+        // carry row h_-[p][16ct+4q..] for the lane's columns, fetched first
+        const float* hrow = cst + w * R;
+        f4 hv[NT];
 #pragma unroll
-        for (int ks = 0; ks < CK; ks++) {
-          const bf8 x8 = ld_frag(xs + pl * KP + 32 * ks + 8 * q);
-#pragma unroll
-          for (int e = 0; e < 8; e++) xv[ks][e] = (float)x8[e];
-        }
-        const float* hrow = carry + (((size_t)bh * g.NK + nc) * g.p + p) * g.r;
-        f4 hT[NT][2];
-#pragma unroll
-        for (int ct = 0; ct < NT; ct++) {
-          const f4 hv = load_cols4(hrow, g.r, 16 * ct + 4 * q);
-#pragma unroll
-          for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) hT[ct][tt][i] = s_d[16 * tt + n] * hv[i];
-        }
+        for (int ct = 0; ct < NT; ct++) hv[ct] = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
+        // ---- W fragments: W[t][(j,c)] = L[t,j] xhat[(j,c)][p], t = 16tt+n ----
         u4 Wf[2][CK];
         {
+          float xv[CK][8];
+#pragma unroll
+          for (int ks = 0; ks < CK; ks++) {
+            const u4 x8 = *reinterpret_cast<const u4*>(xs + pl * KP + 32 * ks + 8 * q);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              xv[ks][2 * e] = bf16_lo(x8[e]);
+              xv[ks][2 * e + 1] = bf16_hi(x8[e]);
+            }
+          }
           float lw[16];
 #pragma unroll
           for (int e4 = 0; e4 < 4; e4++) {
@@ -331,11 +362,16 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             for (int ks = 0; ks < CK; ks++)
 #pragma unroll
               for (int e = 0; e < 8; e += 2) {
-                const int b = (tt * CK + ks) * (8 / CK);
-                Wf[tt][ks][e / 2] = pk_bf16(lw[b + e / CK] * xv[ks][e], lw[b + (e + 1) / CK] * xv[ks][e + 1]);
+                const int b0 = (tt * CK + ks) * (8 / CK);
+                Wf[tt][ks][e / 2] = pk_bf16(lw[b0 + e / CK] * xv[ks][e], lw[b0 + (e + 1) / CK] * xv[ks][e + 1]);
               }
         }
-        // ---- states, transposed: h~^T[col][t] ------------------------------
+        // ---- states, transposed: h~^T[col][t] (carry added on read-out) ----
+        f4 hT[NT][2];
+#pragma unroll
+        for (int ct = 0; ct < NT; ct++)
+#pragma unroll
+          for (int tt = 0; tt < 2; tt++) hT[ct][tt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < CK; ks++)
 #pragma unroll
@@ -347,43 +383,43 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
               hT[ct][tt] = MM<bf16>::mma(a, as_bf8(Wf[tt][ks]), hT[ct][tt]);
             }
           }
-        // ---- de-rotation in the lane; c^T packed as K-slot fragments --------
+        // ---- carry, de-rotation in the lane; c^T (and h~^T) packed ---------
         u4 cP[KSR][2];
-        u4 hP[ROT == 3 ? KSR : 1][2];  // quaternion: h~ packed the same way
+        u4 hP[ROT == 3 ? KSR : 1][2];
+        const float dt[2] = {s_d[n], s_d[16 + n]};
 #pragma unroll
         for (int ct = 0; ct < NT; ct++)
 #pragma unroll
           for (int tt = 0; tt < 2; tt++) {
-            f4 c = hT[ct][tt];
+            f4 h;
+#pragma unroll
+            for (int i = 0; i < 4; i++) h[i] = hT[ct][tt][i] + dt[tt] * hv[ct][i];
+            f4 c = h;
             const int t = 16 * tt + n;
             if constexpr (ROT == 1) {
-              if (8 * ct < g.A) {
-                const f4 r4 = *reinterpret_cast<const f4*>(rt + (t * AP + 8 * ct + 2 * q) * 2);
-                const f4 h = c;
+              if (ct < RT) {
+                const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
                 c[0] = r4[0] * h[0] + r4[1] * h[1];
                 c[1] = r4[0] * h[1] - r4[1] * h[0];
                 c[2] = r4[2] * h[2] + r4[3] * h[3];
                 c[3] = r4[2] * h[3] - r4[3] * h[2];
               }
             } else if constexpr (ROT == 3) {
-              if (4 * ct < g.J) {
-                const f4 Q = *reinterpret_cast<const f4*>(rt + (t * JP + 4 * ct + q) * 4);
-                const f4 h = c;
+              if (ct < RT) {
+                const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
                 c[0] = Q[0] * h[0] - Q[1] * h[1] - Q[2] * h[2] - Q[3] * h[3];
                 c[1] = Q[0] * h[1] + Q[1] * h[0] + Q[2] * h[3] - Q[3] * h[2];
                 c[2] = Q[0] * h[2] - Q[1] * h[3] + Q[2] * h[0] + Q[3] * h[1];
                 c[3] = Q[0] * h[3] + Q[1] * h[2] - Q[2] * h[1] + Q[3] * h[0];
               }
+              hP[ROT == 3 ? ct >> 1 : 0][tt][2 * (ct & 1)] = pk_bf16(h[0], h[1]);
+              hP[ROT == 3 ? ct >> 1 : 0][tt][2 * (ct & 1) + 1] = pk_bf16(h[2], h[3]);
             }
             cP[ct >> 1][tt][2 * (ct & 1)] = pk_bf16(c[0], c[1]);
             cP[ct >> 1][tt][2 * (ct & 1) + 1] = pk_bf16(c[2], c[3]);
-            if constexpr (ROT == 3) {
-              hP[ct >> 1][tt][2 * (ct & 1)] = pk_bf16(hT[ct][tt][0], hT[ct][tt][1]);
-              hP[ct >> 1][tt][2 * (ct & 1) + 1] = pk_bf16(hT[ct][tt][2], hT[ct][tt][3]);
-            }
           }
         // ---- d_c^T = S c^T + d_m1, rotation VJP, G, Y = G bhat^T ------------
-        const float* dmrow = dm1i + ((size_t)bh * g.p + p) * R;
+        const float* dmrow = cst + (4 + w) * R;
         f4 Y[NKT][2];
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++)
@@ -407,7 +443,10 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
             for (int tt = 0; tt < 2; tt++) {
               const int t = 16 * tt + n;
-              f4 d = t < tv ? dc[tt] : f4{0.0f, 0.0f, 0.0f, 0.0f};
+              f4 d = dc[tt];
+              if constexpr (MASK) {
+                if (t >= tv) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
+              }
               f4 hc;  // c (complex, none) or h~ (quaternion), from the packed fragments
               {
                 const unsigned w0 = ROT == 3 ? hP[ROT == 3 ? ky : 0][tt][2 * h2] : cP[ky][tt][2 * h2];
@@ -419,25 +458,25 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
               }
               f4 G = d;
               if constexpr (ROT == 3) {
-                if (4 * ct < g.J) {
-                  const f4 Q = *reinterpret_cast<const f4*>(rt + (t * JP + 4 * ct + q) * 4);
+                if (ct < RT) {
+                  const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
                   G[0] = Q[0] * d[0] + Q[1] * d[1] + Q[2] * d[2] + Q[3] * d[3];
                   G[1] = Q[0] * d[1] - Q[1] * d[0] - Q[2] * d[3] + Q[3] * d[2];
                   G[2] = Q[0] * d[2] + Q[1] * d[3] - Q[2] * d[0] - Q[3] * d[1];
                   G[3] = Q[0] * d[3] - Q[1] * d[2] + Q[2] * d[1] - Q[3] * d[0];
-                  racc[tt][ct][0] += d[0] * hc[0] + d[1] * hc[1] + d[2] * hc[2] + d[3] * hc[3];
-                  racc[tt][ct][1] += -d[0] * hc[1] + d[1] * hc[0] - d[2] * hc[3] + d[3] * hc[2];
-                  racc[tt][ct][2] += -d[0] * hc[2] + d[1] * hc[3] + d[2] * hc[0] - d[3] * hc[1];
-                  racc[tt][ct][3] += -d[0] * hc[3] - d[1] * hc[2] + d[2] * hc[1] + d[3] * hc[0];
+                  racc[tt][ct < RT ? ct : 0][0] += d[0] * hc[0] + d[1] * hc[1] + d[2] * hc[2] + d[3] * hc[3];
+                  racc[tt][ct < RT ? ct : 0][1] += -d[0] * hc[1] + d[1] * hc[0] - d[2] * hc[3] + d[3] * hc[2];
+                  racc[tt][ct < RT ? ct : 0][2] += -d[0] * hc[2] + d[1] * hc[3] + d[2] * hc[0] - d[3] * hc[1];
+                  racc[tt][ct < RT ? ct : 0][3] += -d[0] * hc[3] - d[1] * hc[2] + d[2] * hc[1] + d[3] * hc[0];
                 }
                 gacc[tt] += G[0] * hc[0] + G[1] * hc[1] + G[2] * hc[2] + G[3] * hc[3];
               } else {
                 gacc[tt] += d[0] * hc[0] + d[1] * hc[1] + d[2] * hc[2] + d[3] * hc[3];
                 if constexpr (ROT == 1) {
-                  if (8 * ct < g.A) {
-                    const f4 r4 = *reinterpret_cast<const f4*>(rt + (t * AP + 8 * ct + 2 * q) * 2);
-                    racc[tt][ct][0] += d[0] * hc[1] - d[1] * hc[0];
-                    racc[tt][ct][1] += d[2] * hc[3] - d[3] * hc[2];
+                  if (ct < RT) {
+                    const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+                    racc[tt][ct < RT ? ct : 0][0] += d[0] * hc[1] - d[1] * hc[0];
+                    racc[tt][ct < RT ? ct : 0][1] += d[2] * hc[3] - d[3] * hc[2];
                     G[0] = r4[0] * d[0] - r4[1] * d[1];
                     G[1] = r4[1] * d[0] + r4[0] * d[1];
                     G[2] = r4[2] * d[2] - r4[3] * d[3];
@@ -483,6 +522,10 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           if (q == 0) dXs[pl * KP + k] = (bf16)v;
           cc[kt] += v * (float)xs[pl * KP + k];
         }
+      };
+      if (p < g.p) {
+        if (tv >= ELL) row(std::false_type{});
+        else row(std::true_type{});
       }
       __syncthreads();  // the round's G transposes are complete
       float LB[KH][8];  // L[8q+e][j of (j,c) = 16(kh*KH+kt)+n]
@@ -521,14 +564,15 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           const bf8 gb = ld_frag(Gr + (16 * ct + n) * GSP + 8 * q);
 #pragma unroll
           for (int kt = 0; kt < KH; kt++) dbacc[kt][cb] = MM<bf16>::mma(as_bf8(Ab[kt]), gb, dbacc[kt][cb]);
-          if (kh == 0) {
+          if (kh == (rr & 1)) {
             const f4 lo = MM<bf16>::mma(dA, gb, f4{0.0f, 0.0f, 0.0f, 0.0f});
             const int col = 16 * ct + n;
             if (q == 0 && col < g.r) dbrow[col] = lo[0];
           }
         }
       }
-      __syncthreads();  // transposes consumed
+      store_round(pf);
+      __syncthreads();  // transposes consumed; next round's rows staged
     }
     flush_dx(nc, (nrounds - 1) * 4 - ((nrounds - 1) * 4) % XPB);
 
@@ -555,23 +599,19 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     // ---- rotation gradient: fixed-order sum over the waves ---------------------
     if constexpr (ROT != 0) {
       if (d_rot != nullptr) {
-        const int rw = ROT == 3 ? 4 * JP : AP;
+        constexpr int rw = ROT == 3 ? 16 * RTA : 8 * RTA;
         float* RB = (float*)Gs;  // [w][t][rw]
 #pragma unroll
         for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-          for (int ct = 0; ct < NT; ct++) {
+          for (int ct = 0; ct < RTA; ct++) {
             const int t = 16 * tt + n;
             if constexpr (ROT == 1) {
-              if (8 * ct < AP) {
-                RB[(w * ELL + t) * rw + 8 * ct + 2 * q] = racc[tt][ct][0];
-                RB[(w * ELL + t) * rw + 8 * ct + 2 * q + 1] = racc[tt][ct][1];
-              }
+              RB[(w * ELL + t) * rw + 8 * ct + 2 * q] = racc[tt][ct][0];
+              RB[(w * ELL + t) * rw + 8 * ct + 2 * q + 1] = racc[tt][ct][1];
             } else {
-              if (4 * ct < JP) {
 #pragma unroll
-                for (int u = 0; u < 4; u++) RB[(w * ELL + t) * rw + 4 * (4 * ct + q) + u] = racc[tt][ct][u];
-              }
+              for (int u = 0; u < 4; u++) RB[(w * ELL + t) * rw + 4 * (4 * ct + q) + u] = racc[tt][ct][u];
             }
           }
         __syncthreads();

@@ -69,6 +69,9 @@ struct ProfScope {
   }
 };
 
+template <int V> using IC = std::integral_constant<int, V>;
+template <typename T> struct TT { using type = T; };
+
 struct Plan {
   Geo g;
   bool bf;      // bf16 inputs
@@ -85,6 +88,20 @@ int round_nt(int r, bool /*bf*/) {
   if (nt <= 4) nt = 4;
   else nt = 8;
   return nt;
+}
+
+// LDS bytes of k_bwdt for (NT, CK), or 0 when that kernel does not cover the shape.
+size_t bwdt_lds(const Geo& g, int NT, int CK) {
+  const int RT = rot_tiles(g);
+  auto one = [&](auto lt) -> size_t {
+    using LT = typename decltype(lt)::type;
+    return LT::fits(g.rot_kind, RT) ? LT::total(RT) : 0;
+  };
+  if (NT == 4 && CK == 1) return one(TT<LdsT<4, 1>>{});
+  if (NT == 4 && CK == 2) return one(TT<LdsT<4, 2>>{});
+  if (NT == 8 && CK == 1) return one(TT<LdsT<8, 1>>{});
+  if (NT == 8 && CK == 2) return one(TT<LdsT<8, 2>>{});
+  return 0;
 }
 
 int make_plan(const moments_desc* d, Plan* P) {
@@ -160,7 +177,12 @@ int make_plan(const moments_desc* d, Plan* P) {
   P->ws_fwd = o;
   P->db = base;
   o = align256(base + chains * (size_t)g.NK * pr * 4);
-  P->bwdt = bf && P->CK <= 2 && lds_bwdt(g, P->NT, P->CK).total <= kLdsLimit;
+  if (bf && P->CK <= 2) {
+    const size_t lb = bwdt_lds(g, P->NT, P->CK);
+    P->bwdt = lb > 0 && lb <= kLdsLimit;
+  } else {
+    P->bwdt = false;
+  }
   P->dm1i = o;
   if (P->bwdt) o = align256(o + chains * (size_t)g.p * P->R * 4);
   P->ws_bwd = o;
@@ -271,12 +293,29 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
                            dm1i);
         MOM_TRY(check_launch());
       }
-      const size_t lds = lds_bwdt(g, NT, CK).total;
-      MOM_TRY(set_lds(k_bwdt<NT, ROT, CK>, lds));
-      ProfScope ps(KID_BWD, st);
-      hipLaunchKernelGGL((k_bwdt<NT, ROT, CK>), dim3(chains * g.NGR), dim3(NTT), lds, st, g, X, B, D, Rt,
-                         (const float*)carry, dm2, (const float*)dm1i, Db, (T*)dx, (T*)db, (T*)dda, (T*)drot);
-      MOM_TRY(check_launch());
+      const int RT = rot_tiles(g);
+      auto launch = [&](auto rot_c, auto rt_c) -> int {
+        constexpr int RO = decltype(rot_c)::value, RTc = decltype(rt_c)::value;
+        const size_t lds = LdsT<NT, CK>::total(RTc);
+        MOM_TRY(set_lds(k_bwdt<NT, RO, CK, RTc>, lds));
+        ProfScope ps(KID_BWD, st);
+        hipLaunchKernelGGL((k_bwdt<NT, RO, CK, RTc>), dim3(chains * g.NGR), dim3(NTT), lds, st, g, X, B, D, Rt,
+                           (const float*)carry, dm2, (const float*)dm1i, Db, (T*)dx, (T*)db, (T*)dda, (T*)drot);
+        return check_launch();
+      };
+      int rc = MOMENTS_ENOTSUP;
+      if constexpr (ROT == 0) {
+        rc = launch(IC<0>{}, IC<0>{});
+      } else {
+        if (RT == 0) rc = launch(IC<0>{}, IC<0>{});
+        else if (RT == 1) rc = launch(IC<ROT>{}, IC<1>{});
+        else if (RT == 2) rc = launch(IC<ROT>{}, IC<2>{});
+        else if (RT == 4) rc = launch(IC<ROT>{}, IC<4>{});
+        else if (RT == 8) {
+          if constexpr (NT >= 8) rc = launch(IC<ROT>{}, IC<8>{});
+        }
+      }
+      MOM_TRY(rc);
       done = true;
     }
   }
@@ -312,9 +351,6 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   }
   return 0;
 }
-
-template <int V> using IC = std::integral_constant<int, V>;
-template <typename T> struct TT { using type = T; };
 
 // Calls f(TT<T>, IC<NT>, IC<ROT>, IC<CK>) for the compiled variant matching the plan.
 template <class F>
