@@ -54,14 +54,14 @@ template <typename T> __device__ __forceinline__ T to_t(float x);
 template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return (bf16)x; }
 
-// Two floats -> one register of two bf16 (round to nearest even), as an opaque
-// instruction so the compiler keeps the packed value instead of re-deriving it
-// from the float sources at every use.
+// Two floats -> one register of two bf16 (round to nearest even), kept as a
+// 32-bit word so packed fragments are built once and reused.
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float fl2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
-  unsigned r;
-  asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(lo), "v"(hi));
-  return r;
+  const fl2 v = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf2));
 }
 __device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }

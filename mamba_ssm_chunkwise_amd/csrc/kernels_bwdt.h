@@ -7,8 +7,7 @@
 // terms, d_rot complete, and local(n)[p][col] = sum_t d_t G[t][p][col] for the
 // carry-cotangent recurrence.
 //
-// Layout. One wave owns whole state rows p (all columns, all 32 tokens of the
-// chunk). The states are computed transposed, h~^T[col][t] = bhat^T W^T with
+// Layout. The states are computed transposed, h~^T[col][t] = bhat^T W^T with
 // W[t][(j,c)] = L[t,j] xhat[j,c,p], so an accumulator lane holds one token and
 // four consecutive state columns: complex pairs and quaternion 4-blocks sit in
 // one lane's registers and the rotation, its transpose and its gradient need
@@ -18,16 +17,19 @@
 // tokens in registers (d_bhat over (t,p), local over t) read G through a small
 // per-row LDS transpose.
 //
-// Per round, wave w handles row 4*round + w; after a barrier the four waves
-// accumulate d_bhat for the round's rows, each owning a quarter of the
-// (j,c) x column tiles.
+// Work split. Eight waves, two per SIMD. Each round covers four state rows;
+// wave w handles row 4*round + (w % 4) for the tokens of half w / 4 (0..15 or
+// 16..31): nothing in the row computation couples the two halves except the
+// token sum of d_xhat, whose two partials meet in LDS. After a barrier the
+// eight waves accumulate d_bhat for the round's rows, each owning a block of
+// the (j,c) x column tiles.
 #pragma once
 
 #include "kernels.h"
 
 namespace mom {
 
-constexpr int NWT = 4;          // waves of k_bwdt
+constexpr int NWT = 8;          // waves of k_bwdt
 constexpr int NTT = 64 * NWT;   // threads of k_bwdt
 constexpr int GSP = 40;         // G transpose: bf16 per state column (32 tokens + pad)
 constexpr int LTP = 36;         // row pitch of LT[j][t] (floats)
@@ -60,7 +62,7 @@ __host__ __device__ __forceinline__ int rot_tiles(const Geo& g) {
 }
 
 // LDS plan: every region at a compile-time offset (so LDS addresses fold into
-// instruction offsets); the rotation table, sized at run time, comes last.
+// instruction offsets); the rotation table, sized by RT, comes last.
 // Per-lane chunk constants are float4 rows interleaved by lane ([entry][lane]
 // of 16 bytes, conflict-free): LWE entries of W factors, 2*NKT of d_xhat
 // factors.
@@ -78,20 +80,22 @@ struct LdsT {
   static constexpr size_t d = a + ELL * 4;
   static constexpr size_t lw = d + ELL * 4;
   static constexpr size_t cst = lw + (size_t)(LWE + 2 * (K / 16)) * 64 * 16;  // carry, d_m1 rows [2][4][R]
-  static constexpr size_t red = cst + (size_t)2 * 4 * R * 4;
+  static constexpr size_t dxp = cst + (size_t)2 * 4 * R * 4;                   // d_xhat partials [2][4][K]
+  static constexpr size_t red = dxp + (size_t)2 * 4 * K * 4;
+  static constexpr size_t nred = (size_t)NWT * 4 * 16 + 4 * K + ELL;          // floats of red
   // G transposes of the round's rows; at chunk end the d_bhat tile and the
   // rotation-gradient reduction reuse the space
-  static constexpr size_t gsb = (size_t)NWT * R * GSP * 2 > (size_t)K * SP * 2 ? (size_t)NWT * R * GSP * 2
-                                                                                : (size_t)K * SP * 2;
-  static constexpr size_t Gs = red + (size_t)(NWT * 4 * ELL + NWT * K + ELL) * 4;
+  static constexpr size_t gsb = (size_t)4 * R * GSP * 2 > (size_t)K * SP * 2 ? (size_t)4 * R * GSP * 2
+                                                                             : (size_t)K * SP * 2;
+  static constexpr size_t Gs = red + nred * 4;
   static constexpr size_t rot = Gs + gsb;
-  static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0, "aligned regions");
+  static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
   // rotation table (RT rotated tiles): 16*RT + 4 floats per token
   __host__ __device__ static size_t total(int RT) { return rot + (size_t)ELL * (16 * RT + 4) * 4; }
-  // the rotation-gradient reduction [wave][t][8RT or 16RT] must fit the G space
+  // the rotation-gradient reduction [wave][16 tokens][8RT or 16RT] must fit the G space
   __host__ __device__ static bool fits(int rot_kind, int RT) {
     const size_t rw = rot_kind == 3 ? (size_t)16 * RT : (size_t)8 * RT;
-    return (size_t)NWT * ELL * rw * 4 <= gsb;
+    return (size_t)NWT * 16 * rw * 4 <= gsb;
   }
 };
 
@@ -125,15 +129,18 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     const bf16* __restrict__ rot, const float* __restrict__ carry, const float* __restrict__ dm2,
     const float* __restrict__ dm1i, float* Db, bf16* d_xhat, bf16* d_bhat, bf16* d_da, bf16* d_rot) {
   constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8;
-  constexpr int NKT = K / 16;     // (j,c) tiles
-  constexpr int KSR = NT / 2;     // K-steps over state columns
-  constexpr int KH = NKT / 2;     // d_bhat (j,c) tiles per wave
-  constexpr int CH = NT / 2;      // d_bhat column tiles per wave
+  constexpr int NKT = K / 16;      // (j,c) tiles
+  constexpr int KSR = NT / 2;      // K-steps over state columns
+  constexpr int KW = NKT < 4 ? NKT : 4;  // d_bhat: waves along (j,c) tiles
+  constexpr int CW = NWT / KW;     // d_bhat: waves along column tiles
+  constexpr int KH = NKT / KW;     // d_bhat (j,c) tiles per wave
+  constexpr int CH = NT / CW;      // d_bhat column tiles per wave
   constexpr int NRC = ROT == 3 ? 4 : 2;  // rotation-gradient values per (t, rotated tile)
   constexpr int RTA = RT > 0 ? RT : 1;
-  static_assert((ROT == 0) == (RT == 0) && RT <= NT, "rotated tiles");
-  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int RTP = 16 * RT + 4;  // rotation table floats per token (padded)
+  static_assert((ROT == 0) == (RT == 0) && RT <= NT && CH >= 1 && KH >= 1, "tiling");
   using L = LdsT<NT, CK>;
+  extern __shared__ __align__(16) unsigned char smem[];
   bf16* Ss = (bf16*)(smem + L::Ss);
   bf16* bsT = (bf16*)(smem + L::bsT);
   bf16* bsY = (bf16*)(smem + L::bsY);
@@ -145,16 +152,18 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   bf16* Gs = (bf16*)(smem + L::Gs);
   bf16* dXs = (bf16*)(smem + L::dXs);
   float* red = (float*)(smem + L::red);
-  f4* LWt = (f4*)(smem + L::lw);           // [LWE][64]
+  f4* LWt = (f4*)(smem + L::lw);          // [LWE][64]
   f4* LYt = LWt + LWE * 64;               // [2*NKT][64]
   float* cst = (float*)(smem + L::cst);   // [carry | d_m1][row of the round][R]
+  float* dxp = (float*)(smem + L::dxp);   // [token half][row of the round][K]
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
-  constexpr int RTP = 16 * RT + 4;  // rotation table floats per token (padded)
-  const int kh = w >> 1, ch = w & 1;  // this wave's d_bhat tiles: (j,c) half kh, column half ch
+  const int u = w & 3, tt = w >> 2;       // row slot of the round, token half
+  const int t = 16 * tt + n;              // this lane's token in the transposed tiles
+  const int kq = w / CW, cq = w % CW;     // d_bhat block of this wave
 
   // S = d_m2 + d_m2^T: rows internal columns, K-slots in col_of_slot order.
   {
@@ -193,11 +202,11 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         d_xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + pl] = dXs[pl * KP + k];
     }
   };
-
   // The carry rows h_-(n)[p][:] and the d_m1 rows of a round (4 state rows)
   // travel through LDS: every thread fetches one float4 of them a round ahead
   // and stores it after the round's d_bhat work, off the rows' critical path.
   constexpr int CQ = 2 * 4 * R / 4;  // float4 pieces per round
+  static_assert(CQ <= NTT, "one piece per thread");
   auto fetch_round = [&](int nc, int pr0) -> f4 {
     f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
     if (tid < CQ) {
@@ -222,18 +231,18 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     __syncthreads();
     // ---- chunk staging --------------------------------------------------
     if (tid < 64) {
-      const int t = tid & 31;
-      const int pos = nc * ELL + t;
+      const int tk = tid & 31;
+      const int pos = nc * ELL + tk;
       float v = 0.0f;
       if (tid < 32 && pos < g.V) v = (float)da[((size_t)bi * g.s + pos) * g.h + hi];
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) {
-        const float u = __shfl_up(v, off, 32);
-        if (t >= off) v += u;
+        const float up = __shfl_up(v, off, 32);
+        if (tk >= off) v += up;
       }
       if (tid < 32) {
-        s_a[t] = v;
-        s_d[t] = expf(v);
+        s_a[tk] = v;
+        s_d[tk] = expf(v);
       }
     }
     for (int idx = tid; idx < K * R; idx += NTT) {
@@ -248,52 +257,52 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
     if constexpr (ROT == 1) {
       for (int idx = tid; idx < ELL * 8 * RT; idx += NTT) {
-        const int t = idx / (8 * RT), a = idx % (8 * RT);
-        const int pos = nc * ELL + t;
+        const int tk = idx / (8 * RT), a = idx % (8 * RT);
+        const int pos = nc * ELL + tk;
         float th = 0.0f;
         if (a < g.A && pos < g.V) th = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + a];
         float sv, cv;
         sincosf(th, &sv, &cv);
-        rt[t * RTP + 2 * a] = cv;
-        rt[t * RTP + 2 * a + 1] = sv;
+        rt[tk * RTP + 2 * a] = cv;
+        rt[tk * RTP + 2 * a + 1] = sv;
       }
     } else if constexpr (ROT == 3) {
       for (int idx = tid; idx < ELL * 16 * RT; idx += NTT) {
-        const int t = idx / (16 * RT), e = idx % (16 * RT);
-        const int pos = nc * ELL + t;
+        const int tk = idx / (16 * RT), e = idx % (16 * RT);
+        const int pos = nc * ELL + tk;
         float v = (e & 3) == 0 ? 1.0f : 0.0f;
         if ((e >> 2) < g.J && pos < g.V) v = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e];
-        rt[t * RTP + e] = v;
+        rt[tk * RTP + e] = v;
       }
     }
     stage_x(nc, 0);
     store_round(fetch_round(nc, 0));
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
-      const int j = idx / ELL, t = idx % ELL;
-      LT[j * LTP + t] = (j <= t) ? expf(s_a[t] - s_a[j]) : 0.0f;
+      const int j = idx / ELL, tk = idx % ELL;
+      LT[j * LTP + tk] = (j <= tk) ? expf(s_a[tk] - s_a[j]) : 0.0f;
     }
     __syncthreads();
 
-    // ---- per-lane chunk constants (LDS tables, this wave's lanes) ----------
+    // ---- per-lane chunk constants (LDS tables, filled by wave 0's lanes) ----
     const int tv = g.V - nc * ELL;  // valid tokens of this chunk (>= 1)
     if (w == 0) {
-      // W factors: L[16tt+n][j of the slots 32ks+8q..], flattened (tt*CK+ks)*(8/CK)+u
+      // W factors: L[16h+n][j of the slots 32ks+8q..], flattened (h*CK+ks)*(8/CK)+v
 #pragma unroll
       for (int f = 0; f < 16; f++) {
-        const int tt = f / 8, rest = f % 8, ks = rest / (8 / CK), u = rest % (8 / CK);
+        const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), v = rest % (8 / CK);
         reinterpret_cast<float*>(LWt + (f >> 2) * 64 + lane)[f & 3] =
-            LT[((32 * ks + 8 * q) / CK + u) * LTP + 16 * tt + n];
+            LT[((32 * ks + 8 * q) / CK + v) * LTP + 16 * hh + n];
       }
-      // d_xhat factors: L[16tt+4q+i][j of (j,c) = 16kt+n], entry tt*NKT+kt
+      // d_xhat factors: L[16h+4q+i][j of (j,c) = 16kt+n], entry h*NKT+kt
 #pragma unroll
-      for (int tt = 0; tt < 2; tt++)
+      for (int hh = 0; hh < 2; hh++)
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) {
           f4 v;
 #pragma unroll
-          for (int i = 0; i < 4; i++) v[i] = LT[((16 * kt + n) / CK) * LTP + 16 * tt + 4 * q + i];
-          LYt[(tt * NKT + kt) * 64 + lane] = v;
+          for (int i = 0; i < 4; i++) v[i] = LT[((16 * kt + n) / CK) * LTP + 16 * hh + 4 * q + i];
+          LYt[(hh * NKT + kt) * 64 + lane] = v;
         }
     }
     __syncthreads();
@@ -303,17 +312,14 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     for (int a = 0; a < KH; a++)
 #pragma unroll
       for (int b = 0; b < CH; b++) dbacc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    float racc[2][RTA][NRC];
+    float racc[RTA][NRC];
 #pragma unroll
-    for (int tt = 0; tt < 2; tt++)
+    for (int ct = 0; ct < RTA; ct++)
 #pragma unroll
-      for (int ct = 0; ct < RTA; ct++)
-#pragma unroll
-        for (int u = 0; u < NRC; u++) racc[tt][ct][u] = 0.0f;
-    float gacc[2] = {0.0f, 0.0f};
-    float cc[NKT];
-#pragma unroll
-    for (int kt = 0; kt < NKT; kt++) cc[kt] = 0.0f;
+      for (int v = 0; v < NRC; v++) racc[ct][v] = 0.0f;
+    float gacc = 0.0f;  // sum over this wave's rows and columns of <d_c, c> at token t
+    float cct = 0.0f;   // thread (rr, k) < 4K: sum over rows rr of the rounds of xhat * d_xhat
+    const float dtl = s_d[t];
 
     for (int round = 0; round < nrounds; round++) {
       const int pr0 = 4 * round;
@@ -324,20 +330,15 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         stage_x(nc, pblk);
         __syncthreads();
       }
-      const int p = pr0 + w;
+      const int p = pr0 + u;
       const f4 pf = fetch_round(nc, pr0 + 4);  // next round's rows, stored after the d_bhat work
-      // One state row, all columns and tokens; MASK zeroes d_c at tokens >= tv
-      // (only the chunk holding valid_len needs it).
+      // One state row, all columns, this wave's 16 tokens; MASK zeroes d_c at
+      // tokens >= tv (only the chunk holding valid_len needs it).
       auto row = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int pl = p - pblk;
-        // carry row h_-[p][16ct+4q..] for the lane's columns, fetched first
-        const float* hrow = cst + w * R;
-        f4 hv[NT];
-#pragma unroll
-        for (int ct = 0; ct < NT; ct++) hv[ct] = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
-        // ---- W fragments: W[t][(j,c)] = L[t,j] xhat[(j,c)][p], t = 16tt+n ----
-        u4 Wf[2][CK];
+        // ---- W fragment: W[t][(j,c)] = L[t,j] xhat[(j,c)][p] ----------------
+        u4 Wf[CK];
         {
           float xv[CK][8];
 #pragma unroll
@@ -349,201 +350,190 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
               xv[ks][2 * e + 1] = bf16_hi(x8[e]);
             }
           }
-          float lw[16];
+          float lw[8];
 #pragma unroll
-          for (int e4 = 0; e4 < 4; e4++) {
-            const f4 v = LWt[e4 * 64 + lane];
+          for (int e4 = 0; e4 < 2; e4++) {
+            const f4 v = LWt[(2 * tt + e4) * 64 + lane];
 #pragma unroll
             for (int i = 0; i < 4; i++) lw[4 * e4 + i] = v[i];
           }
 #pragma unroll
-          for (int tt = 0; tt < 2; tt++)
+          for (int ks = 0; ks < CK; ks++)
 #pragma unroll
-            for (int ks = 0; ks < CK; ks++)
-#pragma unroll
-              for (int e = 0; e < 8; e += 2) {
-                const int b0 = (tt * CK + ks) * (8 / CK);
-                Wf[tt][ks][e / 2] = pk_bf16(lw[b0 + e / CK] * xv[ks][e], lw[b0 + (e + 1) / CK] * xv[ks][e + 1]);
-              }
+            for (int e = 0; e < 8; e += 2) {
+              const int b0 = ks * (8 / CK);
+              Wf[ks][e / 2] = pk_bf16(lw[b0 + e / CK] * xv[ks][e], lw[b0 + (e + 1) / CK] * xv[ks][e + 1]);
+            }
         }
         // ---- states, transposed: h~^T[col][t] (carry added on read-out) ----
-        f4 hT[NT][2];
+        f4 hT[NT];
 #pragma unroll
-        for (int ct = 0; ct < NT; ct++)
+        for (int ct = 0; ct < NT; ct++) hT[ct] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        // tokens 0..15 see j <= 15 only: their last K-steps are all zero
+        const int nks = tt == 0 ? (CK + 1) / 2 : CK;
 #pragma unroll
-          for (int tt = 0; tt < 2; tt++) hT[ct][tt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ks = 0; ks < CK; ks++) {
+          if (ks < nks) {
 #pragma unroll
-        for (int ks = 0; ks < CK; ks++)
-#pragma unroll
-          for (int ct = 0; ct < NT; ct++) {
-            const bf8 a = ld_frag(bsT + (16 * ct + n) * KP + 32 * ks + 8 * q);
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++) {
-              if (tt == 0 && 2 * ks >= CK) continue;  // tokens 0..15 see j <= 15 only
-              hT[ct][tt] = MM<bf16>::mma(a, as_bf8(Wf[tt][ks]), hT[ct][tt]);
+            for (int ct = 0; ct < NT; ct++) {
+              const bf8 a = ld_frag(bsT + (16 * ct + n) * KP + 32 * ks + 8 * q);
+              hT[ct] = MM<bf16>::mma(a, as_bf8(Wf[ks]), hT[ct]);
             }
           }
+        }
         // ---- carry, de-rotation in the lane; c^T (and h~^T) packed ---------
-        u4 cP[KSR][2];
-        u4 hP[ROT == 3 ? KSR : 1][2];
-        const float dt[2] = {s_d[n], s_d[16 + n]};
+        u4 cP[KSR];
+        u4 hP[ROT == 3 ? KSR : 1];
+        const float* hrow = cst + u * R;
 #pragma unroll
-        for (int ct = 0; ct < NT; ct++)
+        for (int ct = 0; ct < NT; ct++) {
+          const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
+          f4 h;
 #pragma unroll
-          for (int tt = 0; tt < 2; tt++) {
-            f4 h;
-#pragma unroll
-            for (int i = 0; i < 4; i++) h[i] = hT[ct][tt][i] + dt[tt] * hv[ct][i];
-            f4 c = h;
-            const int t = 16 * tt + n;
-            if constexpr (ROT == 1) {
-              if (ct < RT) {
-                const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
-                c[0] = r4[0] * h[0] + r4[1] * h[1];
-                c[1] = r4[0] * h[1] - r4[1] * h[0];
-                c[2] = r4[2] * h[2] + r4[3] * h[3];
-                c[3] = r4[2] * h[3] - r4[3] * h[2];
-              }
-            } else if constexpr (ROT == 3) {
-              if (ct < RT) {
-                const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
-                c[0] = Q[0] * h[0] - Q[1] * h[1] - Q[2] * h[2] - Q[3] * h[3];
-                c[1] = Q[0] * h[1] + Q[1] * h[0] + Q[2] * h[3] - Q[3] * h[2];
-                c[2] = Q[0] * h[2] - Q[1] * h[3] + Q[2] * h[0] + Q[3] * h[1];
-                c[3] = Q[0] * h[3] + Q[1] * h[2] - Q[2] * h[1] + Q[3] * h[0];
-              }
-              hP[ROT == 3 ? ct >> 1 : 0][tt][2 * (ct & 1)] = pk_bf16(h[0], h[1]);
-              hP[ROT == 3 ? ct >> 1 : 0][tt][2 * (ct & 1) + 1] = pk_bf16(h[2], h[3]);
+          for (int i = 0; i < 4; i++) h[i] = hT[ct][i] + dtl * hv[i];
+          f4 c = h;
+          if constexpr (ROT == 1) {
+            if (ct < RT) {
+              const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+              c[0] = r4[0] * h[0] + r4[1] * h[1];
+              c[1] = r4[0] * h[1] - r4[1] * h[0];
+              c[2] = r4[2] * h[2] + r4[3] * h[3];
+              c[3] = r4[2] * h[3] - r4[3] * h[2];
             }
-            cP[ct >> 1][tt][2 * (ct & 1)] = pk_bf16(c[0], c[1]);
-            cP[ct >> 1][tt][2 * (ct & 1) + 1] = pk_bf16(c[2], c[3]);
+          } else if constexpr (ROT == 3) {
+            if (ct < RT) {
+              const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+              c[0] = Q[0] * h[0] - Q[1] * h[1] - Q[2] * h[2] - Q[3] * h[3];
+              c[1] = Q[0] * h[1] + Q[1] * h[0] + Q[2] * h[3] - Q[3] * h[2];
+              c[2] = Q[0] * h[2] - Q[1] * h[3] + Q[2] * h[0] + Q[3] * h[1];
+              c[3] = Q[0] * h[3] + Q[1] * h[2] - Q[2] * h[1] + Q[3] * h[0];
+            }
+            hP[ROT == 3 ? ct >> 1 : 0][2 * (ct & 1)] = pk_bf16(h[0], h[1]);
+            hP[ROT == 3 ? ct >> 1 : 0][2 * (ct & 1) + 1] = pk_bf16(h[2], h[3]);
           }
+          cP[ct >> 1][2 * (ct & 1)] = pk_bf16(c[0], c[1]);
+          cP[ct >> 1][2 * (ct & 1) + 1] = pk_bf16(c[2], c[3]);
+        }
         // ---- d_c^T = S c^T + d_m1, rotation VJP, G, Y = G bhat^T ------------
-        const float* dmrow = cst + (4 + w) * R;
-        f4 Y[NKT][2];
+        const float* dmrow = cst + (4 + u) * R;
+        f4 Y[NKT];
 #pragma unroll
-        for (int kt = 0; kt < NKT; kt++)
-#pragma unroll
-          for (int tt = 0; tt < 2; tt++) Y[kt][tt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        bf16* Gw = Gs + (size_t)w * R * GSP;
+        for (int kt = 0; kt < NKT; kt++) Y[kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        unsigned short* Gw = reinterpret_cast<unsigned short*>(Gs) + (size_t)u * R * GSP + t;
 #pragma unroll
         for (int ky = 0; ky < KSR; ky++) {
-          u4 GP[2];
+          u4 GP;
 #pragma unroll
           for (int h2 = 0; h2 < 2; h2++) {
             const int ct = 2 * ky + h2;
-            const f4 dmv = *reinterpret_cast<const f4*>(dmrow + 16 * ct + 4 * q);
-            f4 dc[2] = {dmv, dmv};
+            f4 d = *reinterpret_cast<const f4*>(dmrow + 16 * ct + 4 * q);
 #pragma unroll
             for (int ks = 0; ks < KSR; ks++) {
               const bf8 a = ld_frag(Ss + (16 * ct + n) * SP + 32 * ks + 8 * q);
-#pragma unroll
-              for (int tt = 0; tt < 2; tt++) dc[tt] = MM<bf16>::mma(a, as_bf8(cP[ks][tt]), dc[tt]);
+              d = MM<bf16>::mma(a, as_bf8(cP[ks]), d);
             }
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++) {
-              const int t = 16 * tt + n;
-              f4 d = dc[tt];
-              if constexpr (MASK) {
-                if (t >= tv) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (MASK) {
+              if (t >= tv) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            f4 hc;  // c (complex, none) or h~ (quaternion), from the packed fragments
+            {
+              const unsigned w0 = ROT == 3 ? hP[ROT == 3 ? ky : 0][2 * h2] : cP[ky][2 * h2];
+              const unsigned w1 = ROT == 3 ? hP[ROT == 3 ? ky : 0][2 * h2 + 1] : cP[ky][2 * h2 + 1];
+              hc[0] = bf16_lo(w0);
+              hc[1] = bf16_hi(w0);
+              hc[2] = bf16_lo(w1);
+              hc[3] = bf16_hi(w1);
+            }
+            f4 G = d;
+            if constexpr (ROT == 3) {
+              if (ct < RT) {
+                const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+                G[0] = Q[0] * d[0] + Q[1] * d[1] + Q[2] * d[2] + Q[3] * d[3];
+                G[1] = Q[0] * d[1] - Q[1] * d[0] - Q[2] * d[3] + Q[3] * d[2];
+                G[2] = Q[0] * d[2] + Q[1] * d[3] - Q[2] * d[0] - Q[3] * d[1];
+                G[3] = Q[0] * d[3] - Q[1] * d[2] + Q[2] * d[1] - Q[3] * d[0];
+                float* ra = racc[ct < RT ? ct : 0];
+                ra[0] += d[0] * hc[0] + d[1] * hc[1] + d[2] * hc[2] + d[3] * hc[3];
+                ra[1] += -d[0] * hc[1] + d[1] * hc[0] - d[2] * hc[3] + d[3] * hc[2];
+                ra[2] += -d[0] * hc[2] + d[1] * hc[3] + d[2] * hc[0] - d[3] * hc[1];
+                ra[3] += -d[0] * hc[3] - d[1] * hc[2] + d[2] * hc[1] + d[3] * hc[0];
               }
-              f4 hc;  // c (complex, none) or h~ (quaternion), from the packed fragments
-              {
-                const unsigned w0 = ROT == 3 ? hP[ROT == 3 ? ky : 0][tt][2 * h2] : cP[ky][tt][2 * h2];
-                const unsigned w1 = ROT == 3 ? hP[ROT == 3 ? ky : 0][tt][2 * h2 + 1] : cP[ky][tt][2 * h2 + 1];
-                hc[0] = bf16_lo(w0);
-                hc[1] = bf16_hi(w0);
-                hc[2] = bf16_lo(w1);
-                hc[3] = bf16_hi(w1);
-              }
-              f4 G = d;
-              if constexpr (ROT == 3) {
+              gacc += G[0] * hc[0] + G[1] * hc[1] + G[2] * hc[2] + G[3] * hc[3];
+            } else {
+              gacc += d[0] * hc[0] + d[1] * hc[1] + d[2] * hc[2] + d[3] * hc[3];
+              if constexpr (ROT == 1) {
                 if (ct < RT) {
-                  const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
-                  G[0] = Q[0] * d[0] + Q[1] * d[1] + Q[2] * d[2] + Q[3] * d[3];
-                  G[1] = Q[0] * d[1] - Q[1] * d[0] - Q[2] * d[3] + Q[3] * d[2];
-                  G[2] = Q[0] * d[2] + Q[1] * d[3] - Q[2] * d[0] - Q[3] * d[1];
-                  G[3] = Q[0] * d[3] - Q[1] * d[2] + Q[2] * d[1] - Q[3] * d[0];
-                  racc[tt][ct < RT ? ct : 0][0] += d[0] * hc[0] + d[1] * hc[1] + d[2] * hc[2] + d[3] * hc[3];
-                  racc[tt][ct < RT ? ct : 0][1] += -d[0] * hc[1] + d[1] * hc[0] - d[2] * hc[3] + d[3] * hc[2];
-                  racc[tt][ct < RT ? ct : 0][2] += -d[0] * hc[2] + d[1] * hc[3] + d[2] * hc[0] - d[3] * hc[1];
-                  racc[tt][ct < RT ? ct : 0][3] += -d[0] * hc[3] - d[1] * hc[2] + d[2] * hc[1] + d[3] * hc[0];
-                }
-                gacc[tt] += G[0] * hc[0] + G[1] * hc[1] + G[2] * hc[2] + G[3] * hc[3];
-              } else {
-                gacc[tt] += d[0] * hc[0] + d[1] * hc[1] + d[2] * hc[2] + d[3] * hc[3];
-                if constexpr (ROT == 1) {
-                  if (ct < RT) {
-                    const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
-                    racc[tt][ct < RT ? ct : 0][0] += d[0] * hc[1] - d[1] * hc[0];
-                    racc[tt][ct < RT ? ct : 0][1] += d[2] * hc[3] - d[3] * hc[2];
-                    G[0] = r4[0] * d[0] - r4[1] * d[1];
-                    G[1] = r4[1] * d[0] + r4[0] * d[1];
-                    G[2] = r4[2] * d[2] - r4[3] * d[3];
-                    G[3] = r4[3] * d[2] + r4[2] * d[3];
-                  }
+                  const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+                  float* ra = racc[ct < RT ? ct : 0];
+                  ra[0] += d[0] * hc[1] - d[1] * hc[0];
+                  ra[1] += d[2] * hc[3] - d[3] * hc[2];
+                  G[0] = r4[0] * d[0] - r4[1] * d[1];
+                  G[1] = r4[1] * d[0] + r4[0] * d[1];
+                  G[2] = r4[2] * d[2] - r4[3] * d[3];
+                  G[3] = r4[3] * d[2] + r4[2] * d[3];
                 }
               }
-              GP[tt][2 * h2] = pk_bf16(G[0], G[1]);
-              GP[tt][2 * h2 + 1] = pk_bf16(G[2], G[3]);
             }
+            GP[2 * h2] = pk_bf16(G[0], G[1]);
+            GP[2 * h2 + 1] = pk_bf16(G[2], G[3]);
           }
           // Y[t][(j,c)] += sum over this K-step's columns of G[t][col] bhat[(j,c)][col]
 #pragma unroll
           for (int kt = 0; kt < NKT; kt++) {
             const bf8 b = ld_frag(bsY + (16 * kt + n) * SP + 32 * ky + 8 * q);
-#pragma unroll
-            for (int tt = 0; tt < 2; tt++) Y[kt][tt] = MM<bf16>::mma(as_bf8(GP[tt]), b, Y[kt][tt]);
+            Y[kt] = MM<bf16>::mma(as_bf8(GP), b, Y[kt]);
           }
           // G^T into the row's transpose buffer, [col][t]
 #pragma unroll
-          for (int tt = 0; tt < 2; tt++)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const int col = 32 * ky + 16 * (e >> 2) + 4 * q + (e & 3);
-              unsigned short* gw = reinterpret_cast<unsigned short*>(Gw) + col * GSP + 16 * tt + n;
-              const unsigned word = GP[tt][e / 2];
-              gw[0] = (unsigned short)(word & 0xffffu);
-              gw[GSP] = (unsigned short)(word >> 16);
-            }
+          for (int e = 0; e < 8; e += 2) {
+            const int col = 32 * ky + 16 * (e >> 2) + 4 * q + (e & 3);
+            const unsigned word = GP[e / 2];
+            Gw[col * GSP] = (unsigned short)(word & 0xffffu);
+            Gw[(col + 1) * GSP] = (unsigned short)(word >> 16);
+          }
         }
-        // ---- d_xhat[(j,c)][p] = sum_t L[t,j] Y[t][(j,c)] ----------------------
+        // ---- this half's share of d_xhat[(j,c)][p] = sum_t L[t,j] Y[t][(j,c)] ----
+        float* part = dxp + (tt * 4 + u) * K;
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) {
-          float v = 0.0f;
-#pragma unroll
-          for (int tt = 0; tt < 2; tt++) {
-            const f4 ly = LYt[(tt * NKT + kt) * 64 + lane];
-#pragma unroll
-            for (int i = 0; i < 4; i++) v += ly[i] * Y[kt][tt][i];
-          }
+          const f4 ly = LYt[(tt * NKT + kt) * 64 + lane];
+          float v = ly[0] * Y[kt][0] + ly[1] * Y[kt][1] + ly[2] * Y[kt][2] + ly[3] * Y[kt][3];
           v = col4_sum(v);
-          const int k = 16 * kt + n;
-          if (q == 0) dXs[pl * KP + k] = (bf16)v;
-          cc[kt] += v * (float)xs[pl * KP + k];
+          if (q == 0) part[16 * kt + n] = v;
         }
       };
       if (p < g.p) {
         if (tv >= ELL) row(std::false_type{});
         else row(std::true_type{});
       }
-      __syncthreads();  // the round's G transposes are complete
-      float LB[KH][8];  // L[8q+e][j of (j,c) = 16(kh*KH+kt)+n]
+      __syncthreads();  // the round's G transposes and d_xhat partials are complete
+      // ---- d_xhat of the round's rows: the two token halves added ---------------
+      if (tid < 4 * K) {
+        const int rr = tid / K, k = tid % K;
+        const int pp = pr0 + rr;
+        if (pp < g.p) {
+          const float v = dxp[rr * K + k] + dxp[(4 + rr) * K + k];
+          const int pl = pp - pblk;
+          dXs[pl * KP + k] = (bf16)v;
+          cct += v * (float)xs[pl * KP + k];
+        }
+      }
+      // ---- d_bhat[(j,c)][col] += sum_t L[t,j] xhat[(j,c)][p] G[t][col]; local ----
+      float LB[KH][8];  // L[8q+e][j of (j,c) = 16(kq*KH+kb)+n]
 #pragma unroll
-      for (int kt = 0; kt < KH; kt++) {
-        const float* src = LT + ((16 * (kh * KH + kt) + n) / CK) * LTP + 8 * q;
+      for (int kb = 0; kb < KH; kb++) {
+        const float* src = LT + ((16 * (kq * KH + kb) + n) / CK) * LTP + 8 * q;
         const f4 l0 = *reinterpret_cast<const f4*>(src);
         const f4 l1 = *reinterpret_cast<const f4*>(src + 4);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-          LB[kt][e] = l0[e];
-          LB[kt][e + 4] = l1[e];
+          LB[kb][e] = l0[e];
+          LB[kb][e + 4] = l1[e];
         }
       }
       bf8 dA;  // A operand of local: row 0 = d_t over the K-slots t = 8q+e
 #pragma unroll
       for (int e = 0; e < 8; e++) dA[e] = (bf16)(n == 0 ? s_d[8 * q + e] : 0.0f);
-      // ---- d_bhat[(j,c)][col] += sum_t L[t,j] xhat[(j,c)][p] G[t][col]; local ----
 #pragma unroll 1
       for (int rr = 0; rr < 4; rr++) {
         const int pp = pr0 + rr;
@@ -551,20 +541,21 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         const int pl = pp - pblk;
         u4 Ab[KH];
 #pragma unroll
-        for (int kt = 0; kt < KH; kt++) {
-          const float xk = (float)xs[pl * KP + 16 * (kh * KH + kt) + n];
+        for (int kb = 0; kb < KH; kb++) {
+          const float xk = (float)xs[pl * KP + 16 * (kq * KH + kb) + n];
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) Ab[kt][e / 2] = pk_bf16(LB[kt][e] * xk, LB[kt][e + 1] * xk);
+          for (int e = 0; e < 8; e += 2) Ab[kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
         }
         const bf16* Gr = Gs + (size_t)rr * R * GSP;
         float* dbrow = Db + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r;
+        const bool do_local = kq == (rr % KW);  // each (row, column tile) once
 #pragma unroll
         for (int cb = 0; cb < CH; cb++) {
-          const int ct = ch * CH + cb;
+          const int ct = cq * CH + cb;
           const bf8 gb = ld_frag(Gr + (16 * ct + n) * GSP + 8 * q);
 #pragma unroll
-          for (int kt = 0; kt < KH; kt++) dbacc[kt][cb] = MM<bf16>::mma(as_bf8(Ab[kt]), gb, dbacc[kt][cb]);
-          if (kh == (rr & 1)) {
+          for (int kb = 0; kb < KH; kb++) dbacc[kb][cb] = MM<bf16>::mma(as_bf8(Ab[kb]), gb, dbacc[kb][cb]);
+          if (do_local) {
             const f4 lo = MM<bf16>::mma(dA, gb, f4{0.0f, 0.0f, 0.0f, 0.0f});
             const int col = 16 * ct + n;
             if (q == 0 && col < g.r) dbrow[col] = lo[0];
@@ -580,12 +571,12 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     if (d_bhat != nullptr) {
       bf16* DBs = Gs;  // [K][SP]
 #pragma unroll
-      for (int kt = 0; kt < KH; kt++)
+      for (int kb = 0; kb < KH; kb++)
 #pragma unroll
         for (int cb = 0; cb < CH; cb++)
 #pragma unroll
           for (int i = 0; i < 4; i++)
-            DBs[(16 * (kh * KH + kt) + 4 * q + i) * SP + 16 * (ch * CH + cb) + n] = (bf16)dbacc[kt][cb][i];
+            DBs[(16 * (kq * KH + kb) + 4 * q + i) * SP + 16 * (cq * CH + cb) + n] = (bf16)dbacc[kb][cb][i];
       __syncthreads();
       for (int idx = tid; idx < K * g.r; idx += NTT) {
         const int k = idx / g.r, ra = idx - k * g.r;
@@ -596,55 +587,52 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       }
       __syncthreads();
     }
-    // ---- rotation gradient: fixed-order sum over the waves ---------------------
+    // ---- rotation gradient: fixed-order sum over the waves of a token half -----
     if constexpr (ROT != 0) {
       if (d_rot != nullptr) {
         constexpr int rw = ROT == 3 ? 16 * RTA : 8 * RTA;
-        float* RB = (float*)Gs;  // [w][t][rw]
+        float* RB = (float*)Gs;  // [w][16 tokens][rw]
 #pragma unroll
-        for (int tt = 0; tt < 2; tt++)
+        for (int ct = 0; ct < RTA; ct++) {
+          float* dst = RB + (w * 16 + n) * rw;
+          if constexpr (ROT == 1) {
+            dst[8 * ct + 2 * q] = racc[ct][0];
+            dst[8 * ct + 2 * q + 1] = racc[ct][1];
+          } else {
 #pragma unroll
-          for (int ct = 0; ct < RTA; ct++) {
-            const int t = 16 * tt + n;
-            if constexpr (ROT == 1) {
-              RB[(w * ELL + t) * rw + 8 * ct + 2 * q] = racc[tt][ct][0];
-              RB[(w * ELL + t) * rw + 8 * ct + 2 * q + 1] = racc[tt][ct][1];
-            } else {
-#pragma unroll
-              for (int u = 0; u < 4; u++) RB[(w * ELL + t) * rw + 4 * (4 * ct + q) + u] = racc[tt][ct][u];
-            }
+            for (int v = 0; v < 4; v++) dst[4 * (4 * ct + q) + v] = racc[ct][v];
           }
+        }
         __syncthreads();
         for (int idx = tid; idx < ELL * g.RW; idx += NTT) {
-          const int t = idx / g.RW, e = idx % g.RW;
+          const int tk = idx / g.RW, e = idx % g.RW;
+          const int half = tk >> 4;
           float s = 0.0f;
 #pragma unroll
-          for (int ww = 0; ww < NWT; ww++) s += RB[(ww * ELL + t) * rw + e];
-          const int pos = nc * ELL + t;
+          for (int uu = 0; uu < 4; uu++) s += RB[((4 * half + uu) * 16 + (tk & 15)) * rw + e];
+          const int pos = nc * ELL + tk;
           if (pos < g.s) d_rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e] = (bf16)s;
         }
       }
     }
     // ---- d_da without the carry-cotangent terms --------------------------------
-    float* rsum = red;                    // [w][q][t]
-    float* csum = red + NWT * 4 * ELL;    // [w][(j,c)]
-    float* ddv = csum + NWT * K;          // [t]
-#pragma unroll
-    for (int tt = 0; tt < 2; tt++) rsum[(w * 4 + q) * ELL + 16 * tt + n] = gacc[tt];
-    if (q == 0) {
-#pragma unroll
-      for (int kt = 0; kt < NKT; kt++) csum[w * K + 16 * kt + n] = cc[kt];
-    }
+    float* rsum = red;                    // [w][q][16]
+    float* csum = red + NWT * 4 * 16;     // [rr][(j,c)]
+    float* ddv = csum + 4 * K;            // [t]
+    rsum[(w * 4 + q) * 16 + n] = gacc;
+    if (tid < 4 * K) csum[tid] = cct;
     __syncthreads();
     if (tid == 0) {
       float acc = 0.0f;
-      for (int t = ELL - 1; t >= 0; t--) {
+      for (int tk = ELL - 1; tk >= 0; tk--) {
+        const int half = tk >> 4;
         float rtm = 0.0f, ctm = 0.0f;
-        for (int e = 0; e < NWT * 4; e++) rtm += rsum[e * ELL + t];
-        for (int ww = 0; ww < NWT; ww++)
-          for (int ci = 0; ci < g.c; ci++) ctm += csum[ww * K + t * CK + ci];
+        for (int uu = 0; uu < 4; uu++)
+          for (int qq = 0; qq < 4; qq++) rtm += rsum[((4 * half + uu) * 4 + qq) * 16 + (tk & 15)];
+        for (int rr = 0; rr < 4; rr++)
+          for (int ci = 0; ci < g.c; ci++) ctm += csum[rr * K + tk * CK + ci];
         acc += rtm - ctm;
-        ddv[t] = acc;
+        ddv[tk] = acc;
       }
     }
     __syncthreads();

@@ -93,9 +93,10 @@ def compare(w, gpu, ref, tol=None, names=None):
         g = _np64(gpu[k])
         assert g is not None, f"{k} missing from the GPU outputs"
         assert np.all(np.isfinite(g)), f"{k} has non-finite values"
-        e = rel_err(g, ref[k])
-        errs[k] = e
-        assert e <= tol, f"{w.name}: {k} normwise relative error {e:.3e} > {tol:.1e}"
+        errs[k] = rel_err(g, ref[k])
+    bad = {k: e for k, e in errs.items() if not e <= tol}
+    assert not bad, f"{w.name}: normwise relative errors above {tol:.1e}: " + ", ".join(
+        f"{k} {e:.3e}" for k, e in errs.items())
     V = min(w.valid_len, w.s)
     for k in ("d_xhat", "d_bhat", "d_da", "d_rot"):
         if k in gpu and gpu[k] is not None:

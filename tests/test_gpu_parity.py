@@ -47,6 +47,12 @@ SMALL = [
     (W.ROT_PAIRWISE, "f32", dict(h0_sd=None, valid_len=33)),
     (W.ROT_PAIRWISE, "f32", dict(valid_len=31)),   # a single partial chunk
     (W.ROT_QUAT, "bf16", dict(valid_len=96, p=64, r=128, quat_blocks=32, c=4)),
+    # one channel; state rows crossing the 32-row blocks of the bf16 backward
+    (W.ROT_QUAT, "bf16", dict(c=1, p=40, r=128, quat_blocks=8, valid_len=96)),
+    (W.ROT_PAIRWISE, "bf16", dict(c=1, p=40, r=128, rope_dim=64, valid_len=90)),
+    (W.ROT_NONE, "bf16", dict(c=1, p=37, r=64, valid_len=96)),
+    (W.ROT_PAIRWISE, "bf16", dict(c=2, p=70, r=128, rope_dim=64, valid_len=96)),
+    (W.ROT_QUAT, "bf16", dict(c=2, p=33, r=128, quat_blocks=32, valid_len=70)),
 ]
 
 
