@@ -1,0 +1,307 @@
+// Forward main kernel in the transposed state layout (bf16 inputs, K <= 64).
+//
+// Same contract as k_fwd (source: burn-mamba "recalculated.rs" source page,
+// moments_phys_fwd): per (b,h) chain, for a group of kernel chunks, the states
+// h~ (chunk_states plus the boundary carry), the de-rotation c = M h~, and
+// the partial moments m2 += c^T c and m1 += sum_t c over the group.
+//
+// The row work follows k_bwdt: eight waves, wave w computes state row
+// 4*round + (w % 4) for the tokens of half w / 4, transposed (one token per
+// lane, four consecutive state columns per lane), de-rotates in the lane and
+// writes c^T through a per-row LDS transpose. After a barrier every wave
+// reads the round's c fragments (tokens in registers) and accumulates a 2 x 4
+// block of 16 x 16 m2 tiles on MFMA; m1 comes from the same fragments through
+// a ones-row MFMA into a per-block table in LDS.
+#pragma once
+
+#include "kernels_bwdt.h"
+
+namespace mom {
+
+template <int NT, int CK>
+struct LdsF {
+  static constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8;
+  static constexpr size_t bsT = 0;                                    // bhat^T [col][(j,c)]
+  static constexpr size_t xs = bsT + (size_t)R * KP * 2;              // xhat block [p][(j,c)]
+  static constexpr size_t LT = xs + (size_t)XPB * KP * 2;             // L^T [j][t]
+  static constexpr size_t a = LT + (size_t)ELL * LTP * 4;
+  static constexpr size_t d = a + ELL * 4;
+  static constexpr size_t lw = d + ELL * 4;                           // W factors [LWE][64] float4
+  static constexpr size_t cst = lw + (size_t)LWE * 64 * 16;           // carry rows of the round [4][R]
+  static constexpr size_t Gs = cst + (size_t)4 * R * 4;               // c transposes [4][R][GSP]
+  static constexpr size_t rot = Gs + (size_t)4 * R * GSP * 2;
+  static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
+  // m1 table [p][R] fp32 after the rotation table (RT rotated tiles)
+  __host__ __device__ static size_t m1s(int RT) { return rot + (size_t)ELL * (16 * RT + 4) * 4; }
+  __host__ __device__ static size_t total(int RT, int p) { return m1s(RT) + (size_t)p * R * 4; }
+};
+
+template <int NT, int ROT, int CK, int RT>
+__global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__ xhat,
+                                                  const bf16* __restrict__ bhat, const bf16* __restrict__ da,
+                                                  const bf16* __restrict__ rot, const float* __restrict__ carry,
+                                                  float* m2part, float* m1part) {
+  constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8;
+  constexpr int RTP = 16 * RT + 4;
+  constexpr int MA = NT / 4, MB = NT / 2;  // m2 tiles per wave: MA row tiles x MB column tiles
+  static_assert((ROT == 0) == (RT == 0) && RT <= NT && NT % 4 == 0, "tiling");
+  using L = LdsF<NT, CK>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* bsT = (bf16*)(smem + L::bsT);
+  bf16* xs = (bf16*)(smem + L::xs);
+  float* LT = (float*)(smem + L::LT);
+  float* s_a = (float*)(smem + L::a);
+  float* s_d = (float*)(smem + L::d);
+  f4* LWt = (f4*)(smem + L::lw);
+  float* cst = (float*)(smem + L::cst);
+  bf16* Gs = (bf16*)(smem + L::Gs);
+  float* rt = (float*)(smem + L::rot);
+  float* m1s = (float*)(smem + L::m1s(RT));
+
+  const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
+  const int bi = bh / g.h, hi = bh % g.h;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int u = w & 3, tt = w >> 2;
+  const int t = 16 * tt + n;
+  const int ta0 = MA * (w >> 1), tb0 = MB * (w & 1);  // this wave's m2 tiles
+
+  for (int idx = tid; idx < g.p * R; idx += NTT) m1s[idx] = 0.0f;
+
+  auto stage_x = [&](int nc, int pblk) {
+    for (int idx = tid; idx < K * XPB; idx += NTT) {
+      const int k = idx / XPB, pl = idx % XPB;
+      const int j = k / CK, ci = k % CK;
+      const int pos = nc * ELL + j;
+      float v = 0.0f;
+      if (pblk + pl < g.p && ci < g.c && pos < g.V)
+        v = (float)xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + pl];
+      xs[pl * KP + k] = (bf16)v;
+    }
+  };
+  // carry rows of a round through LDS, fetched a round ahead (one float4 per thread)
+  auto fetch_round = [&](int nc, int pr0) -> f4 {
+    f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (tid < R) {
+      const int rr = tid / (R / 4), col = 4 * (tid % (R / 4));
+      const int pp = pr0 + rr;
+      if (pp < g.p) v = load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col);
+    }
+    return v;
+  };
+  auto store_round = [&](f4 v) {
+    if (tid < R) reinterpret_cast<f4*>(cst)[tid] = v;
+  };
+
+  f4 m2acc[MA][MB];
+#pragma unroll
+  for (int a = 0; a < MA; a++)
+#pragma unroll
+    for (int b = 0; b < MB; b++) m2acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  bf8 ones;  // A operand of m1: row 0 all ones over the 32 token slots
+#pragma unroll
+  for (int e = 0; e < 8; e++) ones[e] = (bf16)(n == 0 ? 1.0f : 0.0f);
+
+  const int n0 = gi * g.G;
+  const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
+  const int nrounds = (g.p + 3) / 4;
+  for (int nc = n0; nc < n1; nc++) {
+    __syncthreads();
+    // ---- chunk staging --------------------------------------------------
+    if (tid < 64) {
+      const int tk = tid & 31;
+      const int pos = nc * ELL + tk;
+      float v = 0.0f;
+      if (tid < 32 && pos < g.V) v = (float)da[((size_t)bi * g.s + pos) * g.h + hi];
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float up = __shfl_up(v, off, 32);
+        if (tk >= off) v += up;
+      }
+      if (tid < 32) {
+        s_a[tk] = v;
+        s_d[tk] = expf(v);
+      }
+    }
+    for (int idx = tid; idx < K * R; idx += NTT) {
+      const int k = idx / R, col = idx % R;
+      const int j = k / CK, ci = k % CK;
+      const int pos = nc * ELL + j;
+      bf16 v = (bf16)0.0f;
+      if (col < g.r && pos < g.V && ci < g.c)
+        v = bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, col)];
+      bsT[col * KP + k] = v;
+    }
+    if constexpr (ROT == 1) {
+      for (int idx = tid; idx < ELL * 8 * RT; idx += NTT) {
+        const int tk = idx / (8 * RT), a = idx % (8 * RT);
+        const int pos = nc * ELL + tk;
+        float th = 0.0f;
+        if (a < g.A && pos < g.V) th = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + a];
+        float sv, cv;
+        sincosf(th, &sv, &cv);
+        rt[tk * RTP + 2 * a] = cv;
+        rt[tk * RTP + 2 * a + 1] = sv;
+      }
+    } else if constexpr (ROT == 3) {
+      for (int idx = tid; idx < ELL * 16 * RT; idx += NTT) {
+        const int tk = idx / (16 * RT), e = idx % (16 * RT);
+        const int pos = nc * ELL + tk;
+        float v = (e & 3) == 0 ? 1.0f : 0.0f;
+        if ((e >> 2) < g.J && pos < g.V) v = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e];
+        rt[tk * RTP + e] = v;
+      }
+    }
+    stage_x(nc, 0);
+    store_round(fetch_round(nc, 0));
+    __syncthreads();
+    for (int idx = tid; idx < ELL * ELL; idx += NTT) {
+      const int j = idx / ELL, tk = idx % ELL;
+      LT[j * LTP + tk] = (j <= tk) ? expf(s_a[tk] - s_a[j]) : 0.0f;
+    }
+    __syncthreads();
+    const int tv = g.V - nc * ELL;  // valid tokens of this chunk (>= 1)
+    if (w == 0) {
+#pragma unroll
+      for (int f = 0; f < 16; f++) {
+        const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), v = rest % (8 / CK);
+        reinterpret_cast<float*>(LWt + (f >> 2) * 64 + lane)[f & 3] =
+            LT[((32 * ks + 8 * q) / CK + v) * LTP + 16 * hh + n];
+      }
+    }
+    __syncthreads();
+    const float dtl = s_d[t];
+    const bool live = t < tv;  // tokens past valid_len contribute nothing
+
+    for (int round = 0; round < nrounds; round++) {
+      const int pr0 = 4 * round;
+      const int pblk = pr0 - pr0 % XPB;
+      if (round > 0 && pr0 % XPB == 0) {
+        stage_x(nc, pblk);
+        __syncthreads();
+      }
+      const int p = pr0 + u;
+      const f4 pf = fetch_round(nc, pr0 + 4);
+      if (p < g.p) {
+        const int pl = p - pblk;
+        // ---- W fragment --------------------------------------------------------
+        u4 Wf[CK];
+        {
+          float xv[CK][8];
+#pragma unroll
+          for (int ks = 0; ks < CK; ks++) {
+            const u4 x8 = *reinterpret_cast<const u4*>(xs + pl * KP + 32 * ks + 8 * q);
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              xv[ks][2 * e] = bf16_lo(x8[e]);
+              xv[ks][2 * e + 1] = bf16_hi(x8[e]);
+            }
+          }
+          float lw[8];
+#pragma unroll
+          for (int e4 = 0; e4 < 2; e4++) {
+            const f4 v = LWt[(2 * tt + e4) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; i++) lw[4 * e4 + i] = v[i];
+          }
+#pragma unroll
+          for (int ks = 0; ks < CK; ks++)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const int b0 = ks * (8 / CK);
+              Wf[ks][e / 2] = pk_bf16(lw[b0 + e / CK] * xv[ks][e], lw[b0 + (e + 1) / CK] * xv[ks][e + 1]);
+            }
+        }
+        // ---- states, transposed ---------------------------------------------------
+        f4 hT[NT];
+#pragma unroll
+        for (int ct = 0; ct < NT; ct++) hT[ct] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        const int nks = tt == 0 ? (CK + 1) / 2 : CK;
+#pragma unroll
+        for (int ks = 0; ks < CK; ks++) {
+          if (ks < nks) {
+#pragma unroll
+            for (int ct = 0; ct < NT; ct++) {
+              const bf8 a = ld_frag(bsT + (16 * ct + n) * KP + 32 * ks + 8 * q);
+              hT[ct] = MM<bf16>::mma(a, as_bf8(Wf[ks]), hT[ct]);
+            }
+          }
+        }
+        // ---- carry, de-rotation, c^T into the row's transpose buffer --------------
+        const float* hrow = cst + u * R;
+        unsigned short* Gw = reinterpret_cast<unsigned short*>(Gs) + (size_t)u * R * GSP + t;
+#pragma unroll
+        for (int ct = 0; ct < NT; ct++) {
+          const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
+          f4 h;
+#pragma unroll
+          for (int i = 0; i < 4; i++) h[i] = hT[ct][i] + dtl * hv[i];
+          f4 c = h;
+          if constexpr (ROT == 1) {
+            if (ct < RT) {
+              const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+              c[0] = r4[0] * h[0] + r4[1] * h[1];
+              c[1] = r4[0] * h[1] - r4[1] * h[0];
+              c[2] = r4[2] * h[2] + r4[3] * h[3];
+              c[3] = r4[2] * h[3] - r4[3] * h[2];
+            }
+          } else if constexpr (ROT == 3) {
+            if (ct < RT) {
+              const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+              c[0] = Q[0] * h[0] - Q[1] * h[1] - Q[2] * h[2] - Q[3] * h[3];
+              c[1] = Q[0] * h[1] + Q[1] * h[0] + Q[2] * h[3] - Q[3] * h[2];
+              c[2] = Q[0] * h[2] - Q[1] * h[3] + Q[2] * h[0] + Q[3] * h[1];
+              c[3] = Q[0] * h[3] + Q[1] * h[2] - Q[2] * h[1] + Q[3] * h[0];
+            }
+          }
+          const unsigned w0 = live ? pk_bf16(c[0], c[1]) : 0u;
+          const unsigned w1 = live ? pk_bf16(c[2], c[3]) : 0u;
+          const int col = 16 * ct + 4 * q;
+          Gw[col * GSP] = (unsigned short)(w0 & 0xffffu);
+          Gw[(col + 1) * GSP] = (unsigned short)(w0 >> 16);
+          Gw[(col + 2) * GSP] = (unsigned short)(w1 & 0xffffu);
+          Gw[(col + 3) * GSP] = (unsigned short)(w1 >> 16);
+        }
+      }
+      __syncthreads();  // the round's c transposes are complete
+      // ---- m2 += c^T c over the round's rows and tokens; m1 row sums -------------
+#pragma unroll 1
+      for (int rr = 0; rr < 4; rr++) {
+        const int pp = pr0 + rr;
+        if (pp >= g.p) break;
+        const bf16* Gr = Gs + (size_t)rr * R * GSP;
+        bf8 fa[MA], fb[MB];
+#pragma unroll
+        for (int a = 0; a < MA; a++) fa[a] = ld_frag(Gr + (16 * (ta0 + a) + n) * GSP + 8 * q);
+#pragma unroll
+        for (int b = 0; b < MB; b++) fb[b] = ld_frag(Gr + (16 * (tb0 + b) + n) * GSP + 8 * q);
+#pragma unroll
+        for (int a = 0; a < MA; a++)
+#pragma unroll
+          for (int b = 0; b < MB; b++) m2acc[a][b] = MM<bf16>::mma(fa[a], fb[b], m2acc[a][b]);
+        if ((w >> 1) == rr) {  // m1 of this row over this wave's column tiles
+#pragma unroll
+          for (int b = 0; b < MB; b++) {
+            const f4 s1 = MM<bf16>::mma(ones, fb[b], f4{0.0f, 0.0f, 0.0f, 0.0f});
+            if (q == 0) m1s[pp * R + 16 * (tb0 + b) + n] += s1[0];
+          }
+        }
+      }
+      store_round(pf);
+      __syncthreads();  // transposes consumed; next round's carry rows staged
+    }
+  }
+  __syncthreads();
+  // ---- the group's partials: m2 tiles straight out, m1 rows from LDS ----------
+  float* m2o = m2part + ((size_t)bh * g.NGR + gi) * R * R;
+#pragma unroll
+  for (int a = 0; a < MA; a++)
+#pragma unroll
+    for (int b = 0; b < MB; b++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) m2o[(16 * (ta0 + a) + 4 * q + i) * R + 16 * (tb0 + b) + n] = m2acc[a][b][i];
+  float* m1o = m1part + ((size_t)bh * g.NGR + gi) * g.p * R;
+  for (int idx = tid; idx < g.p * R; idx += NTT) m1o[idx] = m1s[idx];
+}
+
+}  // namespace mom

@@ -11,6 +11,7 @@
 
 #include "kernels_bwd.h"
 #include "kernels_bwdt.h"
+#include "kernels_fwdt.h"
 
 using namespace mom;
 
@@ -79,6 +80,7 @@ struct Plan {
   int NT, R;    // state columns padded to R = 16*NT
   int PK;       // state rows padded for MFMA K over rows
   bool bwdt;    // backward main kernel in the transposed layout (bf16, c <= 2)
+  bool fwdt;    // forward main kernel in the transposed layout (bf16, c <= 2)
   size_t carry, dec, m2p, m1p, db, dm1i;  // workspace offsets
   size_t ws_fwd, ws_bwd;
 };
@@ -88,6 +90,16 @@ int round_nt(int r, bool /*bf*/) {
   if (nt <= 4) nt = 4;
   else nt = 8;
   return nt;
+}
+
+// LDS bytes of k_fwdt for (NT, CK), or 0 when that kernel does not cover the shape.
+size_t fwdt_lds(const Geo& g, int NT, int CK) {
+  const int RT = rot_tiles(g);
+  if (NT == 4 && CK == 1) return LdsF<4, 1>::total(RT, g.p);
+  if (NT == 4 && CK == 2) return LdsF<4, 2>::total(RT, g.p);
+  if (NT == 8 && CK == 1) return LdsF<8, 1>::total(RT, g.p);
+  if (NT == 8 && CK == 2) return LdsF<8, 2>::total(RT, g.p);
+  return 0;
 }
 
 // LDS bytes of k_bwdt for (NT, CK), or 0 when that kernel does not cover the shape.
@@ -178,6 +190,12 @@ int make_plan(const moments_desc* d, Plan* P) {
   P->db = base;
   o = align256(base + chains * (size_t)g.NK * pr * 4);
   if (bf && P->CK <= 2) {
+    const size_t lf = fwdt_lds(g, P->NT, P->CK);
+    P->fwdt = lf > 0 && lf <= kLdsLimit;
+  } else {
+    P->fwdt = false;
+  }
+  if (bf && P->CK <= 2) {
     const size_t lb = bwdt_lds(g, P->NT, P->CK);
     P->bwdt = lb > 0 && lb <= kLdsLimit;
   } else {
@@ -251,7 +269,36 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   float* m2p = (float*)(ws + P.m2p);
   float* m1p = (float*)(ws + P.m1p);
   const int chains = g.b * g.h;
-  if (g.NK >= 1) {
+  bool done = false;
+  if constexpr (std::is_same<T, bf16>::value && CK <= 2) {
+    if (P.fwdt && g.NK >= 1) {
+      const int RT = rot_tiles(g);
+      auto launch = [&](auto rot_c, auto rt_c) -> int {
+        constexpr int RO = decltype(rot_c)::value, RTc = decltype(rt_c)::value;
+        const size_t lds = LdsF<NT, CK>::total(RTc, g.p);
+        MOM_TRY(set_lds(k_fwdt<NT, RO, CK, RTc>, lds));
+        ProfScope ps(KID_FWD, st);
+        hipLaunchKernelGGL((k_fwdt<NT, RO, CK, RTc>), dim3(chains * g.NGR), dim3(NTT), lds, st, g, X, B, D, Rt,
+                           (const float*)(ws + P.carry), m2p, m1p);
+        return check_launch();
+      };
+      int rc = MOMENTS_ENOTSUP;
+      if constexpr (ROT == 0) {
+        rc = launch(IC<0>{}, IC<0>{});
+      } else {
+        if (RT == 0) rc = launch(IC<0>{}, IC<0>{});
+        else if (RT == 1) rc = launch(IC<ROT>{}, IC<1>{});
+        else if (RT == 2) rc = launch(IC<ROT>{}, IC<2>{});
+        else if (RT == 4) rc = launch(IC<ROT>{}, IC<4>{});
+        else if (RT == 8) {
+          if constexpr (NT >= 8) rc = launch(IC<ROT>{}, IC<8>{});
+        }
+      }
+      MOM_TRY(rc);
+      done = true;
+    }
+  }
+  if (!done && g.NK >= 1) {
     const size_t lds = lds_fwd(g, P.R, sizeof(T), P.NT).total;
     MOM_TRY(set_lds(k_fwd<T, NT, ROT, CK>, lds));
     ProfScope ps(KID_FWD, st);
