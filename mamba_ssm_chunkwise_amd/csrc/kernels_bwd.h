@@ -545,6 +545,192 @@ __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Group fix-up of the transposed backward (k_bwdt walks each group of chunks
+// backward with D = 0 entering at the group's end). For group g covering chunks
+// [n0_g, n1_g), with D_in(n) the walk's value and Q_g(n) = prod_{k=n}^{n1_g-1}
+// dec_k, the recurrence D(n) = local(n) + dec_n D(n+1) gives
+//   D(n) = D_in(n) + Q_g(n) D_B(g),   D_B(g) = D(n1_g) = D(n0_{g+1}),
+// so D_B(g) = D_in(n0_{g+1}) + Q_{g+1}(n0_{g+1}) D_B(g+1), D_B(last) = 0, and
+// chunk n of group g still lacks the carry cotangent Q_g(n+1) D_B(g).
+// ---------------------------------------------------------------------------
+
+// k_gscan: DB[bh][g] = D_B(g) for g < NGR-1, and d_h0 = D(0).
+template <typename T>
+__global__ __launch_bounds__(NTH) void k_gscan(Geo g, const float* __restrict__ Db,
+                                               const float* __restrict__ dec, float* DB, T* d_h0) {
+  const int bh = blockIdx.x;
+  const int e = blockIdx.y * NTH + threadIdx.x;
+  const int pr = g.p * g.r;
+  if (e >= pr) return;
+  const float* Dc = dec + (size_t)bh * g.NK;
+  auto qprod = [&](int gr) {  // Q over the whole group gr (its chunks are all < NK-1 here)
+    const int a = gr * g.G, b = (a + g.G < g.NK) ? a + g.G : g.NK;
+    float qv = 1.0f;
+    for (int k = a; k < b; k++) qv *= Dc[k];
+    return qv;
+  };
+  float D = 0.0f;  // D_B(g + 1) while walking down
+  for (int gr = g.NGR - 2; gr >= 0; gr--) {
+    const int n0n = (gr + 1) * g.G;
+    const float din = Db[((size_t)bh * g.NK + n0n) * pr + e];
+    D = (gr + 1 < g.NGR - 1) ? din + qprod(gr + 1) * D : din;
+    DB[((size_t)bh * g.NGR + gr) * pr + e] = D;
+  }
+  if (d_h0 != nullptr) {
+    float d0 = g.NK > 0 ? Db[(size_t)bh * g.NK * pr + e] : 0.0f;
+    if (g.NGR > 1) d0 += qprod(0) * D;
+    const int p0 = e / g.r, rc = e % g.r;
+    d_h0[((size_t)bh * g.p + p0) * g.r + perm_rc(g, rc)] = to_t<T>(d0);
+  }
+}
+
+// k_gfix: for group g < NGR-1 of chain bh, chunks n = n1_g-1 down to n0_g while
+// the scale Q_g(n+1) is nonzero, add the carry-cotangent terms of
+// D+ = Q_g(n+1) D_B(g), the cotangent of h~[l-1] = h_-(n+1):
+//   v[p][(j,c)] = sum_col D+[p][col] bhat[j,c,col]   d_xhat += L[l-1,j] v
+//   y[col][(j,c)] = sum_p D+[p][col] xhat[j,c,p]     d_bhat += L[l-1,j] y
+//   d_da_s += d_{l-1} <D+, h_-(n)> + sum_{j<s} L[l-1,j] sum_c <xhat[j,c], v[:, (j,c)]>
+// (d_da in its direct form, as in k_bwdt).
+// Once Q underflows to zero every later term is exactly zero, so the walk stops.
+template <typename T, int NT, int CK>
+__global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restrict__ xhat,
+                                                  const T* __restrict__ bhat, const T* __restrict__ da,
+                                                  const float* __restrict__ carry, const float* __restrict__ dec,
+                                                  const float* __restrict__ DB, T* d_xhat, T* d_bhat, T* d_da) {
+  constexpr int R = 16 * NT, KS = MM<T>::KS, E = MM<T>::E, K = ELL * CK, RP = R + pad_of<T>();
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Lds L = lds_fix(g, R, sizeof(T), PK);
+  const int PP = g.PP;
+  float* s_a = (float*)(smem + L.a);
+  float* s_d = (float*)(smem + L.d);
+  float* s_L = (float*)(smem + L.L);
+  T* dp = (T*)(smem + L.lx);
+  T* dpt = (T*)(smem + L.ltx);
+  T* bn = (T*)(smem + L.bs);
+  T* xn = (T*)(smem + L.xr);
+  float* xv = (float*)(smem + L.red);
+  float* red = xv + K;
+  float* ddv = red + NTH;
+
+  const int ng = g.NGR - 1;
+  const int bh = blockIdx.x / ng, grp = blockIdx.x % ng;
+  const int bi = bh / g.h, hi = bh % g.h;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
+  const int pr = g.p * g.r;
+  const float* Dp = DB + ((size_t)bh * g.NGR + grp) * pr;
+  for (int idx = threadIdx.x; idx < PK * R; idx += NTH) {
+    const int pp = idx / R, rc = idx % R;
+    const float v = (pp < g.p && rc < g.r) ? Dp[pp * g.r + rc] : 0.0f;
+    dp[pp * RP + rc] = to_t<T>(v);
+    dpt[rc * PP + pp] = to_t<T>(v);
+  }
+  const int n0 = grp * g.G;
+  const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
+  float Q = 1.0f;
+  for (int n = n1 - 1; n >= n0 && Q != 0.0f; n--) {
+    __syncthreads();
+    stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
+    for (int idx = threadIdx.x; idx < K * R; idx += NTH) {
+      const int k = idx / R, rc = idx % R;
+      const int j = k / CK, ci = k % CK;
+      const int pos = n * ELL + j;
+      float v = 0.0f;
+      if (rc < g.r && ci < g.c) v = to_f(bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, rc)]);
+      bn[k * RP + rc] = to_t<T>(v);
+    }
+    for (int idx = threadIdx.x; idx < K * PK; idx += NTH) {
+      const int k = idx / PK, pp = idx % PK;
+      const int j = k / CK, ci = k % CK;
+      const int pos = n * ELL + j;
+      float v = 0.0f;
+      if (pp < g.p && ci < g.c) v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp]);
+      xn[k * PP + pp] = to_t<T>(v);
+    }
+    const float* Hn = carry + ((size_t)bh * g.NK + n) * pr;  // h_-(n), entering the chunk
+    float hd = 0.0f;
+    for (int e = threadIdx.x; e < pr; e += NTH) hd += Dp[e] * Hn[e];
+    red[threadIdx.x] = hd;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float s = 0.0f;
+      for (int i = 0; i < NTH; i++) s += red[i];
+      red[0] = s;
+    }
+    __syncthreads();
+    hd = Q * s_d[ELL - 1] * red[0];
+    const float* ll = s_L + (ELL - 1) * (ELL + 1);
+    constexpr int NTK = K / 16;
+    for (int nt = w; nt < NTK; nt += NW) {
+      const int k = 16 * nt + m;
+      const int j = k / CK, ci = k % CK;
+      const int pos = n * ELL + j;
+      const float lj = Q * ll[j];
+      float xsum = 0.0f;
+      for (int mt = 0; mt < PK / 16; mt++) {
+        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int ks = 0; ks < R / KS; ks++) {
+          const int k0 = ks * KS + E * q;
+          acc = MM<T>::mma(ld_frag(dp + (16 * mt + m) * RP + k0), ld_frag(bn + (16 * nt + m) * RP + k0), acc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int pp = 16 * mt + 4 * q + i;
+          if (pp < g.p && ci < g.c) {
+            xsum += to_f(xn[k * PP + pp]) * acc[i];
+            if (d_xhat != nullptr) {
+              T* dst = d_xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp;
+              *dst = to_t<T>(to_f(*dst) + lj * acc[i]);
+            }
+          }
+        }
+      }
+      xsum = col4_sum(xsum);
+      if (q == 0) xv[k] = Q * xsum;
+    }
+    if (d_bhat != nullptr) {
+      for (int nt = w; nt < NTK; nt += NW) {
+        const int k = 16 * nt + m;
+        const int j = k / CK, ci = k % CK;
+        const int pos = n * ELL + j;
+        const float lj = Q * ll[j];
+        for (int mt = 0; mt < NT; mt++) {
+          f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+          for (int ks = 0; ks < PK / KS; ks++) {
+            const int k0 = ks * KS + E * q;
+            acc = MM<T>::mma(ld_frag(dpt + (16 * mt + m) * PP + k0), ld_frag(xn + (16 * nt + m) * PP + k0), acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int rc = 16 * mt + 4 * q + i;
+            if (rc < g.r && ci < g.c) {
+              T* dst = d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, rc);
+              *dst = to_t<T>(to_f(*dst) + lj * acc[i]);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float acc = 0.0f;
+      for (int j = 0; j < ELL; j++) {
+        ddv[j] = hd + acc;
+        float cj = 0.0f;
+        for (int ci = 0; ci < g.c; ci++) cj += xv[j * CK + ci];
+        acc += ll[j] * cj;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < ELL && d_da != nullptr) {
+      const int pos = n * ELL + threadIdx.x;
+      T* dst = d_da + ((size_t)bi * g.s + pos) * g.h + hi;
+      *dst = to_t<T>(to_f(*dst) + ddv[threadIdx.x]);
+    }
+    Q *= dec[(size_t)bh * g.NK + n];
+  }
+}
+
 // Zeros for every gradient at positions [z0, s) (chunks never processed).
 template <typename T>
 __global__ __launch_bounds__(NTH) void k_zero_tail(Geo g, int z0, T* d_xhat, T* d_bhat, T* d_da,

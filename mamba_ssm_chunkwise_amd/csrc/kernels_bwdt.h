@@ -1,11 +1,22 @@
 // Backward main kernel in the transposed state layout (bf16 inputs, K <= 64).
 //
-// Same contract as k_bwd (sources: burn-mamba "recalculated.rs" and
-// "backward.rs" source pages, moments_phys_bwd and its module doc "Gradient
-// math"): per (b,h) chain and kernel chunk it recomputes the states, applies
-// the de-rotation, and writes d_xhat, d_bhat, d_da without the carry-cotangent
-// terms, d_rot complete, and local(n)[p][col] = sum_t d_t G[t][p][col] for the
-// carry-cotangent recurrence.
+// Sources: burn-mamba "recalculated.rs" and "backward.rs" source pages,
+// moments_phys_bwd and its module doc "Gradient math". Per (b,h) chain a
+// workgroup owns a group of consecutive kernel chunks and walks them from the
+// last to the first. For each chunk it recomputes the states, applies the
+// de-rotation and forms G = M^T d_c; the cotangent D(n+1) of the state leaving
+// the chunk (computed by the previous step of the walk, zero at the group's
+// end) is added to G at the chunk's last token. Then
+//   D(n) = sum_t d_t G[t]            (the carry-cotangent recurrence, written
+//                                     to Db[n] for the next step of the walk)
+// and d_xhat, d_bhat, d_da and d_rot of the chunk follow from G. d_da is taken
+// in its direct form (differentiate a_t = cumsum da inside L and d):
+//   d_da_s = sum_{t>=s} ( d_t <G[t], h_-> + sum_{j<s} L[t,j] <G[t], W_j> ),
+// with <G[t], W_j> = sum_c sum_p xhat[j,c,p] Y_p[t,(j,c)]; unlike the
+// reverse-cumsum identity it has no cancellation between large terms when the
+// decay is strong. They are exact
+// except for the cotangent entering at the group's end, which the group fix-up
+// adds afterwards (k_gscan, k_gfix).
 //
 // Layout. The states are computed transposed, h~^T[col][t] = bhat^T W^T with
 // W[t][(j,c)] = L[t,j] xhat[j,c,p], so an accumulator lane holds one token and
@@ -79,14 +90,16 @@ struct LdsT {
   static constexpr size_t a = LT + (size_t)ELL * LTP * 4;
   static constexpr size_t d = a + ELL * 4;
   static constexpr size_t lw = d + ELL * 4;
-  static constexpr size_t cst = lw + (size_t)(LWE + 2 * (K / 16)) * 64 * 16;  // carry, d_m1 rows [2][4][R]
-  static constexpr size_t dxp = cst + (size_t)2 * 4 * R * 4;                   // d_xhat partials [2][4][K]
+  static constexpr size_t cst = lw + (size_t)(LWE + 2 * (K / 16)) * 64 * 16;  // carry, d_m1, D+ rows [3][4][R]
+  static constexpr size_t dxp = cst + (size_t)3 * 4 * R * 4;                   // d_xhat partials [2][4][K]
   static constexpr size_t red = dxp + (size_t)2 * 4 * K * 4;
   static constexpr size_t nred = (size_t)NWT * 4 * 16 + 4 * K + ELL;          // floats of red
-  // G transposes of the round's rows; at chunk end the d_bhat tile and the
-  // rotation-gradient reduction reuse the space
-  static constexpr size_t gsb = (size_t)4 * R * GSP * 2 > (size_t)K * SP * 2 ? (size_t)4 * R * GSP * 2
-                                                                             : (size_t)K * SP * 2;
+  // G transposes of the round's rows; at chunk end the d_bhat tile, the
+  // rotation-gradient reduction and the d_da partials reuse the space
+  static constexpr size_t gs0 = (size_t)4 * R * GSP * 2;                       // G transposes
+  static constexpr size_t gs1 = (size_t)K * SP * 2;                            // d_bhat tile
+  static constexpr size_t gs2 = (size_t)NWT * 16 * K * 4 + (size_t)ELL * ELL * 4;  // d_da partials
+  static constexpr size_t gsb = gs0 > gs1 ? (gs0 > gs2 ? gs0 : gs2) : (gs1 > gs2 ? gs1 : gs2);
   static constexpr size_t Gs = red + nred * 4;
   static constexpr size_t rot = Gs + gsb;
   static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
@@ -154,7 +167,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   float* red = (float*)(smem + L::red);
   f4* LWt = (f4*)(smem + L::lw);          // [LWE][64]
   f4* LYt = LWt + LWE * 64;               // [2*NKT][64]
-  float* cst = (float*)(smem + L::cst);   // [carry | d_m1][row of the round][R]
+  float* cst = (float*)(smem + L::cst);   // [carry | d_m1 | D+][row of the round][R]
   float* dxp = (float*)(smem + L::dxp);   // [token half][row of the round][K]
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
@@ -202,12 +215,13 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         d_xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + pl] = dXs[pl * KP + k];
     }
   };
-  // The carry rows h_-(n)[p][:] and the d_m1 rows of a round (4 state rows)
-  // travel through LDS: every thread fetches one float4 of them a round ahead
-  // and stores it after the round's d_bhat work, off the rows' critical path.
-  constexpr int CQ = 2 * 4 * R / 4;  // float4 pieces per round
+  // The carry rows h_-(n)[p][:], the d_m1 rows and the D(n+1) rows of a round
+  // (4 state rows) travel through LDS: every thread fetches one float4 of them
+  // a round ahead and stores it after the round's d_bhat work, off the rows'
+  // critical path. D(n+1) was written by this workgroup one chunk earlier.
+  constexpr int CQ = 3 * 4 * R / 4;  // float4 pieces per round
   static_assert(CQ <= NTT, "one piece per thread");
-  auto fetch_round = [&](int nc, int pr0) -> f4 {
+  auto fetch_round = [&](int nc, int pr0, bool has_next) -> f4 {
     f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
     if (tid < CQ) {
       const int arr = tid / (4 * R / 4), rest = tid % (4 * R / 4);
@@ -215,7 +229,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       const int pp = pr0 + rr;
       if (pp < g.p) {
         if (arr == 0) v = load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col);
-        else v = *reinterpret_cast<const f4*>(dm1i + ((size_t)bh * g.p + pp) * R + col);
+        else if (arr == 1) v = *reinterpret_cast<const f4*>(dm1i + ((size_t)bh * g.p + pp) * R + col);
+        else if (has_next) v = load_cols4(Db + (((size_t)bh * g.NK + nc + 1) * g.p + pp) * g.r, g.r, col);
       }
     }
     return v;
@@ -227,7 +242,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
   const int nrounds = (g.p + 3) / 4;
-  for (int nc = n0; nc < n1; nc++) {
+  for (int nc = n1 - 1; nc >= n0; nc--) {
+    const bool has_next = nc + 1 < n1;  // D(n+1) comes from this walk; zero at the group's end
     __syncthreads();
     // ---- chunk staging --------------------------------------------------
     if (tid < 64) {
@@ -276,7 +292,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       }
     }
     stage_x(nc, 0);
-    store_round(fetch_round(nc, 0));
+    store_round(fetch_round(nc, 0, has_next));
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, tk = idx % ELL;
@@ -317,8 +333,10 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     for (int ct = 0; ct < RTA; ct++)
 #pragma unroll
       for (int v = 0; v < NRC; v++) racc[ct][v] = 0.0f;
-    float gacc = 0.0f;  // sum over this wave's rows and columns of <d_c, c> at token t
-    float cct = 0.0f;   // thread (rr, k) < 4K: sum over rows rr of the rounds of xhat * d_xhat
+    float gcar = 0.0f;  // sum over this wave's rows and columns of G[t] h_- at token t
+    f4 Aacc[NKT];       // sum over this wave's rows of xhat[(j,c)][p] Y_p[t][(j,c)], t = 16tt+4q+i, (j,c) = 16kt+n
+#pragma unroll
+    for (int kt = 0; kt < NKT; kt++) Aacc[kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
     const float dtl = s_d[t];
 
     for (int round = 0; round < nrounds; round++) {
@@ -331,7 +349,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         __syncthreads();
       }
       const int p = pr0 + u;
-      const f4 pf = fetch_round(nc, pr0 + 4);  // next round's rows, stored after the d_bhat work
+      const f4 pf = fetch_round(nc, pr0 + 4, has_next);  // next round's rows, stored after the d_bhat work
       // One state row, all columns, this wave's 16 tokens; MASK zeroes d_c at
       // tokens >= tv (only the chunk holding valid_len needs it).
       auto row = [&](auto mask_tag) {
@@ -385,6 +403,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         u4 cP[KSR];
         u4 hP[ROT == 3 ? KSR : 1];
         const float* hrow = cst + u * R;
+        const float* dprow = cst + (8 + u) * R;  // D(n+1)[p][:], enters G at the last token
+        const float f31 = t == ELL - 1 ? 1.0f : 0.0f;
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
           const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
@@ -458,9 +478,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
                 ra[2] += -d[0] * hc[2] + d[1] * hc[3] + d[2] * hc[0] - d[3] * hc[1];
                 ra[3] += -d[0] * hc[3] - d[1] * hc[2] + d[2] * hc[1] + d[3] * hc[0];
               }
-              gacc += G[0] * hc[0] + G[1] * hc[1] + G[2] * hc[2] + G[3] * hc[3];
             } else {
-              gacc += d[0] * hc[0] + d[1] * hc[1] + d[2] * hc[2] + d[3] * hc[3];
               if constexpr (ROT == 1) {
                 if (ct < RT) {
                   const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
@@ -473,6 +491,15 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
                   G[3] = r4[3] * d[2] + r4[2] * d[3];
                 }
               }
+            }
+            if (tt == 1 && has_next) {
+              const f4 dp = *reinterpret_cast<const f4*>(dprow + 16 * ct + 4 * q);
+#pragma unroll
+              for (int i = 0; i < 4; i++) G[i] += f31 * dp[i];
+            }
+            {
+              const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
+              gcar += G[0] * hv[0] + G[1] * hv[1] + G[2] * hv[2] + G[3] * hv[3];
             }
             GP[2 * h2] = pk_bf16(G[0], G[1]);
             GP[2 * h2 + 1] = pk_bf16(G[2], G[3]);
@@ -500,6 +527,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           float v = ly[0] * Y[kt][0] + ly[1] * Y[kt][1] + ly[2] * Y[kt][2] + ly[3] * Y[kt][3];
           v = col4_sum(v);
           if (q == 0) part[16 * kt + n] = v;
+          const float xk = (float)xs[pl * KP + 16 * kt + n];
+#pragma unroll
+          for (int i = 0; i < 4; i++) Aacc[kt][i] += xk * Y[kt][i];
         }
       };
       if (p < g.p) {
@@ -515,7 +545,6 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           const float v = dxp[rr * K + k] + dxp[(4 + rr) * K + k];
           const int pl = pp - pblk;
           dXs[pl * KP + k] = (bf16)v;
-          cct += v * (float)xs[pl * KP + k];
         }
       }
       // ---- d_bhat[(j,c)][col] += sum_t L[t,j] xhat[(j,c)][p] G[t][col]; local ----
@@ -615,25 +644,44 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
       }
     }
-    // ---- d_da without the carry-cotangent terms --------------------------------
-    float* rsum = red;                    // [w][q][16]
-    float* csum = red + NWT * 4 * 16;     // [rr][(j,c)]
-    float* ddv = csum + 4 * K;            // [t]
-    rsum[(w * 4 + q) * 16 + n] = gacc;
-    if (tid < 4 * K) csum[tid] = cct;
+    // ---- d_da, direct form ---------------------------------------------------------
+    __syncthreads();                      // G space free again
+    float* rg = red;                      // [w][q][16] partial G h_-
+    float* gct = red + NWT * 4 * 16;      // [t]
+    float* ddv = gct + ELL;               // [t]
+    float* Ap = (float*)Gs;               // [w][16 tokens][K] partial <G[t], W_(j,c)>
+    float* Am = Ap + NWT * 16 * K;        // [t][j]
+    rg[(w * 4 + q) * 16 + n] = gcar;
+#pragma unroll
+    for (int kt = 0; kt < NKT; kt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) Ap[(w * 16 + 4 * q + i) * K + 16 * kt + n] = Aacc[kt][i];
     __syncthreads();
-    if (tid == 0) {
-      float acc = 0.0f;
-      for (int tk = ELL - 1; tk >= 0; tk--) {
-        const int half = tk >> 4;
-        float rtm = 0.0f, ctm = 0.0f;
-        for (int uu = 0; uu < 4; uu++)
-          for (int qq = 0; qq < 4; qq++) rtm += rsum[((4 * half + uu) * 4 + qq) * 16 + (tk & 15)];
-        for (int rr = 0; rr < 4; rr++)
-          for (int ci = 0; ci < g.c; ci++) ctm += csum[rr * K + tk * CK + ci];
-        acc += rtm - ctm;
-        ddv[tk] = acc;
+    for (int idx = tid; idx < ELL * ELL; idx += NTT) {
+      const int tk = idx / ELL, j = idx % ELL;
+      const int half = tk >> 4;
+      float a = 0.0f;
+      for (int uu = 0; uu < 4; uu++)
+        for (int ci = 0; ci < g.c; ci++) a += Ap[((4 * half + uu) * 16 + (tk & 15)) * K + j * CK + ci];
+      Am[tk * ELL + j] = a;
+    }
+    if (tid < ELL) {
+      const int half = tid >> 4;
+      float a = 0.0f;
+      for (int uu = 0; uu < 4; uu++)
+        for (int qq = 0; qq < 4; qq++) a += rg[((4 * half + uu) * 4 + qq) * 16 + (tid & 15)];
+      gct[tid] = a;
+    }
+    __syncthreads();
+    if (tid < ELL) {
+      const int sp = tid;
+      float a = 0.0f;
+      for (int tk = sp; tk < ELL; tk++) {
+        float b = s_d[tk] * gct[tk];
+        for (int j = 0; j < sp; j++) b += LT[j * LTP + tk] * Am[tk * ELL + j];
+        a += b;
       }
+      ddv[sp] = a;
     }
     __syncthreads();
     if (tid < ELL && d_da != nullptr) {

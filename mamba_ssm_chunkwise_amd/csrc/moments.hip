@@ -22,9 +22,12 @@ std::atomic<int> g_last_hip{0};
 constexpr size_t kLdsLimit = 160 * 1024;
 
 // ---- optional per-kernel event timing (moments_profile_*) -------------------
-enum KernelId { KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_PREP, KID_N };
-const char* const kKernelNames[KID_N] = {"k_carry", "k_scan", "k_fwd", "k_reduce",
-                                         "k_bwd", "k_dscan", "k_fix", "k_zero_tail", "k_prep_dm1"};
+enum KernelId {
+  KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_PREP, KID_GSCAN, KID_GFIX,
+  KID_N
+};
+const char* const kKernelNames[KID_N] = {"k_carry", "k_scan",      "k_fwd",      "k_reduce", "k_bwd",  "k_dscan",
+                                         "k_fix",   "k_zero_tail", "k_prep_dm1", "k_gscan",  "k_gfix"};
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -81,7 +84,7 @@ struct Plan {
   int PK;       // state rows padded for MFMA K over rows
   bool bwdt;    // backward main kernel in the transposed layout (bf16, c <= 2)
   bool fwdt;    // forward main kernel in the transposed layout (bf16, c <= 2)
-  size_t carry, dec, m2p, m1p, db, dm1i;  // workspace offsets
+  size_t carry, dec, m2p, m1p, db, dm1i, gdb;  // workspace offsets
   size_t ws_fwd, ws_bwd;
 };
 
@@ -203,6 +206,8 @@ int make_plan(const moments_desc* d, Plan* P) {
   }
   P->dm1i = o;
   if (P->bwdt) o = align256(o + chains * (size_t)g.p * P->R * 4);
+  P->gdb = o;  // per-group boundary cotangents of the transposed backward
+  if (P->bwdt) o = align256(o + chains * (size_t)g.NGR * pr * 4);
   P->ws_bwd = o;
   return MOMENTS_OK;
 }
@@ -374,14 +379,33 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
                        (const float*)carry, dm2, dm1, Db, (T*)dx, (T*)db, (T*)dda, (T*)drot);
     MOM_TRY(check_launch());
   }
-  {
-    const int pr = g.p * g.r;
-    ProfScope ps(KID_DSCAN, st);
-    hipLaunchKernelGGL((k_dscan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, Db,
-                       (const float*)dec, (T*)dh0);
+  const int pr = g.p * g.r;
+  if (done) {
+    // the transposed kernel walked each group backward; add what enters at the group ends
+    float* gdb = (float*)(ws + P.gdb);
+    {
+      ProfScope ps(KID_GSCAN, st);
+      hipLaunchKernelGGL((k_gscan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g,
+                         (const float*)Db, (const float*)dec, gdb, (T*)dh0);
+      MOM_TRY(check_launch());
+    }
+    if (g.NGR > 1 && (dx != nullptr || db != nullptr || dda != nullptr)) {
+      const size_t lds = lds_fix(g, P.R, sizeof(T), P.PK).total;
+      MOM_TRY(set_lds(k_gfix<T, NT, CK>, lds));
+      ProfScope ps(KID_GFIX, st);
+      hipLaunchKernelGGL((k_gfix<T, NT, CK>), dim3(chains * (g.NGR - 1)), dim3(NTH), lds, st, g, P.PK, X, B, D,
+                         (const float*)carry, (const float*)dec, (const float*)gdb, (T*)dx, (T*)db, (T*)dda);
+      MOM_TRY(check_launch());
+    }
+  } else {
+    {
+      ProfScope ps(KID_DSCAN, st);
+      hipLaunchKernelGGL((k_dscan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, Db,
+                         (const float*)dec, (T*)dh0);
+    }
+    MOM_TRY(check_launch());
   }
-  MOM_TRY(check_launch());
-  if (g.NK >= 2 && (dx != nullptr || db != nullptr || dda != nullptr)) {
+  if (!done && g.NK >= 2 && (dx != nullptr || db != nullptr || dda != nullptr)) {
     const size_t lds = lds_fix(g, P.R, sizeof(T), P.PK).total;
     MOM_TRY(set_lds(k_fix<T, NT, CK>, lds));
     ProfScope ps(KID_FIX, st);

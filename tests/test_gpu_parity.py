@@ -67,6 +67,30 @@ def test_small_parity(rot_kind, dtype, kw):
     _log(f"[small] errors {errs}")
 
 
+# Enough chunks that a workgroup walks several of them (2 or more chunks per
+# group), with weak decay (the carry cotangent reaches back over whole groups)
+# and strong decay (it vanishes after a chunk or two).
+GROUPED = [
+    (W.ROT_PAIRWISE, dict(b=2, h=8, s=4224, valid_len=4200, c=2, p=8, r=32, rope_dim=16, da_mu=-6.0)),
+    (W.ROT_PAIRWISE, dict(b=2, h=8, s=4224, valid_len=4200, c=2, p=8, r=32, rope_dim=16, da_mu=2.5)),
+    (W.ROT_QUAT, dict(b=2, h=8, s=4224, valid_len=4224, c=1, p=12, r=32, quat_blocks=4, da_mu=1.5)),
+    (W.ROT_NONE, dict(b=3, h=6, s=4096, valid_len=4000, c=2, p=8, r=48, da_mu=1.0)),
+]
+
+
+@pytest.mark.parametrize("rot_kind,kw", GROUPED, ids=[f"{a}-{i}" for i, (a, _) in enumerate(GROUPED)])
+def test_grouped_walk_parity(rot_kind, kw):
+    base = dict(chunk_len=32, seed=21, angle_step=0.05, quat_sd=0.05)
+    base.update(kw)
+    w = W.small(f"grouped_{rot_kind}", dtype="bf16", rot_kind=rot_kind, **base)
+    t = W.generate(w, device="cpu")
+    _log(f"[grouped] {w}")
+    gpu = gpu_run(w, {k: (None if v is None else v.to(DEV)) for k, v in t.items()})
+    ref = oracle_run(w, t)
+    errs = compare(w, gpu, ref)
+    _log(f"[grouped] errors {errs}")
+
+
 @pytest.mark.parametrize("valid_len", [0, 1, 96, 500])
 def test_valid_len_edges(valid_len):
     w = _small(W.ROT_PAIRWISE, "f32", valid_len=valid_len)
