@@ -9,12 +9,15 @@
 // end) is added to G at the chunk's last token. Then
 //   D(n) = sum_t d_t G[t]            (the carry-cotangent recurrence, written
 //                                     to Db[n] for the next step of the walk)
-// and d_xhat, d_bhat, d_da and d_rot of the chunk follow from G. d_da is taken
-// in its direct form (differentiate a_t = cumsum da inside L and d):
-//   d_da_s = sum_{t>=s} ( d_t <G[t], h_-> + sum_{j<s} L[t,j] <G[t], W_j> ),
-// with <G[t], W_j> = sum_c sum_p xhat[j,c,p] Y_p[t,(j,c)]; unlike the
-// reverse-cumsum identity it has no cancellation between large terms when the
-// decay is strong. They are exact
+// and d_xhat, d_bhat, d_da and d_rot of the chunk follow from G. d_da: with
+// a_t = cumsum da inside L and d, and E[t][j] = L[t,j] <G[t], W_j> where
+// <G[t], W_j> = sum_c sum_p xhat[j,c,p] Y_p[t,(j,c)],
+//   d_da_s = sum_{t>=s} d_t <G[t], h_->  +  sum_{j<s<=t} E[t][j]
+//          = sum_{t>=s} d_t <G[t], h_->  +  sum_{s'<s} (C[s'] - Rw[s']),
+// C[j] = sum_t E[t][j] (column sums: sum_c sum_p xhat d_xhat) and Rw[t] =
+// sum_j E[t][j] (row sums). Both sums take the same E values, so the large
+// diagonal terms E[t][t], which the reverse-cumsum identity subtracts between
+// two differently rounded quantities, cancel up to fp32 rounding only. They are exact
 // except for the cotangent entering at the group's end, which the group fix-up
 // adds afterwards (k_gscan, k_gfix).
 //
@@ -93,13 +96,12 @@ struct LdsT {
   static constexpr size_t cst = lw + (size_t)(LWE + 2 * (K / 16)) * 64 * 16;  // carry, d_m1, D+ rows [3][4][R]
   static constexpr size_t dxp = cst + (size_t)3 * 4 * R * 4;                   // d_xhat partials [2][4][K]
   static constexpr size_t red = dxp + (size_t)2 * 4 * K * 4;
-  static constexpr size_t nred = (size_t)NWT * 4 * 16 + 4 * K + ELL;          // floats of red
-  // G transposes of the round's rows; at chunk end the d_bhat tile, the
-  // rotation-gradient reduction and the d_da partials reuse the space
+  static constexpr size_t nred = (size_t)NWT * 4 * 16 + NWT * 16 + 4 * K + ELL;  // floats of red
+  // G transposes of the round's rows; at chunk end the d_bhat tile and the
+  // rotation-gradient reduction reuse the space
   static constexpr size_t gs0 = (size_t)4 * R * GSP * 2;                       // G transposes
   static constexpr size_t gs1 = (size_t)K * SP * 2;                            // d_bhat tile
-  static constexpr size_t gs2 = (size_t)NWT * 16 * K * 4 + (size_t)ELL * ELL * 4;  // d_da partials
-  static constexpr size_t gsb = gs0 > gs1 ? (gs0 > gs2 ? gs0 : gs2) : (gs1 > gs2 ? gs1 : gs2);
+  static constexpr size_t gsb = gs0 > gs1 ? gs0 : gs1;
   static constexpr size_t Gs = red + nred * 4;
   static constexpr size_t rot = Gs + gsb;
   static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
@@ -334,9 +336,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
       for (int v = 0; v < NRC; v++) racc[ct][v] = 0.0f;
     float gcar = 0.0f;  // sum over this wave's rows and columns of G[t] h_- at token t
-    f4 Aacc[NKT];       // sum over this wave's rows of xhat[(j,c)][p] Y_p[t][(j,c)], t = 16tt+4q+i, (j,c) = 16kt+n
-#pragma unroll
-    for (int kt = 0; kt < NKT; kt++) Aacc[kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    f4 rwa = f4{0.0f, 0.0f, 0.0f, 0.0f};  // row sums of E at t = 16tt+4q+i, over this lane's (j,c) and rows
+    float cct = 0.0f;   // thread (rr, k) < 4K: sum over the rounds' rows rr of xhat * d_xhat
     const float dtl = s_d[t];
 
     for (int round = 0; round < nrounds; round++) {
@@ -445,6 +446,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           u4 GP;
 #pragma unroll
           for (int h2 = 0; h2 < 2; h2++) {
+            // keep each column tile's operand loads next to their use (bounds live registers)
+            __builtin_amdgcn_sched_barrier(0);
             const int ct = 2 * ky + h2;
             f4 d = *reinterpret_cast<const f4*>(dmrow + 16 * ct + 4 * q);
 #pragma unroll
@@ -524,12 +527,15 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) {
           const f4 ly = LYt[(tt * NKT + kt) * 64 + lane];
-          float v = ly[0] * Y[kt][0] + ly[1] * Y[kt][1] + ly[2] * Y[kt][2] + ly[3] * Y[kt][3];
+          const float xk = (float)xs[pl * KP + 16 * kt + n];
+          f4 e;
+#pragma unroll
+          for (int i = 0; i < 4; i++) e[i] = ly[i] * Y[kt][i];
+#pragma unroll
+          for (int i = 0; i < 4; i++) rwa[i] += xk * e[i];
+          float v = e[0] + e[1] + e[2] + e[3];
           v = col4_sum(v);
           if (q == 0) part[16 * kt + n] = v;
-          const float xk = (float)xs[pl * KP + 16 * kt + n];
-#pragma unroll
-          for (int i = 0; i < 4; i++) Aacc[kt][i] += xk * Y[kt][i];
         }
       };
       if (p < g.p) {
@@ -545,6 +551,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           const float v = dxp[rr * K + k] + dxp[(4 + rr) * K + k];
           const int pl = pp - pblk;
           dXs[pl * KP + k] = (bf16)v;
+          cct += v * (float)xs[pl * KP + k];
         }
       }
       // ---- d_bhat[(j,c)][col] += sum_t L[t,j] xhat[(j,c)][p] G[t][col]; local ----
@@ -644,44 +651,48 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
       }
     }
-    // ---- d_da, direct form ---------------------------------------------------------
-    __syncthreads();                      // G space free again
-    float* rg = red;                      // [w][q][16] partial G h_-
-    float* gct = red + NWT * 4 * 16;      // [t]
-    float* ddv = gct + ELL;               // [t]
-    float* Ap = (float*)Gs;               // [w][16 tokens][K] partial <G[t], W_(j,c)>
-    float* Am = Ap + NWT * 16 * K;        // [t][j]
+    // ---- d_da: sum_{t>=s} d_t <G[t], h_-> + sum_{s'<s} (C[s'] - Rw[s']) ------------
+    float* rg = red;                      // [w][q][16] partial <G[t], h_->
+    float* rwp = rg + NWT * 4 * 16;       // [w][16] partial row sums Rw
+    float* csum = rwp + NWT * 16;         // [rr][(j,c)] partial column sums
+    float* ddv = csum + 4 * K;            // [t]
     rg[(w * 4 + q) * 16 + n] = gcar;
 #pragma unroll
-    for (int kt = 0; kt < NKT; kt++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) Ap[(w * 16 + 4 * q + i) * K + 16 * kt + n] = Aacc[kt][i];
-    __syncthreads();
-    for (int idx = tid; idx < ELL * ELL; idx += NTT) {
-      const int tk = idx / ELL, j = idx % ELL;
-      const int half = tk >> 4;
-      float a = 0.0f;
-      for (int uu = 0; uu < 4; uu++)
-        for (int ci = 0; ci < g.c; ci++) a += Ap[((4 * half + uu) * 16 + (tk & 15)) * K + j * CK + ci];
-      Am[tk * ELL + j] = a;
+    for (int i = 0; i < 4; i++) {
+      const float r = row16_sum(rwa[i]);
+      if (n == 0) rwp[w * 16 + 4 * q + i] = r;
     }
-    if (tid < ELL) {
-      const int half = tid >> 4;
-      float a = 0.0f;
-      for (int uu = 0; uu < 4; uu++)
-        for (int qq = 0; qq < 4; qq++) a += rg[((4 * half + uu) * 4 + qq) * 16 + (tid & 15)];
-      gct[tid] = a;
-    }
+    if (tid < 4 * K) csum[tid] = cct;
     __syncthreads();
-    if (tid < ELL) {
-      const int sp = tid;
-      float a = 0.0f;
-      for (int tk = sp; tk < ELL; tk++) {
-        float b = s_d[tk] * gct[tk];
-        for (int j = 0; j < sp; j++) b += LT[j * LTP + tk] * Am[tk * ELL + j];
-        a += b;
+    if (tid < 64) {
+      // lane t < 32: x = d_t <G[t], h_->, y = C[t] - Rw[t]; then a suffix scan of x
+      // and an exclusive prefix scan of y across the lanes (fixed order)
+      const int tk = tid & 31, half = tk >> 4;
+      float x = 0.0f, y = 0.0f;
+      if (tid < ELL) {
+        float gt = 0.0f, rw = 0.0f, cj = 0.0f;
+        for (int uu = 0; uu < 4; uu++) {
+          for (int qq = 0; qq < 4; qq++) gt += rg[((4 * half + uu) * 4 + qq) * 16 + (tk & 15)];
+          rw += rwp[(4 * half + uu) * 16 + (tk & 15)];
+        }
+        for (int rr = 0; rr < 4; rr++)
+          for (int ci = 0; ci < g.c; ci++) cj += csum[rr * K + tk * CK + ci];
+        x = s_d[tk] * gt;
+        y = cj - rw;
       }
-      ddv[sp] = a;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float xd = __shfl_down(x, off, 32);
+        const float yu = __shfl_up(y, off, 32);
+        if (tk + off < 32) x += xd;
+        if (tk >= off) y += yu;
+      }
+      const float yex = __shfl_up(y, 1, 32);
+      if (tid < ELL) {
+        const float pre = tk > 0 ? yex : 0.0f;
+        // past valid_len every term vanishes; C - Rw cancels there only up to rounding
+        ddv[tk] = tk < tv ? x + pre : 0.0f;
+      }
     }
     __syncthreads();
     if (tid < ELL && d_da != nullptr) {
