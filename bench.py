@@ -26,34 +26,67 @@ PEAK_HBM_GBS = 8000.0
 
 
 def algorithmic(w):
-    """Algorithmic flops and bytes per launch of each kernel. The unit is one
-    (b, h, 32-token chunk); per unit (l = 32, K over the folded (j,c) axis only
-    on and below the diagonal):
-      states   c*p*r*l*(l+1)      m2, d_c  2*l*p*r^2 each      d_W  p*r*l*(l+1)
-      carry    2*l*c*p*r          d_xhat, d_bhat  2*l*c*p*r each
-    Bytes count each input read once and each output written once per launch
-    (workspace carries in fp32)."""
+    """Algorithmic flops and HBM bytes per launch of each kernel, counted as the
+    method's contractions over the causal triangle with the caller's chunk
+    length l (per token-head: states c*p*r*(l+1), m2 and d_c 2*p*r^2 each,
+    d_W and <G, W> p*r*(l+1) each). Bytes count every input read once and every
+    output written once; the fp32 carries are the implementation's own extra
+    (p*r*4 per 32-token kernel chunk, written by the carry pass and read back)."""
     V = min(w.valid_len, w.s)
-    nk = -(-V // ELL)
-    units = w.b * w.h * nk
-    p, r, c, l = w.p, w.r, w.c, ELL
+    th = w.b * V * w.h                         # token-heads
+    p, r, c, l = w.p, w.r, w.c, w.chunk_len
     e = 2 if w.dtype == "bf16" else 4
-    states = c * p * r * l * (l + 1)
-    gram = 2 * l * p * r * r
-    dw = p * r * l * (l + 1)
-    small = 2 * l * c * p * r
+    states = c * p * r * (l + 1)
+    gram = 2 * p * r * r
+    dw = p * r * (l + 1)
     rw = w.rot_width
-    in_tok = l * (c * p + c * r + 1 + rw) * e          # xhat, bhat, da, rot per unit
-    carry = p * r * 4
+    tok_in = (c * p + c * r + 1 + rw) * e          # xhat, bhat, da, rot per token-head
+    nk = -(-V // ELL)
+    carry_b = w.b * w.h * nk * p * r * 4          # one fp32 carry per kernel chunk
+    small = w.b * w.h * (2 * p * r + r * r) * 4   # h0 in, m2/m1 out or d_m2/d_m1 in, d_h0 out
+    fwd_b = th * tok_in + small
+    bwd_b = 2 * th * tok_in + small + w.b * w.h * p * r * e
     return {
-        "k_fwd": dict(flops=units * (states + gram), bytes=units * (in_tok + carry)),
-        "k_bwd": dict(flops=units * (states + gram + dw + 2 * small),
-                      bytes=units * (2 * in_tok + 2 * carry)),
-        "k_carry": dict(flops=units * small, bytes=units * (l * (c * p + c * r + 1) * e + carry)),
-        "k_fix": dict(flops=units * 2 * small, bytes=units * (3 * l * c * (p + r) * e + 2 * carry)),
-        "k_scan": dict(flops=0, bytes=units * 2 * carry),
-        "k_dscan": dict(flops=0, bytes=units * 2 * carry),
+        "k_fwd": dict(flops=th * (states + gram), bytes=fwd_b + carry_b),
+        "k_bwd": dict(flops=th * (states + gram + 2 * dw), bytes=bwd_b + 2 * carry_b),
+        "k_carry": dict(flops=th * 2 * c * p * r, bytes=th * (c * p + c * r + 1) * e + carry_b),
+        "k_scan": dict(flops=0, bytes=2 * carry_b),
+        "step": dict(flops=th * (2 * states + 2 * gram + 2 * dw), bytes=fwd_b + bwd_b),
     }
+
+
+def source_digest():
+    """Digest of the kernel sources: a stored traffic figure applies only to the
+    build it was measured on."""
+    import hashlib
+    d = hashlib.sha256()
+    src = os.path.join(ROOT, "mamba_ssm_chunkwise_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(src, name), "rb") as f:
+                d.update(name.encode() + b"\0" + f.read())
+    return d.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE + WRITE_SIZE, scaled
+    by a plain copy of known size), from profiles/<kernel>_<workload>.traffic.txt,
+    or None when absent or measured on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, seconds_hint=15.0):
@@ -96,6 +129,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_pairwise_b8_s8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run one plain device copy of 1 GiB (reads 1 GiB, writes "
+                         "1 GiB) so a counter run can calibrate HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -148,27 +184,45 @@ def main():
     value = tokens / (ms / 1e3)
 
     alg = algorithmic(w)
+    # per-kernel names as the library reports them (the transposed bf16 kernels
+    # report under the same names as the general ones)
     per_kernel = {k: (n, tot / max(n, 1)) for k, (n, tot) in prof.items() if n > 0}
     dom = max(per_kernel, key=lambda k: per_kernel[k][0] * per_kernel[k][1])
     avg_ms = per_kernel[dom][1]
     a = alg.get(dom, {"flops": 0, "bytes": 0})
+    kname = {"k_bwd": "k_bwdt", "k_fwd": "k_fwdt"}.get(dom, dom) if w.dtype == "bf16" and w.c <= 2 else dom
+    traffic = stored_traffic(kname, w.name)
     if a["flops"] > 0:
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
         achieved = a["flops"] / (avg_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kname,
                 "avg_ms": round(avg_ms, 4)}
     else:
         achieved = a["bytes"] / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dom,
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": kname,
                 "avg_ms": round(avg_ms, 4)}
+    # whole fwd+bwd step against its roofline time max(flops / MFMA peak, bytes / HBM peak)
+    st = alg["step"]
+    pk = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12
+    t_roof = max(st["flops"] / pk, st["bytes"] / (PEAK_HBM_GBS * 1e9))
+    step_roof = {"flops": st["flops"], "bytes": st["bytes"], "roofline_ms": round(t_roof * 1e3, 3),
+                 "frac": round(t_roof * 1e3 / ms, 4)}
     for k, (n, avg) in sorted(per_kernel.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
         fl = alg.get(k, {}).get("flops", 0)
         by = alg.get(k, {}).get("bytes", 0)
         print(f"[bench] {k:12s} launches {n:4d} avg {avg:9.4f} ms  "
               f"{fl / (avg / 1e3) / 1e12 if fl else 0:8.1f} TFLOP/s  {by / (avg / 1e3) / 1e9:8.1f} GB/s",
               file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        src_t = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        torch.add(src_t, 0.0, out=dst_t)   # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src_t, dst_t
 
     cpu = None
     if not args.no_cpu:
@@ -192,6 +246,7 @@ def main():
                    "p": w.p, "r": w.r, "chunk_len": w.chunk_len, "rot_kind": w.rot_kind,
                    "rope_dim": w.rope_dim, "quat_blocks": w.quat_blocks, "parallelism": "none"},
         "roofline": roof,
+        "step_roofline": step_roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
