@@ -90,10 +90,10 @@ def stored_traffic(kernel, workload):
 
 
 def cpu_baseline(w, seconds_hint=15.0):
-    """The oracle (as it stands) on a bounded sample: nthreads whole (b,h) chains
-    of the workload's shapes over the first T tokens, fwd + bwd, all host cores.
-    Workload tokens/s = (chains * T / h) / time (a token carries h chains)."""
-    import numpy as np
+    """The oracle (as it stands) on a bounded sample: whole (b,h) chains of the
+    workload's shapes over its valid length, fwd + bwd, all host cores; the number
+    of chains is a multiple of the thread count chosen for about seconds_hint of
+    work. Workload tokens/s = (chains * T / h) / time (a token carries h chains)."""
     import torch
 
     import workloads as W
@@ -101,10 +101,9 @@ def cpu_baseline(w, seconds_hint=15.0):
     from oracle.oracle import default_threads
 
     nt = default_threads()
-    nch = nt
-    T = min(w.valid_len, w.s, 4096)
-    # calibrate on a short prefix so the sample lands near seconds_hint
-    def run(Tn):
+    T = min(w.valid_len, w.s)
+
+    def run(nch, Tn):
         ws = w.replace(b=1, h=nch, s=Tn, valid_len=Tn, chunk_len=1, seed=w.seed + 17)
         t = {k: (None if v is None else v.double().numpy()) for k, v in W.generate(ws, device="cpu").items()}
         t0 = time.perf_counter()
@@ -112,14 +111,16 @@ def cpu_baseline(w, seconds_hint=15.0):
         oracle_bwd(t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], t["d_m2"], t["d_m1"], Tn, w.rot_kind,
                    w.rope_dim, nthreads=nt)
         return time.perf_counter() - t0
-    dt = run(64)
-    T = int(max(64, min(T, 64 * seconds_hint / max(dt, 1e-3))))
-    dt = run(T)
-    del np, torch
+    Tp = min(T, 256)
+    dt = run(nt, Tp)                                  # calibration on a short prefix
+    per_round = dt * T / Tp                           # nt chains of T tokens
+    k = int(max(1, min(64, round(seconds_hint / max(per_round, 1e-3)))))
+    nch = nt * k
+    dt = run(nch, T)
     rate = nch * T / w.h / dt
     return {"value": rate, "unit": "tokens/s", "cores": nt, "kind": "oracle",
             "sample": f"{nch} (b,h) chains x {T} tokens of {w.name} shapes (p={w.p}, r={w.r}, c={w.c}), "
-                      f"fwd+bwd fp64, {dt:.1f} s; tokens/s = chains*tokens/h/time"}
+                      f"fwd+bwd fp64 on {nt} threads, {dt:.1f} s; tokens/s = chains*tokens/h/time"}
 
 
 def main():
