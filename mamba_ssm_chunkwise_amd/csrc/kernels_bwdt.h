@@ -45,7 +45,6 @@ namespace mom {
 
 constexpr int NWT = 8;          // waves of k_bwdt
 constexpr int NTT = 64 * NWT;   // threads of k_bwdt
-constexpr int GSP = 40;         // G transpose: bf16 per state column (32 tokens + pad)
 constexpr int LTP = 36;         // row pitch of LT[j][t] (floats)
 constexpr int XPB = 32;         // state rows per staged xhat block
 
@@ -59,6 +58,28 @@ __host__ __device__ __forceinline__ int col_of_slot(int s) {
 __host__ __device__ __forceinline__ int slot_of_col(int c) {
   const int ks = c >> 5, h = (c >> 4) & 1, q = (c >> 2) & 3, e = c & 3;
   return 32 * ks + 8 * q + 4 * h + e;
+}
+
+// gfx950 transposing LDS read of four 16-bit values: within each group of 16
+// lanes, lane j receives element j % 4 of the 8-byte pieces addressed by lanes
+// 4r + j / 4 of its group, r = 0..3 in that order.
+typedef short s4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s4 lds_read_tr16(const bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)p);
+}
+
+// MFMA operand over the 32 tokens of a chunk from a [token][column] block of
+// pitch P (bf16): lane (q, n) gets state column 16ct + n at K-slots 8q+e =
+// tokens tslot(8q+e), i.e. 4q+e (e < 4) and 16+4q+e-4. Each of the two reads
+// covers four tokens; lane 4r+s of a group addresses token 4q+r (+16),
+// columns 16ct+4s.. . With P = R + 16 (R/2 + 8 dwords) the eight token rows a
+// half wave reads start 8 banks apart.
+template <int P>
+__device__ __forceinline__ bf8 ld_tok_frag(const bf16* blk, int ct, int lane) {
+  const bf16* p0 = blk + (4 * (lane >> 4) + ((lane >> 2) & 3)) * P + 4 * (lane & 3) + 16 * ct;
+  const s4 a = lds_read_tr16(p0), b = lds_read_tr16(p0 + 16 * P);
+  const s4 v[2] = {a, b};
+  return __builtin_bit_cast(bf8, v);
 }
 
 // Column tiles of 16 internal state columns that carry a rotation, rounded up
@@ -83,7 +104,7 @@ __host__ __device__ __forceinline__ int rot_tiles(const Geo& g) {
 constexpr int LWE = 4;
 template <int NT, int CK>
 struct LdsT {
-  static constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8;
+  static constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8, GTP = R + 16;
   static constexpr size_t Ss = 0;                                     // S rows, K-slot order
   static constexpr size_t bsT = Ss + (size_t)R * SP * 2;              // bhat^T [col][(j,c)]
   static constexpr size_t bsY = bsT + (size_t)R * KP * 2;             // bhat [(j,c)][col slot]
@@ -97,9 +118,9 @@ struct LdsT {
   static constexpr size_t dxp = cst + (size_t)3 * 4 * R * 4;                   // d_xhat partials [2][4][K]
   static constexpr size_t red = dxp + (size_t)2 * 4 * K * 4;
   static constexpr size_t nred = (size_t)NWT * 4 * 16 + NWT * 16 + 4 * K + ELL;  // floats of red
-  // G transposes of the round's rows; at chunk end the d_bhat tile and the
-  // rotation-gradient reduction reuse the space
-  static constexpr size_t gs0 = (size_t)4 * R * GSP * 2;                       // G transposes
+  // G of the round's rows, [row][token][column] (pitch GTP); at chunk end the
+  // d_bhat tile and the rotation-gradient reduction reuse the space
+  static constexpr size_t gs0 = (size_t)4 * ELL * GTP * 2;                     // G blocks
   static constexpr size_t gs1 = (size_t)K * SP * 2;                            // d_bhat tile
   static constexpr size_t gsb = gs0 > gs1 ? gs0 : gs1;
   static constexpr size_t Gs = red + nred * 4;
@@ -143,7 +164,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     Geo g, const bf16* __restrict__ xhat, const bf16* __restrict__ bhat, const bf16* __restrict__ da,
     const bf16* __restrict__ rot, const float* __restrict__ carry, const float* __restrict__ dm2,
     const float* __restrict__ dm1i, float* Db, bf16* d_xhat, bf16* d_bhat, bf16* d_da, bf16* d_rot) {
-  constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8;
+  constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8, GTP = R + 16;
   constexpr int NKT = K / 16;      // (j,c) tiles
   constexpr int KSR = NT / 2;      // K-steps over state columns
   constexpr int KW = NKT < 4 ? NKT : 4;  // d_bhat: waves along (j,c) tiles
@@ -440,7 +461,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         f4 Y[NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) Y[kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        unsigned short* Gw = reinterpret_cast<unsigned short*>(Gs) + (size_t)u * R * GSP + t;
+        bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * q;  // this lane's token row of G
 #pragma unroll
         for (int ky = 0; ky < KSR; ky++) {
           u4 GP;
@@ -513,13 +534,11 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             const bf8 b = ld_frag(bsY + (16 * kt + n) * SP + 32 * ky + 8 * q);
             Y[kt] = MM<bf16>::mma(as_bf8(GP), b, Y[kt]);
           }
-          // G^T into the row's transpose buffer, [col][t]
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const int col = 32 * ky + 16 * (e >> 2) + 4 * q + (e & 3);
-            const unsigned word = GP[e / 2];
-            Gw[col * GSP] = (unsigned short)(word & 0xffffu);
-            Gw[(col + 1) * GSP] = (unsigned short)(word >> 16);
+          // G into the row's block, [token][column]: columns 32ky+4q.. and 32ky+16+4q..
+          {
+            const unsigned lo[2] = {GP[0], GP[1]}, hi[2] = {GP[2], GP[3]};
+            *reinterpret_cast<unsigned long long*>(Gw + 32 * ky) = __builtin_bit_cast(unsigned long long, lo);
+            *reinterpret_cast<unsigned long long*>(Gw + 32 * ky + 16) = __builtin_bit_cast(unsigned long long, hi);
           }
         }
         // ---- this half's share of d_xhat[(j,c)][p] = sum_t L[t,j] Y[t][(j,c)] ----
@@ -555,46 +574,85 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
       }
       // ---- d_bhat[(j,c)][col] += sum_t L[t,j] xhat[(j,c)][p] G[t][col]; local ----
-      float LB[KH][8];  // L[8q+e][j of (j,c) = 16(kq*KH+kb)+n]
+      float LB[KH][8];  // L[tslot(8q+e)][j of (j,c) = 16(kq*KH+kb)+n]
 #pragma unroll
       for (int kb = 0; kb < KH; kb++) {
-        const float* src = LT + ((16 * (kq * KH + kb) + n) / CK) * LTP + 8 * q;
+        const float* src = LT + ((16 * (kq * KH + kb) + n) / CK) * LTP + 4 * q;
         const f4 l0 = *reinterpret_cast<const f4*>(src);
-        const f4 l1 = *reinterpret_cast<const f4*>(src + 4);
+        const f4 l1 = *reinterpret_cast<const f4*>(src + 16);
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           LB[kb][e] = l0[e];
           LB[kb][e + 4] = l1[e];
         }
       }
-      bf8 dA;  // A operand of local: row 0 = d_t over the K-slots t = 8q+e
+      bf8 dA;  // A operand of local: row 0 = d_t over the K-slots, t = tslot(8q+e)
 #pragma unroll
-      for (int e = 0; e < 8; e++) dA[e] = (bf16)(n == 0 ? s_d[8 * q + e] : 0.0f);
-#pragma unroll 1
-      for (int rr = 0; rr < 4; rr++) {
-        const int pp = pr0 + rr;
-        if (pp >= g.p) break;
-        const int pl = pp - pblk;
-        u4 Ab[KH];
+      for (int e = 0; e < 8; e++) dA[e] = (bf16)(n == 0 ? s_d[(e < 4 ? 4 * q + e : 16 + 4 * q + e - 4)] : 0.0f);
+      if (pr0 + 4 <= g.p) {
+        // all four rows present: every G^T fragment of the round is loaded up
+        // front, so one LDS latency covers the whole phase
+        bf8 gbf[4][CH];
 #pragma unroll
-        for (int kb = 0; kb < KH; kb++) {
-          const float xk = (float)xs[pl * KP + 16 * (kq * KH + kb) + n];
+        for (int rr = 0; rr < 4; rr++)
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) Ab[kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
-        }
-        const bf16* Gr = Gs + (size_t)rr * R * GSP;
-        float* dbrow = Db + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r;
-        const bool do_local = kq == (rr % KW);  // each (row, column tile) once
+          for (int cb = 0; cb < CH; cb++)
+            gbf[rr][cb] = ld_tok_frag<GTP>(Gs + (size_t)rr * ELL * GTP, cq * CH + cb, lane);
+        u4 Ab[4][KH];
 #pragma unroll
-        for (int cb = 0; cb < CH; cb++) {
-          const int ct = cq * CH + cb;
-          const bf8 gb = ld_frag(Gr + (16 * ct + n) * GSP + 8 * q);
+        for (int rr = 0; rr < 4; rr++)
 #pragma unroll
-          for (int kb = 0; kb < KH; kb++) dbacc[kb][cb] = MM<bf16>::mma(as_bf8(Ab[kb]), gb, dbacc[kb][cb]);
-          if (do_local) {
-            const f4 lo = MM<bf16>::mma(dA, gb, f4{0.0f, 0.0f, 0.0f, 0.0f});
-            const int col = 16 * ct + n;
+          for (int kb = 0; kb < KH; kb++) {
+            const float xk = (float)xs[(pr0 + rr - pblk) * KP + 16 * (kq * KH + kb) + n];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) Ab[rr][kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
+          }
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+          for (int cb = 0; cb < CH; cb++)
+#pragma unroll
+            for (int kb = 0; kb < KH; kb++)
+              dbacc[kb][cb] = MM<bf16>::mma(as_bf8(Ab[rr][kb]), gbf[rr][cb], dbacc[kb][cb]);
+        // local of the rows rr with rr % KW == kq (each (row, column tile) once)
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+          if (rr % KW != kq) continue;
+          float* dbrow = Db + (((size_t)bh * g.NK + nc) * g.p + pr0 + rr) * g.r;
+#pragma unroll
+          for (int cb = 0; cb < CH; cb++) {
+            const f4 lo = MM<bf16>::mma(dA, gbf[rr][cb], f4{0.0f, 0.0f, 0.0f, 0.0f});
+            const int col = 16 * (cq * CH + cb) + n;
             if (q == 0 && col < g.r) dbrow[col] = lo[0];
+          }
+        }
+      } else {
+#pragma unroll 1
+        for (int rr = 0; rr < 4; rr++) {
+          const int pp = pr0 + rr;
+          if (pp >= g.p) break;
+          const int pl = pp - pblk;
+          u4 Ab[KH];
+#pragma unroll
+          for (int kb = 0; kb < KH; kb++) {
+            const float xk = (float)xs[pl * KP + 16 * (kq * KH + kb) + n];
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) Ab[kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
+          }
+          const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
+          float* dbrow = Db + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r;
+          const bool do_local = kq == (rr % KW);  // each (row, column tile) once
+#pragma unroll
+          for (int cb = 0; cb < CH; cb++) {
+            const int ct = cq * CH + cb;
+            const bf8 gb = ld_tok_frag<GTP>(Gr, ct, lane);
+#pragma unroll
+            for (int kb = 0; kb < KH; kb++) dbacc[kb][cb] = MM<bf16>::mma(as_bf8(Ab[kb]), gb, dbacc[kb][cb]);
+            if (do_local) {
+              const f4 lo = MM<bf16>::mma(dA, gb, f4{0.0f, 0.0f, 0.0f, 0.0f});
+              const int col = 16 * ct + n;
+              if (q == 0 && col < g.r) dbrow[col] = lo[0];
+            }
           }
         }
       }

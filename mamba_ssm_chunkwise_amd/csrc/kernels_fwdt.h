@@ -20,7 +20,7 @@ namespace mom {
 
 template <int NT, int CK>
 struct LdsF {
-  static constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8;
+  static constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8, GTP = R + 16;
   static constexpr size_t bsT = 0;                                    // bhat^T [col][(j,c)]
   static constexpr size_t xs = bsT + (size_t)R * KP * 2;              // xhat block [p][(j,c)]
   static constexpr size_t LT = xs + (size_t)XPB * KP * 2;             // L^T [j][t]
@@ -28,8 +28,8 @@ struct LdsF {
   static constexpr size_t d = a + ELL * 4;
   static constexpr size_t lw = d + ELL * 4;                           // W factors [LWE][64] float4
   static constexpr size_t cst = lw + (size_t)LWE * 64 * 16;           // carry rows of the round [4][R]
-  static constexpr size_t Gs = cst + (size_t)4 * R * 4;               // c transposes [4][R][GSP]
-  static constexpr size_t rot = Gs + (size_t)4 * R * GSP * 2;
+  static constexpr size_t Gs = cst + (size_t)4 * R * 4;               // c blocks [4][token][column]
+  static constexpr size_t rot = Gs + (size_t)4 * ELL * GTP * 2;
   static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
   // m1 table [p][R] fp32 after the rotation table (RT rotated tiles)
   __host__ __device__ static size_t m1s(int RT) { return rot + (size_t)ELL * (16 * RT + 4) * 4; }
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
                                                   const bf16* __restrict__ bhat, const bf16* __restrict__ da,
                                                   const bf16* __restrict__ rot, const float* __restrict__ carry,
                                                   float* m2part, float* m1part) {
-  constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8;
+  constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8, GTP = R + 16;
   constexpr int RTP = 16 * RT + 4;
   constexpr int MA = NT / 4, MB = NT / 2;  // m2 tiles per wave: MA row tiles x MB column tiles
   static_assert((ROT == 0) == (RT == 0) && RT <= NT && NT % 4 == 0, "tiling");
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
         }
         // ---- carry, de-rotation, c^T into the row's transpose buffer --------------
         const float* hrow = cst + u * R;
-        unsigned short* Gw = reinterpret_cast<unsigned short*>(Gs) + (size_t)u * R * GSP + t;
+        bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * q;  // this lane's token row of c
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
           const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
@@ -256,11 +256,8 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
           }
           const unsigned w0 = live ? pk_bf16(c[0], c[1]) : 0u;
           const unsigned w1 = live ? pk_bf16(c[2], c[3]) : 0u;
-          const int col = 16 * ct + 4 * q;
-          Gw[col * GSP] = (unsigned short)(w0 & 0xffffu);
-          Gw[(col + 1) * GSP] = (unsigned short)(w0 >> 16);
-          Gw[(col + 2) * GSP] = (unsigned short)(w1 & 0xffffu);
-          Gw[(col + 3) * GSP] = (unsigned short)(w1 >> 16);
+          const unsigned pr[2] = {w0, w1};  // columns 16ct+4q..
+          *reinterpret_cast<unsigned long long*>(Gw + 16 * ct) = __builtin_bit_cast(unsigned long long, pr);
         }
       }
       __syncthreads();  // the round's c transposes are complete
@@ -269,12 +266,12 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
       for (int rr = 0; rr < 4; rr++) {
         const int pp = pr0 + rr;
         if (pp >= g.p) break;
-        const bf16* Gr = Gs + (size_t)rr * R * GSP;
+        const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
         bf8 fa[MA], fb[MB];
 #pragma unroll
-        for (int a = 0; a < MA; a++) fa[a] = ld_frag(Gr + (16 * (ta0 + a) + n) * GSP + 8 * q);
+        for (int a = 0; a < MA; a++) fa[a] = ld_tok_frag<GTP>(Gr, ta0 + a, lane);
 #pragma unroll
-        for (int b = 0; b < MB; b++) fb[b] = ld_frag(Gr + (16 * (tb0 + b) + n) * GSP + 8 * q);
+        for (int b = 0; b < MB; b++) fb[b] = ld_tok_frag<GTP>(Gr, tb0 + b, lane);
 #pragma unroll
         for (int a = 0; a < MA; a++)
 #pragma unroll
