@@ -51,6 +51,8 @@ def algorithmic(w):
         "k_bwd": dict(flops=th * (states + gram + 2 * dw), bytes=bwd_b + 2 * carry_b),
         "k_carry": dict(flops=th * 2 * c * p * r, bytes=th * (c * p + c * r + 1) * e + carry_b),
         "k_scan": dict(flops=0, bytes=2 * carry_b),
+        # one sequential walk per chain: inputs read once, carries written once
+        "k_cscan": dict(flops=th * 2 * c * p * r, bytes=th * (c * p + c * r + 1) * e + carry_b),
         "step": dict(flops=th * (2 * states + 2 * gram + 2 * dw), bytes=fwd_b + bwd_b),
     }
 

@@ -1,0 +1,222 @@
+// Boundary carries in one pass per (b,h) chain (bf16 inputs).
+//
+// Source: burn-mamba "backward.rs" source page, boundary_carries: the state
+// entering chunk n is h_-(0) = h0 and h_-(n+1) = dec_n h_-(n) + U_n, where
+// dec_n = exp(a_last) and U_n[p][col] = sum_{(j,c)} exp(a_last - a_j)
+// xhat[j,c,p] bhat[j,c,col] is the chunk's decay-to-chunk-end product.
+//
+// One workgroup walks one chain from the first chunk to the last. The state
+// rows stay in MFMA accumulators for the whole walk (wave w owns row tiles
+// w, w+4): per chunk the wave stores h_-(n), scales by dec_n and accumulates
+// U_n on MFMA. Each chunk's xhat and bhat are fetched one chunk ahead into
+// registers and stored to LDS in their global layouts ([(j,c)][p] and
+// [(j,c)][col]); transposing LDS reads build both MFMA operands from there.
+// The states are kept in the caller's column order and written to the
+// internal order on store.
+#pragma once
+
+#include "kernels_bwdt.h"
+
+namespace mom {
+
+constexpr int CSW = 4;           // waves of k_cscan
+constexpr int CST = 64 * CSW;    // threads of k_cscan
+constexpr int CMT = 2;           // row tiles per wave at most (state rows <= 128)
+
+// Row pitch (bf16) of a staged [(j,c)][row] block with PK rows: the eight rows
+// a half wave reads in one transposing read start 8 banks apart.
+__host__ __device__ __forceinline__ int cscan_xp(int PK) { return PK + (((PK >> 4) & 1) ? 32 : 16); }
+
+template <int NT, int CK>
+struct LdsC {
+  static constexpr int R = 16 * NT, K = ELL * CK, BP = R + 16;
+  __host__ __device__ static size_t xs(int) { return 0; }                                  // [2][K][XP]
+  __host__ __device__ static size_t bs(int PK) { return (size_t)2 * K * cscan_xp(PK) * 2; }  // [2][K][BP]
+  __host__ __device__ static size_t wv(int PK) { return bs(PK) + (size_t)2 * K * BP * 2; }  // [2][ELL+1]
+  __host__ __device__ static size_t total(int PK) { return wv(PK) + (size_t)2 * (ELL + 4) * 4; }
+};
+
+// Operand over K-step ks of a [(j,c)][x] block (pitch P): lane (q, m) gets x =
+// x0 + m at K-slots 8q+e, which hold (j,c) = 32ks + 4q + e (e < 4) and
+// 32ks + 16 + 4q + e - 4. Lane 4r+s of a group addresses (j,c) 32ks+4q+r
+// (+16), x0 + 4s.
+__device__ __forceinline__ bf8 ld_kx_frag(const bf16* blk, int P, int ks, int x0, int lane) {
+  const bf16* p0 = blk + (32 * ks + 4 * (lane >> 4) + ((lane >> 2) & 3)) * P + x0 + 4 * (lane & 3);
+  const s4 a = lds_read_tr16(p0), b = lds_read_tr16(p0 + 16 * P);
+  const s4 v[2] = {a, b};
+  return __builtin_bit_cast(bf8, v);
+}
+
+// MTW: row tiles per wave (1: state rows <= 64, 2: <= 128).
+template <int NT, int CK, int MTW>
+__global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __restrict__ xhat,
+                                               const bf16* __restrict__ bhat, const bf16* __restrict__ da,
+                                               const bf16* __restrict__ h0, float* carry, float* dec) {
+  constexpr int R = 16 * NT, K = ELL * CK, BP = R + 16, NKS = K / 32;
+  constexpr int XPT = K * 16 / CST;      // xhat pieces (8 rows) per thread, rows <= 128
+  constexpr int BPT = K * R / 8 / CST;   // bhat pieces (8 columns) per thread
+  static_assert(XPT >= 1 && BPT >= 1, "tiling");
+  using L = LdsC<NT, CK>;
+  const int XP = cscan_xp(PK);
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* xs = (bf16*)(smem + L::xs(PK));
+  bf16* bs = (bf16*)(smem + L::bs(PK));
+  float* wv = (float*)(smem + L::wv(PK));  // per buffer: exp(a_last - a_j), j < ELL; then dec
+
+  const int bh = blockIdx.x, bi = bh / g.h, hi = bh % g.h;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, q = lane >> 4;
+  const int MT = PK / 16;
+  const int xpr = PK / 8;  // xhat pieces per (j,c)
+  const size_t pr = (size_t)g.p * g.r;
+
+  struct Pf {
+    u4 x[XPT];
+    u4 b[BPT];
+    float d;
+  };
+  auto fetch = [&](int nc) -> Pf {
+    Pf f;
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+      f.x[i] = u4{0u, 0u, 0u, 0u};
+      const int idx = tid + i * CST;
+      const int k = idx / xpr, p0 = 8 * (idx % xpr);
+      const int j = k / CK, ci = k % CK, pos = nc * ELL + j;
+      if (k < K && p0 < g.p && ci < g.c && pos < g.V) {
+        const bf16* src = xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + p0;
+        if ((g.p & 7) == 0) {
+          f.x[i] = *reinterpret_cast<const u4*>(src);
+        } else {
+          unsigned short v[8];
+#pragma unroll
+          for (int e = 0; e < 8; e++) v[e] = p0 + e < g.p ? __builtin_bit_cast(unsigned short, src[e]) : 0;
+          f.x[i] = __builtin_bit_cast(u4, v);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; i++) {
+      f.b[i] = u4{0u, 0u, 0u, 0u};
+      const int idx = tid + i * CST;
+      const int k = idx / (R / 8), c0 = 8 * (idx % (R / 8));
+      const int j = k / CK, ci = k % CK, pos = nc * ELL + j;
+      if (c0 < g.r && ci < g.c && pos < g.V) {
+        const bf16* src = bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + c0;
+        if ((g.r & 7) == 0) {
+          f.b[i] = *reinterpret_cast<const u4*>(src);
+        } else {
+          unsigned short v[8];
+#pragma unroll
+          for (int e = 0; e < 8; e++) v[e] = c0 + e < g.r ? __builtin_bit_cast(unsigned short, src[e]) : 0;
+          f.b[i] = __builtin_bit_cast(u4, v);
+        }
+      }
+    }
+    f.d = 0.0f;
+    if (tid < ELL && nc * ELL + tid < g.V) f.d = (float)da[((size_t)bi * g.s + nc * ELL + tid) * g.h + hi];
+    return f;
+  };
+  auto store = [&](const Pf& f, int buf) {
+    bf16* xb = xs + (size_t)buf * K * XP;
+    bf16* bb = bs + (size_t)buf * K * BP;
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+      const int idx = tid + i * CST;
+      const int k = idx / xpr, p0 = 8 * (idx % xpr);
+      if (k < K) *reinterpret_cast<u4*>(xb + k * XP + p0) = f.x[i];
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; i++) {
+      const int idx = tid + i * CST;
+      const int k = idx / (R / 8), c0 = 8 * (idx % (R / 8));
+      *reinterpret_cast<u4*>(bb + k * BP + c0) = f.b[i];
+    }
+    if (tid < 64) {  // a_j = cumsum of da over the chunk; weights exp(a_last - a_j), dec = exp(a_last)
+      float a = f.d;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const float up = __shfl_up(a, off, 32);
+        if ((tid & 31) >= off) a += up;
+      }
+      const float al = __shfl(a, 31, 32);
+      if (tid < ELL) wv[buf * (ELL + 4) + tid] = expf(al - a);
+      if (tid == 0) wv[buf * (ELL + 4) + ELL] = expf(al);
+    }
+  };
+
+  // h_-(0) = h0, caller's column order
+  static_assert(MTW >= 1 && MTW <= CMT, "row tiles per wave");
+  f4 acc[MTW][NT];
+#pragma unroll
+  for (int mi = 0; mi < MTW; mi++)
+#pragma unroll
+    for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int row = 16 * (w + CSW * mi) + 4 * q + i, col = 16 * nt + m;
+        acc[mi][nt][i] = (h0 != nullptr && row < g.p && col < g.r)
+                             ? (float)h0[((size_t)bh * g.p + row) * g.r + col] : 0.0f;
+      }
+  // internal position of this lane's columns (half-split interleaves the halves)
+  int icol[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; nt++) icol[nt] = 16 * nt + m < g.r ? inv_perm_rc(g, 16 * nt + m) : 0;
+
+  if (g.NK > 1) store(fetch(0), 0);
+  __syncthreads();
+  for (int nc = 0; nc < g.NK; nc++) {
+    const bool more = nc + 2 < g.NK;  // chunk nc+1 contributes U only if it is not the last
+    Pf pf;
+    if (more) pf = fetch(nc + 1);
+    float* out = carry + ((size_t)bh * g.NK + nc) * pr;
+#pragma unroll
+    for (int mi = 0; mi < MTW; mi++) {
+      const int mt = w + CSW * mi;
+      if (mt >= MT) break;
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        if (16 * nt + m >= g.r) continue;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int row = 16 * mt + 4 * q + i;
+          if (row < g.p) out[(size_t)row * g.r + icol[nt]] = acc[mi][nt][i];
+        }
+      }
+    }
+    if (nc + 1 < g.NK) {
+      const int b = nc & 1;
+      const float* wb = wv + b * (ELL + 4);
+      const float dn = wb[ELL];
+      if (tid == 0) dec[(size_t)bh * g.NK + nc] = dn;
+      const bf16* xb = xs + (size_t)b * K * XP;
+      const bf16* bb = bs + (size_t)b * K * BP;
+#pragma unroll
+      for (int mi = 0; mi < MTW; mi++) {
+        const int mt = w + CSW * mi;
+        if (mt >= MT) break;
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) acc[mi][nt][i] *= dn;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++) {
+          // A: rows of this tile, K-slot e weighted by exp(a_last - a_j) of its (j,c)
+          const bf8 xr = ld_kx_frag(xb, XP, ks, 16 * mt, lane);
+          bf8 a;
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const int k = 32 * ks + (e < 4 ? 4 * q + e : 16 + 4 * q + e - 4);
+            a[e] = (bf16)(wb[k / CK] * (float)xr[e]);
+          }
+#pragma unroll
+          for (int nt = 0; nt < NT; nt++)
+            acc[mi][nt] = MM<bf16>::mma(a, ld_kx_frag(bb, BP, ks, 16 * nt, lane), acc[mi][nt]);
+        }
+      }
+    }
+    if (more) store(pf, (nc + 1) & 1);
+    __syncthreads();
+  }
+}
+
+}  // namespace mom

@@ -12,6 +12,7 @@
 #include "kernels_bwd.h"
 #include "kernels_bwdt.h"
 #include "kernels_fwdt.h"
+#include "kernels_cscan.h"
 
 using namespace mom;
 
@@ -24,10 +25,11 @@ constexpr size_t kLdsLimit = 160 * 1024;
 // ---- optional per-kernel event timing (moments_profile_*) -------------------
 enum KernelId {
   KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_PREP, KID_GSCAN, KID_GFIX,
-  KID_N
+  KID_CSCAN, KID_N
 };
 const char* const kKernelNames[KID_N] = {"k_carry", "k_scan",      "k_fwd",      "k_reduce", "k_bwd",  "k_dscan",
-                                         "k_fix",   "k_zero_tail", "k_prep_dm1", "k_gscan",  "k_gfix"};
+                                         "k_fix",   "k_zero_tail", "k_prep_dm1", "k_gscan",  "k_gfix",
+                                         "k_cscan"};
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -244,6 +246,22 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   float* carry = (float*)(ws + P.carry);
   float* dec = (float*)(ws + P.dec);
   const int chains = g.b * g.h;
+  if constexpr (std::is_same<T, bf16>::value) {
+    // one sequential walk per chain when there are enough chains to fill the
+    // chip (or the chains are short); otherwise the chunk-parallel pair below
+    const size_t lds = LdsC<NT, CK>::total(P.PK);
+    if (g.NK >= 1 && P.PK <= 16 * CSW * CMT && lds <= kLdsLimit && (chains >= 64 || g.NK <= 32)) {
+      auto launch = [&](auto mtw_c) -> int {
+        constexpr int MTW = decltype(mtw_c)::value;
+        MOM_TRY(set_lds(k_cscan<NT, CK, MTW>, lds));
+        ProfScope ps(KID_CSCAN, st);
+        hipLaunchKernelGGL((k_cscan<NT, CK, MTW>), dim3(chains), dim3(CST), lds, st, g, P.PK, xhat, bhat, da, h0,
+                           carry, dec);
+        return check_launch();
+      };
+      return P.PK <= 16 * CSW ? launch(IC<1>{}) : launch(IC<2>{});
+    }
+  }
   if (g.NK >= 2) {
     const size_t lds = lds_carry(g, P.R, sizeof(T), P.PK).total;
     MOM_TRY(set_lds(k_carry<T, NT, CK>, lds));
