@@ -174,7 +174,10 @@ int make_plan(const moments_desc* d, Plan* P) {
   g.cinv = (65536 + g.c - 1) / g.c;
   const int64_t chains = (int64_t)g.b * g.h;
   const int64_t total = chains * g.NK;
-  int G = (int)((total + 2047) / 2048);
+  // chunks per workgroup of the main kernels: about 512 workgroups (two per
+  // CU at one resident workgroup each), fewer groups meaning fewer partial
+  // moments and group fix-ups
+  int G = (int)((total + 511) / 512);
   if (G < 1) G = 1;
   if (g.NK > 0 && G > g.NK) G = g.NK;
   g.G = G;
