@@ -34,13 +34,15 @@ struct LdsF {
   // m1 table [p][R] fp32 after the rotation table (RT rotated tiles)
   __host__ __device__ static size_t m1s(int RT) { return rot + (size_t)ELL * (16 * RT + 4) * 4; }
   __host__ __device__ static size_t total(int RT, int p) { return m1s(RT) + (size_t)p * R * 4; }
+  // with the state rows carried in LDS across the chain: [p][R] fp32 after the m1 table
+  __host__ __device__ static size_t total_inc(int RT, int p) { return total(RT, p) + (size_t)p * R * 4; }
 };
 
 template <int NT, int ROT, int CK, int RT>
 __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__ xhat,
                                                   const bf16* __restrict__ bhat, const bf16* __restrict__ da,
                                                   const bf16* __restrict__ rot, const float* __restrict__ carry,
-                                                  float* m2part, float* m1part) {
+                                                  const bf16* __restrict__ h0, float* m2part, float* m1part) {
   constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8, GTP = R + 16;
   constexpr int RTP = 16 * RT + 4;
   constexpr int MA = NT / 4, MB = NT / 2;  // m2 tiles per wave: MA row tiles x MB column tiles
@@ -67,6 +69,17 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   const int ta0 = MA * (w >> 1), tb0 = MB * (w & 1);  // this wave's m2 tiles
 
   for (int idx = tid; idx < g.p * R; idx += NTT) m1s[idx] = 0.0f;
+  // carry == nullptr: one group per chain, and the state entering each chunk is
+  // carried in LDS: the rows start at h0 and the lanes holding the chunk's last
+  // token replace them with the state there, h_-(n+1) = h_{n, last}
+  const bool inc = carry == nullptr;
+  float* carryL = (float*)(smem + L::total(RT, g.p));  // [p][R]
+  if (inc) {
+    for (int idx = tid; idx < g.p * R; idx += NTT) {
+      const int pp = idx / R, col = idx % R;
+      carryL[idx] = (h0 != nullptr && col < g.r) ? (float)h0[((size_t)bh * g.p + pp) * g.r + perm_rc(g, col)] : 0.0f;
+    }
+  }
 
   auto stage_x = [&](int nc, int pblk) {
     for (int idx = tid; idx < K * XPB; idx += NTT) {
@@ -85,7 +98,9 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
     if (tid < R) {
       const int rr = tid / (R / 4), col = 4 * (tid % (R / 4));
       const int pp = pr0 + rr;
-      if (pp < g.p) v = load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col);
+      if (pp < g.p)
+        v = inc ? *reinterpret_cast<const f4*>(carryL + (size_t)pp * R + col)
+                : load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col);
     }
     return v;
   };
@@ -230,12 +245,14 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
         // ---- carry, de-rotation, c^T into the row's transpose buffer --------------
         const float* hrow = cst + u * R;
         bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * q;  // this lane's token row of c
+        f4 hl[NT];  // the state row at this lane's token (kept for the last token's carry)
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
           const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
           f4 h;
 #pragma unroll
           for (int i = 0; i < 4; i++) h[i] = hT[ct][i] + dtl * hv[i];
+          hl[ct] = h;
           f4 c = h;
           if constexpr (ROT == 1) {
             if (ct < RT) {
@@ -258,6 +275,10 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
           const unsigned w1 = live ? pk_bf16(c[2], c[3]) : 0u;
           const unsigned pr[2] = {w0, w1};  // columns 16ct+4q..
           *reinterpret_cast<unsigned long long*>(Gw + 16 * ct) = __builtin_bit_cast(unsigned long long, pr);
+        }
+        if (inc && t == ELL - 1) {
+#pragma unroll
+          for (int ct = 0; ct < NT; ct++) *reinterpret_cast<f4*>(carryL + (size_t)p * R + 16 * ct + 4 * q) = hl[ct];
         }
       }
       __syncthreads();  // the round's c transposes are complete

@@ -86,6 +86,7 @@ struct Plan {
   int PK;       // state rows padded for MFMA K over rows
   bool bwdt;    // backward main kernel in the transposed layout (bf16, c <= 2)
   bool fwdt;    // forward main kernel in the transposed layout (bf16, c <= 2)
+  bool fwdt_inc;  // ... carrying the state rows itself (one group per chain): no carry pass
   size_t carry, dec, m2p, m1p, db, dm1i, gdb;  // workspace offsets
   size_t ws_fwd, ws_bwd;
 };
@@ -200,8 +201,10 @@ int make_plan(const moments_desc* d, Plan* P) {
   if (bf && P->CK <= 2) {
     const size_t lf = fwdt_lds(g, P->NT, P->CK);
     P->fwdt = lf > 0 && lf <= kLdsLimit;
+    P->fwdt_inc = P->fwdt && g.NGR == 1 && lf + (size_t)g.p * P->R * 4 <= kLdsLimit;
   } else {
     P->fwdt = false;
+    P->fwdt_inc = false;
   }
   if (bf && P->CK <= 2) {
     const size_t lb = bwdt_lds(g, P->NT, P->CK);
@@ -291,7 +294,7 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   const T* B = (const T*)bhat;
   const T* D = (const T*)da;
   const T* Rt = (const T*)rot;
-  MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
+  if (!P.fwdt_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
   float* m2p = (float*)(ws + P.m2p);
   float* m1p = (float*)(ws + P.m1p);
   const int chains = g.b * g.h;
@@ -301,11 +304,11 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
       const int RT = rot_tiles(g);
       auto launch = [&](auto rot_c, auto rt_c) -> int {
         constexpr int RO = decltype(rot_c)::value, RTc = decltype(rt_c)::value;
-        const size_t lds = LdsF<NT, CK>::total(RTc, g.p);
+        const size_t lds = P.fwdt_inc ? LdsF<NT, CK>::total_inc(RTc, g.p) : LdsF<NT, CK>::total(RTc, g.p);
         MOM_TRY(set_lds(k_fwdt<NT, RO, CK, RTc>, lds));
         ProfScope ps(KID_FWD, st);
         hipLaunchKernelGGL((k_fwdt<NT, RO, CK, RTc>), dim3(chains * g.NGR), dim3(NTT), lds, st, g, X, B, D, Rt,
-                           (const float*)(ws + P.carry), m2p, m1p);
+                           P.fwdt_inc ? nullptr : (const float*)(ws + P.carry), (const T*)h0, m2p, m1p);
         return check_launch();
       };
       int rc = MOMENTS_ENOTSUP;

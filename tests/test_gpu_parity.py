@@ -75,6 +75,9 @@ GROUPED = [
     (W.ROT_PAIRWISE, dict(b=2, h=8, s=4224, valid_len=4200, c=2, p=8, r=32, rope_dim=16, da_mu=2.5)),
     (W.ROT_QUAT, dict(b=2, h=8, s=4224, valid_len=4224, c=1, p=12, r=32, quat_blocks=4, da_mu=1.5)),
     (W.ROT_NONE, dict(b=3, h=6, s=4096, valid_len=4000, c=2, p=8, r=48, da_mu=1.0)),
+    # 512 chains: one group per chain (the forward carries its state rows itself)
+    (W.ROT_PAIRWISE, dict(b=8, h=64, s=256, valid_len=250, c=2, p=16, r=64, rope_dim=32, da_mu=-1.0)),
+    (W.ROT_HALF, dict(b=8, h=64, s=256, valid_len=256, c=1, p=20, r=64, rope_dim=64, da_mu=0.5)),
 ]
 
 
