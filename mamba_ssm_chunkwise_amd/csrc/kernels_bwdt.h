@@ -196,7 +196,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform in the wave
+  const int lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int u = w & 3, tt = w >> 2;       // row slot of the round, token half
   const int t = 16 * tt + n;              // this lane's token in the transposed tiles
   const int kq = w / CW, cq = w % CW;     // d_bhat block of this wave

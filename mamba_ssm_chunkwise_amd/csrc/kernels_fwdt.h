@@ -63,7 +63,8 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, n = lane & 15, q = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform in the wave
+  const int lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int u = w & 3, tt = w >> 2;
   const int t = 16 * tt + n;
   const int ta0 = MA * (w >> 1), tb0 = MB * (w & 1);  // this wave's m2 tiles
