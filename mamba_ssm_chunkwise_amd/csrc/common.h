@@ -118,11 +118,15 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp<DPP_ROW_MIRROR>(v);
   return v;
 }
-// Sum over the four lane groups (lanes sharing l%16).
+// Sum over the four lane groups (lanes sharing l%16), in registers: the
+// gfx950 permlane swaps pair each 16-lane row with its neighbour (l ^ 16), then
+// each half wave with the other (l ^ 32); both halves of a swap add the same
+// two values, so every lane ends with the same sum.
 __device__ __forceinline__ float col4_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Order LDS traffic between lanes of one wave without a workgroup barrier.

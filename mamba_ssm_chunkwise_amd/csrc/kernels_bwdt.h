@@ -146,7 +146,8 @@ __global__ __launch_bounds__(NTH) void k_prep_dm1(Geo g, int R, const float* __r
 }
 
 // Four consecutive internal columns 4q.. of a state row (zero past r).
-__device__ __forceinline__ f4 load_cols4(const float* row, int r, int col) {
+__device__ __forceinline__ f4 load_cols4(const float* row, int r, int col, int R) {
+  if (r == R) return *reinterpret_cast<const f4*>(row + col);  // every column present
   if ((r & 3) == 0) {
     if (col < r) return *reinterpret_cast<const f4*>(row + col);
     return f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -245,16 +246,17 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   // critical path. D(n+1) was written by this workgroup one chunk earlier.
   constexpr int CQ = 3 * 4 * R / 4;  // float4 pieces per round
   static_assert(CQ <= NTT, "one piece per thread");
+  static_assert(CQ % 64 == 0 && R % 64 == 0, "whole waves per array");
   auto fetch_round = [&](int nc, int pr0, bool has_next) -> f4 {
     f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (tid < CQ) {
-      const int arr = tid / (4 * R / 4), rest = tid % (4 * R / 4);
+    if (w < CQ / 64) {
+      const int arr = (w * 64) / R, rest = tid - arr * R;  // arr uniform in the wave
       const int rr = rest / (R / 4), col = 4 * (rest % (R / 4));
       const int pp = pr0 + rr;
       if (pp < g.p) {
-        if (arr == 0) v = load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col);
+        if (arr == 0) v = load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col, R);
         else if (arr == 1) v = *reinterpret_cast<const f4*>(dm1i + ((size_t)bh * g.p + pp) * R + col);
-        else if (has_next) v = load_cols4(Db + (((size_t)bh * g.NK + nc + 1) * g.p + pp) * g.r, g.r, col);
+        else if (has_next) v = load_cols4(Db + (((size_t)bh * g.NK + nc + 1) * g.p + pp) * g.r, g.r, col, R);
       }
     }
     return v;
@@ -544,6 +546,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
         // ---- this half's share of d_xhat[(j,c)][p] = sum_t L[t,j] Y[t][(j,c)] ----
         float* part = dxp + (tt * 4 + u) * K;
+        float vq = 0.0f;  // the sum of tile kt = q % NKT, which lane group q stores
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) {
           const f4 ly = LYt[(tt * NKT + kt) * 64 + lane];
@@ -555,8 +558,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           for (int i = 0; i < 4; i++) rwa[i] += xk * e[i];
           float v = e[0] + e[1] + e[2] + e[3];
           v = col4_sum(v);
-          if (q == 0) part[16 * kt + n] = v;
+          vq = (q % NKT) == kt ? v : vq;
         }
+        part[16 * (q % NKT) + n] = vq;
       };
       if (p < g.p) {
         if (tv >= ELL) row(std::false_type{});
@@ -587,9 +591,17 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           LB[kb][e + 4] = l1[e];
         }
       }
-      bf8 dA;  // A operand of local: row 0 = d_t over the K-slots, t = tslot(8q+e)
+      bf8 dA;  // A operand of local: rows 0, 4, 8, 12 = d_t over the K-slots, t = tslot(8q+e)
+      {
+        const f4 d0 = *reinterpret_cast<const f4*>(s_d + 4 * q);
+        const f4 d1 = *reinterpret_cast<const f4*>(s_d + 16 + 4 * q);
+        const float on = (n & 3) == 0 ? 1.0f : 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; e++) dA[e] = (bf16)(n == 0 ? s_d[(e < 4 ? 4 * q + e : 16 + 4 * q + e - 4)] : 0.0f);
+        for (int e = 0; e < 4; e++) {
+          dA[e] = (bf16)(on * d0[e]);
+          dA[e + 4] = (bf16)(on * d1[e]);
+        }
+      }
       if (pr0 + 4 <= g.p) {
         // all four rows present: every G^T fragment of the round is loaded up
         // front, so one LDS latency covers the whole phase
@@ -615,17 +627,21 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
             for (int kb = 0; kb < KH; kb++)
               dbacc[kb][cb] = MM<bf16>::mma(as_bf8(Ab[rr][kb]), gbf[rr][cb], dbacc[kb][cb]);
-        // local of the rows rr with rr % KW == kq (each (row, column tile) once)
+        // local of the rows rr with rr % KW == kq (each (row, column tile) once):
+        // every lane group holds the row sums (dA repeats d_t in rows 0, 4, 8,
+        // 12), and group q stores column tile q % CH
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) {
           if (rr % KW != kq) continue;
           float* dbrow = Db + (((size_t)bh * g.NK + nc) * g.p + pr0 + rr) * g.r;
+          float lq = 0.0f;
 #pragma unroll
           for (int cb = 0; cb < CH; cb++) {
             const f4 lo = MM<bf16>::mma(dA, gbf[rr][cb], f4{0.0f, 0.0f, 0.0f, 0.0f});
-            const int col = 16 * (cq * CH + cb) + n;
-            if (q == 0 && col < g.r) dbrow[col] = lo[0];
+            lq = (q % CH) == cb ? lo[0] : lq;
           }
+          const int col = 16 * (cq * CH + q % CH) + n;
+          if (q < CH && col < g.r) dbrow[col] = lq;
         }
       } else {
 #pragma unroll 1
@@ -652,7 +668,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             if (do_local) {
               const f4 lo = MM<bf16>::mma(dA, gb, f4{0.0f, 0.0f, 0.0f, 0.0f});
               const int col = 16 * ct + n;
-              if (q == 0 && col < g.r) dbrow[col] = lo[0];
+              if (q == 0 && col < g.r) dbrow[col] = lo[0];  // every group holds it; group 0 stores
             }
           }
         }

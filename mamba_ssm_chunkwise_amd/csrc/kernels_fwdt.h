@@ -101,7 +101,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
       const int pp = pr0 + rr;
       if (pp < g.p)
         v = inc ? *reinterpret_cast<const f4*>(carryL + (size_t)pp * R + col)
-                : load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col);
+                : load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col, R);
     }
     return v;
   };
