@@ -94,9 +94,10 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
     }
   };
   // carry rows of a round through LDS, fetched a round ahead (one float4 per thread)
+  static_assert(R % 64 == 0, "whole waves fetch the carry rows");
   auto fetch_round = [&](int nc, int pr0) -> f4 {
     f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (tid < R) {
+    if (w < R / 64) {
       const int rr = tid / (R / 4), col = 4 * (tid % (R / 4));
       const int pp = pr0 + rr;
       if (pp < g.p)
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
     return v;
   };
   auto store_round = [&](f4 v) {
-    if (tid < R) reinterpret_cast<f4*>(cst)[tid] = v;
+    if (w < R / 64) reinterpret_cast<f4*>(cst)[tid] = v;
   };
 
   f4 m2acc[MA][MB];
@@ -114,9 +115,9 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   for (int a = 0; a < MA; a++)
 #pragma unroll
     for (int b = 0; b < MB; b++) m2acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  bf8 ones;  // A operand of m1: row 0 all ones over the 32 token slots
+  bf8 ones;  // A operand of m1: rows 0, 4, 8, 12 all ones over the 32 token slots
 #pragma unroll
-  for (int e = 0; e < 8; e++) ones[e] = (bf16)(n == 0 ? 1.0f : 0.0f);
+  for (int e = 0; e < 8; e++) ones[e] = (bf16)((n & 3) == 0 ? 1.0f : 0.0f);
 
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
@@ -284,10 +285,43 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
       }
       __syncthreads();  // the round's c transposes are complete
       // ---- m2 += c^T c over the round's rows and tokens; m1 row sums -------------
+      // all four rows present: their fragments are loaded up front (one LDS
+      // latency for the round); otherwise row by row
+      const int nrr = g.p - pr0 < 4 ? g.p - pr0 : 4;
+      if (nrr == 4) {
+        bf8 fa[4][MA], fb[4][MB];
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++) {
+          const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
+#pragma unroll
+          for (int a = 0; a < MA; a++) fa[rr][a] = ld_tok_frag<GTP>(Gr, ta0 + a, lane);
+#pragma unroll
+          for (int b = 0; b < MB; b++) fb[rr][b] = ld_tok_frag<GTP>(Gr, tb0 + b, lane);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+          for (int a = 0; a < MA; a++)
+#pragma unroll
+            for (int b = 0; b < MB; b++) m2acc[a][b] = MM<bf16>::mma(fa[rr][a], fb[rr][b], m2acc[a][b]);
+        {  // m1 of row w / 2 over this wave's column tiles; group q adds column tile q % MB
+          const int rr = w >> 1;
+          float sq = 0.0f;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; r4++) {
+            if (r4 != rr) continue;
+#pragma unroll
+            for (int b = 0; b < MB; b++) {
+              const f4 s1 = MM<bf16>::mma(ones, fb[r4][b], f4{0.0f, 0.0f, 0.0f, 0.0f});
+              sq = (q % MB) == b ? s1[0] : sq;
+            }
+          }
+          if (q < MB) m1s[(pr0 + rr) * R + 16 * (tb0 + q % MB) + n] += sq;
+        }
+      }
 #pragma unroll 1
-      for (int rr = 0; rr < 4; rr++) {
+      for (int rr = 0; rr < nrr && nrr < 4; rr++) {
         const int pp = pr0 + rr;
-        if (pp >= g.p) break;
         const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
         bf8 fa[MA], fb[MB];
 #pragma unroll
@@ -299,11 +333,14 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
 #pragma unroll
           for (int b = 0; b < MB; b++) m2acc[a][b] = MM<bf16>::mma(fa[a], fb[b], m2acc[a][b]);
         if ((w >> 1) == rr) {  // m1 of this row over this wave's column tiles
+          // every lane group holds the row sums; group q adds column tile q % MB
+          float sq = 0.0f;
 #pragma unroll
           for (int b = 0; b < MB; b++) {
             const f4 s1 = MM<bf16>::mma(ones, fb[b], f4{0.0f, 0.0f, 0.0f, 0.0f});
-            if (q == 0) m1s[pp * R + 16 * (tb0 + b) + n] += s1[0];
+            sq = (q % MB) == b ? s1[0] : sq;
           }
+          if (q < MB) m1s[pp * R + 16 * (tb0 + q % MB) + n] += sq;
         }
       }
       store_round(pf);
