@@ -168,7 +168,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8, GTP = R + 16;
   constexpr int NKT = K / 16;      // (j,c) tiles
   constexpr int KSR = NT / 2;      // K-steps over state columns
-  constexpr int KW = NKT < 4 ? NKT : 4;  // d_bhat: waves along (j,c) tiles
+  constexpr int KW = NKT < 2 ? NKT : 2;  // d_bhat: waves along (j,c) tiles (2 x 2 tile blocks per wave at K = 64)
   constexpr int CW = NWT / KW;     // d_bhat: waves along column tiles
   constexpr int KH = NKT / KW;     // d_bhat (j,c) tiles per wave
   constexpr int CH = NT / CW;      // d_bhat column tiles per wave
