@@ -68,15 +68,27 @@ __device__ __forceinline__ s4 lds_read_tr16(const bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)p);
 }
 
+// Row pitch (elements of 2 bytes) of the LDS operand tiles: the smallest
+// n' >= n with n' = 16 (mod 64). Row-per-lane 16-byte operand reads, and the
+// transposing reads below, are free of bank conflicts at such pitches on
+// gfx950 (72 or 136 are two-way conflicted).
+__host__ __device__ constexpr int cf_pitch(int n) { return n + ((16 - n % 64) + 64) % 64; }
+
+// [token][column] blocks of G (and of c in the forward) store the 4-column
+// pieces of each 16-column tile swizzled by token: logical piece v of token t
+// sits at piece v ^ ((t >> 2) & 3). Writes of a lane's piece and the
+// transposing reads are then both free of bank conflicts (pitch R + 16).
+__device__ __forceinline__ int gpiece(int v, int t) { return v ^ ((t >> 2) & 3); }
+
 // MFMA operand over the 32 tokens of a chunk from a [token][column] block of
 // pitch P (bf16): lane (q, n) gets state column 16ct + n at K-slots 8q+e =
 // tokens tslot(8q+e), i.e. 4q+e (e < 4) and 16+4q+e-4. Each of the two reads
-// covers four tokens; lane 4r+s of a group addresses token 4q+r (+16),
-// columns 16ct+4s.. . With P = R + 16 (R/2 + 8 dwords) the eight token rows a
-// half wave reads start 8 banks apart.
+// covers four tokens; lane 4r+s of a group addresses token 4q+r (+16), logical
+// columns 16ct+4s.. (piece s, swizzled by gpiece; tokens t and t+16 share it).
 template <int P>
 __device__ __forceinline__ bf8 ld_tok_frag(const bf16* blk, int ct, int lane) {
-  const bf16* p0 = blk + (4 * (lane >> 4) + ((lane >> 2) & 3)) * P + 4 * (lane & 3) + 16 * ct;
+  const int row = 4 * (lane >> 4) + ((lane >> 2) & 3);
+  const bf16* p0 = blk + row * P + 4 * gpiece(lane & 3, row) + 16 * ct;
   const s4 a = lds_read_tr16(p0), b = lds_read_tr16(p0 + 16 * P);
   const s4 v[2] = {a, b};
   return __builtin_bit_cast(bf8, v);
@@ -104,7 +116,7 @@ __host__ __device__ __forceinline__ int rot_tiles(const Geo& g) {
 constexpr int LWE = 4;
 template <int NT, int CK>
 struct LdsT {
-  static constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8, GTP = R + 16;
+  static constexpr int R = 16 * NT, K = ELL * CK, SP = cf_pitch(R), KP = cf_pitch(K), GTP = R + 16;
   static constexpr size_t Ss = 0;                                     // S rows, K-slot order
   static constexpr size_t bsT = Ss + (size_t)R * SP * 2;              // bhat^T [col][(j,c)]
   static constexpr size_t bsY = bsT + (size_t)R * KP * 2;             // bhat [(j,c)][col slot]
@@ -165,7 +177,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     Geo g, const bf16* __restrict__ xhat, const bf16* __restrict__ bhat, const bf16* __restrict__ da,
     const bf16* __restrict__ rot, const float* __restrict__ carry, const float* __restrict__ dm2,
     const float* __restrict__ dm1i, float* Db, bf16* d_xhat, bf16* d_bhat, bf16* d_da, bf16* d_rot) {
-  constexpr int R = 16 * NT, K = ELL * CK, SP = R + 8, KP = K + 8, GTP = R + 16;
+  constexpr int R = 16 * NT, K = ELL * CK, SP = cf_pitch(R), KP = cf_pitch(K), GTP = R + 16;
   constexpr int NKT = K / 16;      // (j,c) tiles
   constexpr int KSR = NT / 2;      // K-steps over state columns
   constexpr int KW = NKT < 2 ? NKT : 2;  // d_bhat: waves along (j,c) tiles (2 x 2 tile blocks per wave at K = 64)
@@ -464,7 +476,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         f4 Y[NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) Y[kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * q;  // this lane's token row of G
+        bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);  // this lane's piece of its token row
 #pragma unroll
         for (int ky = 0; ky < KSR; ky++) {
           u4 GP;

@@ -20,7 +20,7 @@ namespace mom {
 
 template <int NT, int CK>
 struct LdsF {
-  static constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8, GTP = R + 16;
+  static constexpr int R = 16 * NT, K = ELL * CK, KP = cf_pitch(K), GTP = R + 16;
   static constexpr size_t bsT = 0;                                    // bhat^T [col][(j,c)]
   static constexpr size_t xs = bsT + (size_t)R * KP * 2;              // xhat block [p][(j,c)]
   static constexpr size_t LT = xs + (size_t)XPB * KP * 2;             // L^T [j][t]
@@ -43,7 +43,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
                                                   const bf16* __restrict__ bhat, const bf16* __restrict__ da,
                                                   const bf16* __restrict__ rot, const float* __restrict__ carry,
                                                   const bf16* __restrict__ h0, float* m2part, float* m1part) {
-  constexpr int R = 16 * NT, K = ELL * CK, KP = K + 8, GTP = R + 16;
+  constexpr int R = 16 * NT, K = ELL * CK, KP = cf_pitch(K), GTP = R + 16;
   constexpr int RTP = 16 * RT + 4;
   constexpr int MA = NT / 4, MB = NT / 2;  // m2 tiles per wave: MA row tiles x MB column tiles
   static_assert((ROT == 0) == (RT == 0) && RT <= NT && NT % 4 == 0, "tiling");
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
         }
         // ---- carry, de-rotation, c^T into the row's transpose buffer --------------
         const float* hrow = cst + u * R;
-        bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * q;  // this lane's token row of c
+        bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);  // this lane's piece of its token row
         f4 hl[NT];  // the state row at this lane's token (kept for the last token's carry)
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
