@@ -73,6 +73,9 @@ __device__ __forceinline__ s4 lds_read_tr16(const bf16* p) {
 // transposing reads below, are free of bank conflicts at such pitches on
 // gfx950 (72 or 136 are two-way conflicted).
 __host__ __device__ constexpr int cf_pitch(int n) { return n + ((16 - n % 64) + 64) % 64; }
+// Row pitch (floats) of the rotation tables: >= n and = 8 (mod 32), the same
+// rule for 4-byte elements.
+__host__ __device__ constexpr int rt_pitch(int n) { return n + ((8 - n % 32) + 32) % 32; }
 
 // [token][column] blocks of G (and of c in the forward) store the 4-column
 // pieces of each 16-column tile swizzled by token: logical piece v of token t
@@ -98,8 +101,7 @@ __device__ __forceinline__ bf8 ld_tok_frag(const bf16* blk, int ct, int lane) {
 // to a power of two (0: no rotation). Complex pairs 8 per tile, quaternion
 // blocks 4 per tile. The rotation tables of k_bwdt hold RT tiles per token,
 // padded with the identity: complex [t][8RT][cos, sin], quaternion [t][4RT][4],
-// each token row padded by 4 floats so consecutive tokens start in different
-// banks.
+// each token row padded to rt_pitch floats.
 __host__ __device__ __forceinline__ int rot_tiles(const Geo& g) {
   const int need = (g.rot_kind == 1 || g.rot_kind == 2) ? (g.A + 7) / 8 : g.rot_kind == 3 ? (g.J + 3) / 4 : 0;
   if (need == 0) return 0;
@@ -139,7 +141,7 @@ struct LdsT {
   static constexpr size_t rot = Gs + gsb;
   static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
   // rotation table (RT rotated tiles): 16*RT + 4 floats per token
-  __host__ __device__ static size_t total(int RT) { return rot + (size_t)ELL * (16 * RT + 4) * 4; }
+  __host__ __device__ static size_t total(int RT) { return rot + (size_t)ELL * rt_pitch(16 * RT) * 4; }
   // the rotation-gradient reduction [wave][16 tokens][8RT or 16RT] must fit the G space
   __host__ __device__ static bool fits(int rot_kind, int RT) {
     const size_t rw = rot_kind == 3 ? (size_t)16 * RT : (size_t)8 * RT;
@@ -186,7 +188,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   constexpr int CH = NT / CW;      // d_bhat column tiles per wave
   constexpr int NRC = ROT == 3 ? 4 : 2;  // rotation-gradient values per (t, rotated tile)
   constexpr int RTA = RT > 0 ? RT : 1;
-  constexpr int RTP = 16 * RT + 4;  // rotation table floats per token (padded)
+  constexpr int RTP = rt_pitch(16 * RT);  // rotation table floats per token (padded)
   static_assert((ROT == 0) == (RT == 0) && RT <= NT && CH >= 1 && KH >= 1, "tiling");
   using L = LdsT<NT, CK>;
   extern __shared__ __align__(16) unsigned char smem[];

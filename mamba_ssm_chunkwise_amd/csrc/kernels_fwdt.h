@@ -32,7 +32,7 @@ struct LdsF {
   static constexpr size_t rot = Gs + (size_t)4 * ELL * GTP * 2;
   static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
   // m1 table [p][R] fp32 after the rotation table (RT rotated tiles)
-  __host__ __device__ static size_t m1s(int RT) { return rot + (size_t)ELL * (16 * RT + 4) * 4; }
+  __host__ __device__ static size_t m1s(int RT) { return rot + (size_t)ELL * rt_pitch(16 * RT) * 4; }
   __host__ __device__ static size_t total(int RT, int p) { return m1s(RT) + (size_t)p * R * 4; }
   // with the state rows carried in LDS across the chain: [p][R] fp32 after the m1 table
   __host__ __device__ static size_t total_inc(int RT, int p) { return total(RT, p) + (size_t)p * R * 4; }
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
                                                   const bf16* __restrict__ rot, const float* __restrict__ carry,
                                                   const bf16* __restrict__ h0, float* m2part, float* m1part) {
   constexpr int R = 16 * NT, K = ELL * CK, KP = cf_pitch(K), GTP = R + 16;
-  constexpr int RTP = 16 * RT + 4;
+  constexpr int RTP = rt_pitch(16 * RT);
   constexpr int MA = NT / 4, MB = NT / 2;  // m2 tiles per wave: MA row tiles x MB column tiles
   static_assert((ROT == 0) == (RT == 0) && RT <= NT && NT % 4 == 0, "tiling");
   using L = LdsF<NT, CK>;
