@@ -261,18 +261,19 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   constexpr int CQ = 3 * 4 * R / 4;  // float4 pieces per round
   static_assert(CQ <= NTT, "one piece per thread");
   static_assert(CQ % 64 == 0 && R % 64 == 0, "whole waves per array");
-  auto fetch_round = [&](int nc, int pr0, bool has_next) -> f4 {
+  // This thread's piece of the round rows is fixed: array farr (uniform in the
+  // wave), row frr of the round, columns fcol..; per chunk only the row
+  // pointer of round 0 changes, and each round steps it by four rows.
+  const int farr = (w * 64) / R, frest = tid - farr * R;
+  const int frr = frest / (R / 4), fcol = 4 * (frest % (R / 4));
+  const bool fthr = w < CQ / 64;
+  const float* frow0 = nullptr;  // set per chunk
+  size_t fstep = 0;
+  int flim = R;
+  bool fon = false;
+  auto fetch_round = [&](int pr0) -> f4 {
     f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (w < CQ / 64) {
-      const int arr = (w * 64) / R, rest = tid - arr * R;  // arr uniform in the wave
-      const int rr = rest / (R / 4), col = 4 * (rest % (R / 4));
-      const int pp = pr0 + rr;
-      if (pp < g.p) {
-        if (arr == 0) v = load_cols4(carry + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r, g.r, col, R);
-        else if (arr == 1) v = *reinterpret_cast<const f4*>(dm1i + ((size_t)bh * g.p + pp) * R + col);
-        else if (has_next) v = load_cols4(Db + (((size_t)bh * g.NK + nc + 1) * g.p + pp) * g.r, g.r, col, R);
-      }
-    }
+    if (fon && pr0 + frr < g.p) v = load_cols4(frow0 + (size_t)(pr0 >> 2) * fstep, flim, fcol, R);
     return v;
   };
   auto store_round = [&](f4 v) {
@@ -284,6 +285,23 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int nrounds = (g.p + 3) / 4;
   for (int nc = n1 - 1; nc >= n0; nc--) {
     const bool has_next = nc + 1 < n1;  // D(n+1) comes from this walk; zero at the group's end
+    if (farr == 0) {
+      frow0 = carry + (((size_t)bh * g.NK + nc) * g.p + frr) * g.r;
+      fstep = (size_t)4 * g.r;
+      flim = g.r;
+      fon = fthr;
+    } else if (farr == 1) {
+      frow0 = dm1i + ((size_t)bh * g.p + frr) * R;
+      fstep = (size_t)4 * R;
+      flim = R;
+      fon = fthr;
+    } else {
+      frow0 = Db + (((size_t)bh * g.NK + nc + 1) * g.p + frr) * g.r;
+      fstep = (size_t)4 * g.r;
+      flim = g.r;
+      fon = fthr && has_next;
+    }
+    float* dbase = Db + ((size_t)bh * g.NK + nc) * g.p * g.r;  // D(n) rows of this chunk
     __syncthreads();
     // ---- chunk staging --------------------------------------------------
     if (tid < 64) {
@@ -332,7 +350,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       }
     }
     stage_x(nc, 0);
-    store_round(fetch_round(nc, 0, has_next));
+    store_round(fetch_round(0));
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, tk = idx % ELL;
@@ -388,7 +406,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         __syncthreads();
       }
       const int p = pr0 + u;
-      const f4 pf = fetch_round(nc, pr0 + 4, has_next);  // next round's rows, stored after the d_bhat work
+      const f4 pf = fetch_round(pr0 + 4);  // next round's rows, stored after the d_bhat work
       // One state row, all columns, this wave's 16 tokens; MASK zeroes d_c at
       // tokens >= tv (only the chunk holding valid_len needs it).
       auto row = [&](auto mask_tag) {
@@ -647,7 +665,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) {
           if (rr % KW != kq) continue;
-          float* dbrow = Db + (((size_t)bh * g.NK + nc) * g.p + pr0 + rr) * g.r;
+          float* dbrow = dbase + (size_t)(pr0 + rr) * g.r;
           float lq = 0.0f;
 #pragma unroll
           for (int cb = 0; cb < CH; cb++) {
@@ -671,7 +689,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             for (int e = 0; e < 8; e += 2) Ab[kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
           }
           const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
-          float* dbrow = Db + (((size_t)bh * g.NK + nc) * g.p + pp) * g.r;
+          float* dbrow = dbase + (size_t)pp * g.r;
           const bool do_local = kq == (rr % KW);  // each (row, column tile) once
 #pragma unroll
           for (int cb = 0; cb < CH; cb++) {
