@@ -506,11 +506,14 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             __builtin_amdgcn_sched_barrier(0);
             const int ct = 2 * ky + h2;
             f4 d = *reinterpret_cast<const f4*>(dmrow + 16 * ct + 4 * q);
+            // the tile's S fragments are all requested before the first MFMA
+            // needs one, so their LDS latencies overlap
+            bf8 sa[KSR];
 #pragma unroll
-            for (int ks = 0; ks < KSR; ks++) {
-              const bf8 a = ld_frag(Ss + (16 * ct + n) * SP + 32 * ks + 8 * q);
-              d = MM<bf16>::mma(a, as_bf8(cP[ks]), d);
-            }
+            for (int ks = 0; ks < KSR; ks++) sa[ks] = ld_frag(Ss + (16 * ct + n) * SP + 32 * ks + 8 * q);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KSR; ks++) d = MM<bf16>::mma(sa[ks], as_bf8(cP[ks]), d);
             if constexpr (MASK) {
               if (t >= tv) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
             }
@@ -564,11 +567,11 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             GP[2 * h2 + 1] = pk_bf16(G[2], G[3]);
           }
           // Y[t][(j,c)] += sum over this K-step's columns of G[t][col] bhat[(j,c)][col]
+          bf8 yb[NKT];
 #pragma unroll
-          for (int kt = 0; kt < NKT; kt++) {
-            const bf8 b = ld_frag(bsY + (16 * kt + n) * SP + 32 * ky + 8 * q);
-            Y[kt] = MM<bf16>::mma(as_bf8(GP), b, Y[kt]);
-          }
+          for (int kt = 0; kt < NKT; kt++) yb[kt] = ld_frag(bsY + (16 * kt + n) * SP + 32 * ky + 8 * q);
+#pragma unroll
+          for (int kt = 0; kt < NKT; kt++) Y[kt] = MM<bf16>::mma(as_bf8(GP), yb[kt], Y[kt]);
           // G into the row's block, [token][column]: columns 32ky+4q.. and 32ky+16+4q..
           {
             const unsigned lo[2] = {GP[0], GP[1]}, hi[2] = {GP[2], GP[3]};
