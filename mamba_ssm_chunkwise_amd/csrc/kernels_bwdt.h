@@ -497,20 +497,27 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) Y[kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
         bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);  // this lane's piece of its token row
+        // S fragments are software-pipelined one column tile ahead: tile ct+1's
+        // reads are in flight while tile ct runs its MFMAs and rotation work
+        bf8 sn[KSR];
+#pragma unroll
+        for (int ks = 0; ks < KSR; ks++) sn[ks] = ld_frag(Ss + n * SP + 32 * ks + 8 * q);
 #pragma unroll
         for (int ky = 0; ky < KSR; ky++) {
           u4 GP;
 #pragma unroll
           for (int h2 = 0; h2 < 2; h2++) {
-            // keep each column tile's operand loads next to their use (bounds live registers)
+            // keep each column tile's work together (bounds live registers)
             __builtin_amdgcn_sched_barrier(0);
             const int ct = 2 * ky + h2;
             f4 d = *reinterpret_cast<const f4*>(dmrow + 16 * ct + 4 * q);
-            // the tile's S fragments are all requested before the first MFMA
-            // needs one, so their LDS latencies overlap
             bf8 sa[KSR];
 #pragma unroll
-            for (int ks = 0; ks < KSR; ks++) sa[ks] = ld_frag(Ss + (16 * ct + n) * SP + 32 * ks + 8 * q);
+            for (int ks = 0; ks < KSR; ks++) sa[ks] = sn[ks];
+            if (ct + 1 < NT) {
+#pragma unroll
+              for (int ks = 0; ks < KSR; ks++) sn[ks] = ld_frag(Ss + (16 * (ct + 1) + n) * SP + 32 * ks + 8 * q);
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ks = 0; ks < KSR; ks++) d = MM<bf16>::mma(sa[ks], as_bf8(cP[ks]), d);
