@@ -440,34 +440,40 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
               Wf[ks][e / 2] = pk_bf16(lw[b0 + e / CK] * xv[ks][e], lw[b0 + (e + 1) / CK] * xv[ks][e + 1]);
             }
         }
-        // ---- states, transposed: h~^T[col][t] (carry added on read-out) ----
-        f4 hT[NT];
-#pragma unroll
-        for (int ct = 0; ct < NT; ct++) hT[ct] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        // ---- states h~^T[col][t] one column tile at a time, then the carry, the
+        // de-rotation in the lane and the packed c^T (and h~^T) --------------------
         // tokens 0..15 see j <= 15 only: their last K-steps are all zero
         const int nks = tt == 0 ? (CK + 1) / 2 : CK;
-#pragma unroll
-        for (int ks = 0; ks < CK; ks++) {
-          if (ks < nks) {
-#pragma unroll
-            for (int ct = 0; ct < NT; ct++) {
-              const bf8 a = ld_frag(bsT + (16 * ct + n) * KP + 32 * ks + 8 * q);
-              hT[ct] = MM<bf16>::mma(a, as_bf8(Wf[ks]), hT[ct]);
-            }
-          }
-        }
-        // ---- carry, de-rotation in the lane; c^T (and h~^T) packed ---------
         u4 cP[KSR];
         u4 hP[ROT == 3 ? KSR : 1];
         const float* hrow = cst + u * R;
         const float* dprow = cst + (8 + u) * R;  // D(n+1)[p][:], enters G at the last token
         const float f31 = t == ELL - 1 ? 1.0f : 0.0f;
+        // bhat^T fragments software-pipelined one column tile ahead
+        bf8 bn[CK];
+#pragma unroll
+        for (int ks = 0; ks < CK; ks++)
+          if (ks < nks) bn[ks] = ld_frag(bsT + n * KP + 32 * ks + 8 * q);
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
+          __builtin_amdgcn_sched_barrier(0);
+          bf8 ba[CK];
+#pragma unroll
+          for (int ks = 0; ks < CK; ks++) ba[ks] = bn[ks];
+          if (ct + 1 < NT) {
+#pragma unroll
+            for (int ks = 0; ks < CK; ks++)
+              if (ks < nks) bn[ks] = ld_frag(bsT + (16 * (ct + 1) + n) * KP + 32 * ks + 8 * q);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          f4 hT = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int ks = 0; ks < CK; ks++)
+            if (ks < nks) hT = MM<bf16>::mma(ba[ks], as_bf8(Wf[ks]), hT);
           const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
           f4 h;
 #pragma unroll
-          for (int i = 0; i < 4; i++) h[i] = hT[ct][i] + dtl * hv[i];
+          for (int i = 0; i < 4; i++) h[i] = hT[i] + dtl * hv[i];
           f4 c = h;
           if constexpr (ROT == 1) {
             if (ct < RT) {
