@@ -11,7 +11,7 @@
 // writes c^T through a per-row LDS transpose. After a barrier every wave
 // reads the round's c fragments (tokens in registers) and accumulates a 2 x 4
 // block of 16 x 16 m2 tiles on MFMA; m1 comes from the same fragments through
-// a ones-row MFMA into a per-block table in LDS.
+// an MFMA whose A operand selects one accumulator row per round.
 #pragma once
 
 #include "kernels_bwdt.h"
@@ -27,13 +27,13 @@ struct LdsF {
   static constexpr size_t a = LT + (size_t)ELL * LTP * 4;
   static constexpr size_t d = a + ELL * 4;
   static constexpr size_t lw = d + ELL * 4;                           // W factors [LWE][64] float4
-  static constexpr size_t cst = lw + (size_t)LWE * 64 * 16;           // carry rows of the round [4][R]
-  static constexpr size_t Gs = cst + (size_t)4 * R * 4;               // c blocks [4][token][column]
-  static constexpr size_t rot = Gs + (size_t)4 * ELL * GTP * 2;
+  // carry rows and c blocks of a round, double-buffered by round parity
+  static constexpr size_t cst = lw + (size_t)LWE * 64 * 16;           // carry rows [2][4][R]
+  static constexpr size_t Gs = cst + (size_t)2 * 4 * R * 4;           // c blocks [2][4][token][column]
+  static constexpr size_t rot = Gs + (size_t)2 * 4 * ELL * GTP * 2;
   static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
-  // m1 table [p][R] fp32 after the rotation table (RT rotated tiles)
-  __host__ __device__ static size_t m1s(int RT) { return rot + (size_t)ELL * rt_pitch(16 * RT) * 4; }
-  __host__ __device__ static size_t total(int RT, int p) { return m1s(RT) + (size_t)p * R * 4; }
+  // the rotation table (RT rotated tiles) comes last
+  __host__ __device__ static size_t total(int RT, int) { return rot + (size_t)ELL * rt_pitch(16 * RT) * 4; }
   // with the state rows carried in LDS across the chain: [p][R] fp32 after the m1 table
   __host__ __device__ static size_t total_inc(int RT, int p) { return total(RT, p) + (size_t)p * R * 4; }
 };
@@ -58,7 +58,6 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   float* cst = (float*)(smem + L::cst);
   bf16* Gs = (bf16*)(smem + L::Gs);
   float* rt = (float*)(smem + L::rot);
-  float* m1s = (float*)(smem + L::m1s(RT));
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
@@ -69,7 +68,6 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   const int t = 16 * tt + n;
   const int ta0 = MA * (w >> 1), tb0 = MB * (w & 1);  // this wave's m2 tiles
 
-  for (int idx = tid; idx < g.p * R; idx += NTT) m1s[idx] = 0.0f;
   // carry == nullptr: one group per chain, and the state entering each chunk is
   // carried in LDS: the rows start at h0 and the lanes holding the chunk's last
   // token replace them with the state there, h_-(n+1) = h_{n, last}
@@ -106,8 +104,8 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
     }
     return v;
   };
-  auto store_round = [&](f4 v) {
-    if (w < R / 64) reinterpret_cast<f4*>(cst)[tid] = v;
+  auto store_round = [&](f4 v, int buf) {
+    if (w < R / 64) reinterpret_cast<f4*>(cst + (size_t)buf * 4 * R)[tid] = v;
   };
 
   f4 m2acc[MA][MB];
@@ -115,9 +113,28 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   for (int a = 0; a < MA; a++)
 #pragma unroll
     for (int b = 0; b < MB; b++) m2acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  bf8 ones;  // A operand of m1: rows 0, 4, 8, 12 all ones over the 32 token slots
+  // m1 stays in MFMA accumulators: wave w adds row 4*round + w/2 of every round
+  // (its column tiles tb0..) into accumulator row round % 16 of round tile
+  // round / 16, through an A operand that is one in that row only
+  constexpr int M1T = 2;  // round tiles: 32 rounds, state rows <= 128
+  f4 m1acc[M1T][MB];
 #pragma unroll
-  for (int e = 0; e < 8; e++) ones[e] = (bf16)((n & 3) == 0 ? 1.0f : 0.0f);
+  for (int a = 0; a < M1T; a++)
+#pragma unroll
+    for (int b = 0; b < MB; b++) m1acc[a][b] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto m1_add = [&](int round, const bf8 (&fbr)[MB]) {
+    const bf16 one = (bf16)(n == (round & 15) ? 1.0f : 0.0f);
+    bf8 sel;
+#pragma unroll
+    for (int e = 0; e < 8; e++) sel[e] = one;
+    if (round < 16) {
+#pragma unroll
+      for (int b = 0; b < MB; b++) m1acc[0][b] = MM<bf16>::mma(sel, fbr[b], m1acc[0][b]);
+    } else {
+#pragma unroll
+      for (int b = 0; b < MB; b++) m1acc[1][b] = MM<bf16>::mma(sel, fbr[b], m1acc[1][b]);
+    }
+  };
 
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
@@ -170,7 +187,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
       }
     }
     stage_x(nc, 0);
-    store_round(fetch_round(nc, 0));
+    store_round(fetch_round(nc, 0), 0);
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, tk = idx % ELL;
@@ -198,6 +215,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
         __syncthreads();
       }
       const int p = pr0 + u;
+      bf16* Gsb = Gs + (size_t)(round & 1) * 4 * ELL * GTP;  // this round's c blocks
       const f4 pf = fetch_round(nc, pr0 + 4);
       if (p < g.p) {
         const int pl = p - pblk;
@@ -245,8 +263,8 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
           }
         }
         // ---- carry, de-rotation, c^T into the row's transpose buffer --------------
-        const float* hrow = cst + u * R;
-        bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);  // this lane's piece of its token row
+        const float* hrow = cst + ((size_t)(round & 1) * 4 + u) * R;
+        bf16* Gw = Gsb + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);  // this lane's piece of its token row
         f4 hl[NT];  // the state row at this lane's token (kept for the last token's carry)
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
@@ -283,7 +301,13 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
           for (int ct = 0; ct < NT; ct++) *reinterpret_cast<f4*>(carryL + (size_t)p * R + 16 * ct + 4 * q) = hl[ct];
         }
       }
-      __syncthreads();  // the round's c transposes are complete
+      // the next round's carry rows go to the other buffer: its last readers
+      // (the row work two rounds back) are behind the previous barrier
+      store_round(pf, (round + 1) & 1);
+      __syncthreads();  // the round's c blocks are complete
+      // No barrier closes the round: a wave done with this m2 work starts the
+      // next round's rows, which write the other c buffer; the next barrier
+      // orders this round's reads before the writes two rounds on.
       // ---- m2 += c^T c over the round's rows and tokens; m1 row sums -------------
       // all four rows present: their fragments are loaded up front (one LDS
       // latency for the round); otherwise row by row
@@ -292,7 +316,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
         bf8 fa[4][MA], fb[4][MB];
 #pragma unroll
         for (int rr = 0; rr < 4; rr++) {
-          const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
+          const bf16* Gr = Gsb + (size_t)rr * ELL * GTP;
 #pragma unroll
           for (int a = 0; a < MA; a++) fa[rr][a] = ld_tok_frag<GTP>(Gr, ta0 + a, lane);
 #pragma unroll
@@ -304,25 +328,14 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
           for (int a = 0; a < MA; a++)
 #pragma unroll
             for (int b = 0; b < MB; b++) m2acc[a][b] = MM<bf16>::mma(fa[rr][a], fb[rr][b], m2acc[a][b]);
-        {  // m1 of row w / 2 over this wave's column tiles; group q adds column tile q % MB
-          const int rr = w >> 1;
-          float sq = 0.0f;
 #pragma unroll
-          for (int r4 = 0; r4 < 4; r4++) {
-            if (r4 != rr) continue;
-#pragma unroll
-            for (int b = 0; b < MB; b++) {
-              const f4 s1 = MM<bf16>::mma(ones, fb[r4][b], f4{0.0f, 0.0f, 0.0f, 0.0f});
-              sq = (q % MB) == b ? s1[0] : sq;
-            }
-          }
-          if (q < MB) m1s[(pr0 + rr) * R + 16 * (tb0 + q % MB) + n] += sq;
-        }
+        for (int r4 = 0; r4 < 4; r4++)  // m1 of row w / 2 over this wave's column tiles
+          if (r4 == (w >> 1)) m1_add(round, fb[r4]);
       }
 #pragma unroll 1
       for (int rr = 0; rr < nrr && nrr < 4; rr++) {
         const int pp = pr0 + rr;
-        const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
+        const bf16* Gr = Gsb + (size_t)rr * ELL * GTP;
         bf8 fa[MA], fb[MB];
 #pragma unroll
         for (int a = 0; a < MA; a++) fa[a] = ld_tok_frag<GTP>(Gr, ta0 + a, lane);
@@ -332,23 +345,12 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
         for (int a = 0; a < MA; a++)
 #pragma unroll
           for (int b = 0; b < MB; b++) m2acc[a][b] = MM<bf16>::mma(fa[a], fb[b], m2acc[a][b]);
-        if ((w >> 1) == rr) {  // m1 of this row over this wave's column tiles
-          // every lane group holds the row sums; group q adds column tile q % MB
-          float sq = 0.0f;
-#pragma unroll
-          for (int b = 0; b < MB; b++) {
-            const f4 s1 = MM<bf16>::mma(ones, fb[b], f4{0.0f, 0.0f, 0.0f, 0.0f});
-            sq = (q % MB) == b ? s1[0] : sq;
-          }
-          if (q < MB) m1s[pp * R + 16 * (tb0 + q % MB) + n] += sq;
-        }
+        if ((w >> 1) == rr) m1_add(round, fb);  // m1 of this row over this wave's column tiles
       }
-      store_round(pf);
-      __syncthreads();  // transposes consumed; next round's carry rows staged
     }
   }
   __syncthreads();
-  // ---- the group's partials: m2 tiles straight out, m1 rows from LDS ----------
+  // ---- the group's partials: m2 and m1 tiles straight out of the accumulators --
   float* m2o = m2part + ((size_t)bh * g.NGR + gi) * R * R;
 #pragma unroll
   for (int a = 0; a < MA; a++)
@@ -357,7 +359,15 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
 #pragma unroll
       for (int i = 0; i < 4; i++) m2o[(16 * (ta0 + a) + 4 * q + i) * R + 16 * (tb0 + b) + n] = m2acc[a][b][i];
   float* m1o = m1part + ((size_t)bh * g.NGR + gi) * g.p * R;
-  for (int idx = tid; idx < g.p * R; idx += NTT) m1o[idx] = m1s[idx];
+#pragma unroll
+  for (int a = 0; a < M1T; a++)
+#pragma unroll
+    for (int b = 0; b < MB; b++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int pp = 4 * (16 * a + 4 * q + i) + (w >> 1);  // row of round 16a + 4q + i
+        if (pp < g.p) m1o[(size_t)pp * R + 16 * (tb0 + b) + n] = m1acc[a][b][i];
+      }
 }
 
 }  // namespace mom

@@ -101,6 +101,7 @@ int round_nt(int r, bool /*bf*/) {
 // LDS bytes of k_fwdt for (NT, CK), or 0 when that kernel does not cover the shape.
 size_t fwdt_lds(const Geo& g, int NT, int CK) {
   const int RT = rot_tiles(g);
+  if (g.p > 128) return 0;  // m1 accumulators cover 32 rounds of 4 rows
   if (NT == 4 && CK == 1) return LdsF<4, 1>::total(RT, g.p);
   if (NT == 4 && CK == 2) return LdsF<4, 2>::total(RT, g.p);
   if (NT == 8 && CK == 1) return LdsF<8, 1>::total(RT, g.p);
