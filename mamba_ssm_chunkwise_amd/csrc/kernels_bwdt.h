@@ -128,8 +128,9 @@ struct LdsT {
   static constexpr size_t a = LT + (size_t)ELL * LTP * 4;
   static constexpr size_t d = a + ELL * 4;
   static constexpr size_t lw = d + ELL * 4;
-  static constexpr size_t cst = lw + (size_t)(LWE + 2 * (K / 16)) * 64 * 16;  // carry, d_m1, D+ rows [3][4][R]
-  static constexpr size_t dxp = cst + (size_t)3 * 4 * R * 4;                   // d_xhat partials [2][4][K]
+  // rows of a round: carry [2 buffers][4][R], then d_m1 [4][R] and D+ [4][R]
+  static constexpr size_t cst = lw + (size_t)(LWE + 2 * (K / 16)) * 64 * 16;
+  static constexpr size_t dxp = cst + (size_t)4 * 4 * R * 4;                   // d_xhat partials [2][4][K]
   static constexpr size_t red = dxp + (size_t)2 * 4 * K * 4;
   static constexpr size_t nred = (size_t)NWT * 4 * 16 + NWT * 16 + 4 * K + ELL;  // floats of red
   // G of the round's rows, [row][token][column] (pitch GTP); at chunk end the
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   float* red = (float*)(smem + L::red);
   f4* LWt = (f4*)(smem + L::lw);          // [LWE][64]
   f4* LYt = LWt + LWE * 64;               // [2*NKT][64]
-  float* cst = (float*)(smem + L::cst);   // [carry | d_m1 | D+][row of the round][R]
+  float* cst = (float*)(smem + L::cst);   // [carry x2 | d_m1 | D+][row of the round][R]
   float* dxp = (float*)(smem + L::dxp);   // [token half][row of the round][K]
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
@@ -276,8 +277,13 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     if (fon && pr0 + frr < g.p) v = load_cols4(frow0 + (size_t)(pr0 >> 2) * fstep, flim, fcol, R);
     return v;
   };
-  auto store_round = [&](f4 v) {
-    if (tid < CQ) reinterpret_cast<f4*>(cst)[tid] = v;
+  // The carry rows go to the buffer of the round's parity (they are read before
+  // the round's first barrier); d_m1 and D+ rows to their single buffers.
+  auto store_carry = [&](f4 v, int buf) {
+    if (fthr && farr == 0) reinterpret_cast<f4*>(cst + (size_t)buf * 4 * R)[frest] = v;
+  };
+  auto store_dmdp = [&](f4 v) {
+    if (fthr && farr > 0) reinterpret_cast<f4*>(cst + (size_t)(4 + 4 * farr) * R)[frest] = v;
   };
 
   const int n0 = gi * g.G;
@@ -350,7 +356,11 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       }
     }
     stage_x(nc, 0);
-    store_round(fetch_round(0));
+    {
+      const f4 v0 = fetch_round(0);
+      store_carry(v0, 0);
+      store_dmdp(v0);
+    }
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, tk = idx % ELL;
@@ -400,18 +410,23 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       const int pr0 = 4 * round;
       const int pblk = pr0 - pr0 % XPB;
       if (round > 0 && pr0 % XPB == 0) {
+        __syncthreads();  // the previous round's d_bhat work read the old block
         flush_dx(nc, pblk - XPB);
         __syncthreads();
         stage_x(nc, pblk);
         __syncthreads();
       }
       const int p = pr0 + u;
-      const f4 pf = fetch_round(pr0 + 4);  // next round's rows, stored after the d_bhat work
-      // One state row, all columns, this wave's 16 tokens; MASK zeroes d_c at
-      // tokens >= tv (only the chunk holding valid_len needs it).
-      auto row = [&](auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        const int pl = p - pblk;
+      const f4 pf = fetch_round(pr0 + 4);  // next round's rows
+      // One state row, all columns, this wave's 16 tokens, in two parts: the
+      // states and the packed c^T, then (after a barrier that retires the
+      // previous round's reads of the G blocks) everything that writes them.
+      // MASK zeroes d_c at tokens >= tv (only the chunk holding valid_len needs it).
+      const int pl = p - pblk;
+      u4 cP[KSR];
+      u4 hP[ROT == 3 ? KSR : 1];
+      const float* hrow = cst + ((size_t)(round & 1) * 4 + u) * R;
+      auto row1 = [&]() {
         // ---- W fragment: W[t][(j,c)] = L[t,j] xhat[(j,c)][p] ----------------
         u4 Wf[CK];
         {
@@ -444,11 +459,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         // de-rotation in the lane and the packed c^T (and h~^T) --------------------
         // tokens 0..15 see j <= 15 only: their last K-steps are all zero
         const int nks = tt == 0 ? (CK + 1) / 2 : CK;
-        u4 cP[KSR];
-        u4 hP[ROT == 3 ? KSR : 1];
-        const float* hrow = cst + u * R;
-        const float* dprow = cst + (8 + u) * R;  // D(n+1)[p][:], enters G at the last token
-        const float f31 = t == ELL - 1 ? 1.0f : 0.0f;
+
         // bhat^T fragments software-pipelined one column tile ahead
         bf8 bn[CK];
 #pragma unroll
@@ -497,8 +508,13 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           cP[ct >> 1][2 * (ct & 1)] = pk_bf16(c[0], c[1]);
           cP[ct >> 1][2 * (ct & 1) + 1] = pk_bf16(c[2], c[3]);
         }
+      };
+      auto row2 = [&](auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         // ---- d_c^T = S c^T + d_m1, rotation VJP, G, Y = G bhat^T ------------
-        const float* dmrow = cst + (4 + u) * R;
+        const float* dmrow = cst + (8 + u) * R;
+        const float* dprow = cst + (12 + u) * R;  // D(n+1)[p][:], enters G at the last token
+        const float f31 = t == ELL - 1 ? 1.0f : 0.0f;
         f4 Y[NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) Y[kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -610,11 +626,15 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
         part[16 * (q % NKT) + n] = vq;
       };
+      if (p < g.p) row1();
+      __syncthreads();  // the previous round's d_bhat reads of the G blocks are done
       if (p < g.p) {
-        if (tv >= ELL) row(std::false_type{});
-        else row(std::true_type{});
+        if (tv >= ELL) row2(std::false_type{});
+        else row2(std::true_type{});
       }
-      __syncthreads();  // the round's G transposes and d_xhat partials are complete
+      store_carry(pf, (round + 1) & 1);  // its buffer was last read two rounds back
+      __syncthreads();  // the round's G blocks and d_xhat partials are complete; next carry rows staged
+      store_dmdp(pf);   // the round's d_c work, their only reader, is done
       // ---- d_xhat of the round's rows: the two token halves added ---------------
       if (tid < 4 * K) {
         const int rr = tid / K, k = tid % K;
@@ -721,9 +741,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           }
         }
       }
-      store_round(pf);
-      __syncthreads();  // transposes consumed; next round's rows staged
     }
+    __syncthreads();  // the last round's d_bhat reads are done
     flush_dx(nc, (nrounds - 1) * 4 - ((nrounds - 1) * 4) % XPB);
 
     // ---- chunk end: d_bhat through LDS, written row by row --------------------
