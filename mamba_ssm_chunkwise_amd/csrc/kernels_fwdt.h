@@ -255,20 +255,29 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
 #pragma unroll
         for (int ks = 0; ks < CK; ks++) {
           if (ks < nks) {
+            // the K-step's fragments are all requested before the first MFMA
+            bf8 af[NT];
 #pragma unroll
-            for (int ct = 0; ct < NT; ct++) {
-              const bf8 a = ld_frag(bsT + (16 * ct + n) * KP + 32 * ks + 8 * q);
-              hT[ct] = MM<bf16>::mma(a, as_bf8(Wf[ks]), hT[ct]);
-            }
+            for (int ct = 0; ct < NT; ct++) af[ct] = ld_frag(bsT + (16 * ct + n) * KP + 32 * ks + 8 * q);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ct = 0; ct < NT; ct++) hT[ct] = MM<bf16>::mma(af[ct], as_bf8(Wf[ks]), hT[ct]);
           }
         }
         // ---- carry, de-rotation, c^T into the row's transpose buffer --------------
         const float* hrow = cst + ((size_t)(round & 1) * 4 + u) * R;
         bf16* Gw = Gsb + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);  // this lane's piece of its token row
         f4 hl[NT];  // the state row at this lane's token (kept for the last token's carry)
+        // carry and rotation rows pipelined one column tile ahead
+        f4 hvn = *reinterpret_cast<const f4*>(hrow + 4 * q);
+        f4 rtn = RT > 0 ? *reinterpret_cast<const f4*>(rt + t * RTP + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
-          const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
+          const f4 hv = hvn, rtc = rtn;
+          if (ct + 1 < NT) {
+            hvn = *reinterpret_cast<const f4*>(hrow + 16 * (ct + 1) + 4 * q);
+            if (ct + 1 < RT) rtn = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * (ct + 1) + 4 * q);
+          }
           f4 h;
 #pragma unroll
           for (int i = 0; i < 4; i++) h[i] = hT[ct][i] + dtl * hv[i];
@@ -276,7 +285,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
           f4 c = h;
           if constexpr (ROT == 1) {
             if (ct < RT) {
-              const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+              const f4 r4 = rtc;
               c[0] = r4[0] * h[0] + r4[1] * h[1];
               c[1] = r4[0] * h[1] - r4[1] * h[0];
               c[2] = r4[2] * h[2] + r4[3] * h[3];
@@ -284,7 +293,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
             }
           } else if constexpr (ROT == 3) {
             if (ct < RT) {
-              const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+              const f4 Q = rtc;
               c[0] = Q[0] * h[0] - Q[1] * h[1] - Q[2] * h[2] - Q[3] * h[3];
               c[1] = Q[0] * h[1] + Q[1] * h[0] + Q[2] * h[3] - Q[3] * h[2];
               c[2] = Q[0] * h[2] - Q[1] * h[3] + Q[2] * h[0] + Q[3] * h[1];
