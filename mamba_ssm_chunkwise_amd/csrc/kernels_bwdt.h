@@ -465,30 +465,35 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
         for (int ks = 0; ks < CK; ks++)
           if (ks < nks) bn[ks] = ld_frag(bsT + n * KP + 32 * ks + 8 * q);
+        // carry and rotation rows pipelined one column tile ahead as well
+        f4 hvn = *reinterpret_cast<const f4*>(hrow + 4 * q);
+        f4 rtn = RT > 0 ? *reinterpret_cast<const f4*>(rt + t * RTP + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
           __builtin_amdgcn_sched_barrier(0);
           bf8 ba[CK];
 #pragma unroll
           for (int ks = 0; ks < CK; ks++) ba[ks] = bn[ks];
+          const f4 hv = hvn, rtc = rtn;
           if (ct + 1 < NT) {
 #pragma unroll
             for (int ks = 0; ks < CK; ks++)
               if (ks < nks) bn[ks] = ld_frag(bsT + (16 * (ct + 1) + n) * KP + 32 * ks + 8 * q);
+            hvn = *reinterpret_cast<const f4*>(hrow + 16 * (ct + 1) + 4 * q);
+            if (ct + 1 < RT) rtn = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * (ct + 1) + 4 * q);
           }
           __builtin_amdgcn_sched_barrier(0);
           f4 hT = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int ks = 0; ks < CK; ks++)
             if (ks < nks) hT = MM<bf16>::mma(ba[ks], as_bf8(Wf[ks]), hT);
-          const f4 hv = *reinterpret_cast<const f4*>(hrow + 16 * ct + 4 * q);
           f4 h;
 #pragma unroll
           for (int i = 0; i < 4; i++) h[i] = hT[i] + dtl * hv[i];
           f4 c = h;
           if constexpr (ROT == 1) {
             if (ct < RT) {
-              const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+              const f4 r4 = rtc;
               c[0] = r4[0] * h[0] + r4[1] * h[1];
               c[1] = r4[0] * h[1] - r4[1] * h[0];
               c[2] = r4[2] * h[2] + r4[3] * h[3];
@@ -496,7 +501,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             }
           } else if constexpr (ROT == 3) {
             if (ct < RT) {
-              const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+              const f4 Q = rtc;
               c[0] = Q[0] * h[0] - Q[1] * h[1] - Q[2] * h[2] - Q[3] * h[3];
               c[1] = Q[0] * h[1] + Q[1] * h[0] + Q[2] * h[3] - Q[3] * h[2];
               c[2] = Q[0] * h[2] - Q[1] * h[3] + Q[2] * h[0] + Q[3] * h[1];
