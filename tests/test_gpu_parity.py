@@ -53,6 +53,8 @@ SMALL = [
     (W.ROT_NONE, "bf16", dict(c=1, p=37, r=64, valid_len=96)),
     (W.ROT_PAIRWISE, "bf16", dict(c=2, p=70, r=128, rope_dim=64, valid_len=96)),
     (W.ROT_QUAT, "bf16", dict(c=2, p=33, r=128, quat_blocks=32, valid_len=70)),
+    # 128 state rows: 32 rounds of the transposed kernels (second m1 tile of the forward)
+    (W.ROT_PAIRWISE, "bf16", dict(c=2, p=128, r=128, rope_dim=64, valid_len=96)),
 ]
 
 
@@ -78,6 +80,8 @@ GROUPED = [
     # 512 chains: one group per chain (the forward carries its state rows itself)
     (W.ROT_PAIRWISE, dict(b=8, h=64, s=256, valid_len=250, c=2, p=16, r=64, rope_dim=32, da_mu=-1.0)),
     (W.ROT_HALF, dict(b=8, h=64, s=256, valid_len=256, c=1, p=20, r=64, rope_dim=64, da_mu=0.5)),
+    # ... with a partial last round of rows (p not a multiple of 4)
+    (W.ROT_QUAT, dict(b=8, h=64, s=128, valid_len=120, c=2, p=18, r=64, quat_blocks=16, da_mu=-0.5)),
 ]
 
 
