@@ -150,6 +150,117 @@ struct LdsT {
   }
 };
 
+// Chunk inputs staged into LDS with wide loads. Used when every caller row is
+// 16-byte aligned (r and p multiples of 8; an even number of angles or of
+// quaternion blocks): each thread issues all of its global loads for the
+// chunk before its first LDS store, so a chunk waits for memory once instead
+// of once per element. BY also fills the bhat tile in (j,c)-row order used by
+// the backward. Rows past r, tokens past valid_len and channels past c are
+// written as zeros (identity rotations), like the element-wise staging.
+template <int NT, int CK, int ROT, int RT, bool BY>
+struct WideStage {
+  static constexpr int R = 16 * NT, K = ELL * CK, KP = cf_pitch(K), SP = cf_pitch(R), RTP = rt_pitch(16 * RT);
+  static constexpr int NBU = K * R / 8, NBL = (NBU + NTT - 1) / NTT;   // bhat: 8 columns per load
+  static constexpr int NXU = K * XPB / 8, NXL = (NXU + NTT - 1) / NTT; // xhat block: 8 rows per load
+  // rotation: complex 2 angles per load (4RT pairs per token), quaternion 2 blocks per load
+  static constexpr int NRU = ROT == 1 ? ELL * 4 * RT : ROT == 3 ? ELL * 2 * RT : 0;
+  static constexpr int NRL = NRU > 0 ? (NRU + NTT - 1) / NTT : 1;
+  u4 bv[NBL];
+  u4 xv[NXL];
+  unsigned r1[NRL];
+  u4 r3[NRL];
+
+  __device__ static bool usable(const Geo& g) {
+    const bool rot_ok = ROT == 0 || (ROT == 1 ? (g.A % 2) == 0 : (g.J % 2) == 0);
+    return (g.r % 8) == 0 && (g.p % 8) == 0 && rot_ok;
+  }
+  __device__ void load_x(const Geo& g, const bf16* __restrict__ xhat, int nc, int pblk, int bi, int hi, int tid) {
+#pragma unroll
+    for (int i = 0; i < NXL; i++) {
+      const int idx = tid + i * NTT;
+      const int k = idx / (XPB / 8), c8 = idx % (XPB / 8);
+      const int j = k / CK, ci = k % CK, pos = nc * ELL + j;
+      xv[i] = u4{0u, 0u, 0u, 0u};
+      if (idx < NXU && pblk + 8 * c8 < g.p && ci < g.c && pos < g.V)
+        xv[i] = *reinterpret_cast<const u4*>(xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + 8 * c8);
+    }
+  }
+  __device__ void store_x(bf16* xs, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NXL; i++) {
+      const int idx = tid + i * NTT;
+      if (idx >= NXU) continue;
+      const int k = idx / (XPB / 8), c8 = idx % (XPB / 8);
+      const bf16* v = reinterpret_cast<const bf16*>(&xv[i]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) xs[(8 * c8 + e) * KP + k] = v[e];
+    }
+  }
+  __device__ void load(const Geo& g, const bf16* __restrict__ xhat, const bf16* __restrict__ bhat,
+                       const bf16* __restrict__ rot, int nc, int bi, int hi, int tid) {
+#pragma unroll
+    for (int i = 0; i < NBL; i++) {
+      const int idx = tid + i * NTT;
+      const int k = idx / (R / 8), c8 = idx % (R / 8);
+      const int j = k / CK, ci = k % CK, pos = nc * ELL + j;
+      bv[i] = u4{0u, 0u, 0u, 0u};
+      if (idx < NBU && 8 * c8 < g.r && ci < g.c && pos < g.V)
+        bv[i] = *reinterpret_cast<const u4*>(bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8);
+    }
+    load_x(g, xhat, nc, 0, bi, hi, tid);
+#pragma unroll
+    for (int i = 0; i < NRL; i++) {
+      const int idx = tid + i * NTT;
+      if constexpr (ROT == 1) {
+        const int tk = idx / (4 * RT), a2 = idx % (4 * RT), pos = nc * ELL + tk;
+        r1[i] = 0u;
+        if (idx < NRU && 2 * a2 < g.A && pos < g.V)
+          r1[i] = *reinterpret_cast<const unsigned*>(rot + (((size_t)bi * g.s + pos) * g.h + hi) * g.RW + 2 * a2);
+      } else if constexpr (ROT == 3) {
+        const int tk = idx / (2 * RT), e8 = idx % (2 * RT), pos = nc * ELL + tk;
+        const unsigned one = 0x3f80u;  // bf16 1.0: identity quaternions (1, 0, 0, 0)
+        r3[i] = u4{one, 0u, one, 0u};
+        if (idx < NRU && 2 * e8 < g.J && pos < g.V)
+          r3[i] = *reinterpret_cast<const u4*>(rot + (((size_t)bi * g.s + pos) * g.h + hi) * g.RW + 8 * e8);
+      }
+    }
+  }
+  __device__ void store(const Geo& g, bf16* bsT, bf16* bsY, bf16* xs, float* rt, int tid) const {
+#pragma unroll
+    for (int i = 0; i < NBL; i++) {
+      const int idx = tid + i * NTT;
+      if (idx >= NBU) continue;
+      const int k = idx / (R / 8), c8 = idx % (R / 8);
+      const bf16* v = reinterpret_cast<const bf16*>(&bv[i]);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const int cc = 8 * c8 + e;                      // caller column
+        const int col = cc < g.r ? inv_perm_rc(g, cc) : cc;  // internal column
+        bsT[col * KP + k] = v[e];
+        if constexpr (BY) bsY[k * SP + slot_of_col(col)] = v[e];
+      }
+    }
+    store_x(xs, tid);
+#pragma unroll
+    for (int i = 0; i < NRL; i++) {
+      const int idx = tid + i * NTT;
+      if (idx >= NRU) continue;
+      if constexpr (ROT == 1) {
+        const int tk = idx / (4 * RT), a2 = idx % (4 * RT);
+        float s0, c0, s1, c1;
+        sincosf(bf16_lo(r1[i]), &s0, &c0);
+        sincosf(bf16_hi(r1[i]), &s1, &c1);
+        *reinterpret_cast<f4*>(rt + tk * RTP + 4 * a2) = f4{c0, s0, c1, s1};
+      } else if constexpr (ROT == 3) {
+        const int tk = idx / (2 * RT), e8 = idx % (2 * RT);
+        float* d = rt + tk * RTP + 8 * e8;
+        *reinterpret_cast<f4*>(d) = f4{bf16_lo(r3[i][0]), bf16_hi(r3[i][0]), bf16_lo(r3[i][1]), bf16_hi(r3[i][1])};
+        *reinterpret_cast<f4*>(d + 4) = f4{bf16_lo(r3[i][2]), bf16_hi(r3[i][2]), bf16_lo(r3[i][3]), bf16_hi(r3[i][3])};
+      }
+    }
+  }
+};
+
 // d_m1 in the internal column order, rows padded to R: dm1i[bh][p][R].
 __global__ __launch_bounds__(NTH) void k_prep_dm1(Geo g, int R, const float* __restrict__ dm1, float* dm1i) {
   const size_t e = (size_t)blockIdx.x * NTH + threadIdx.x;
@@ -286,6 +397,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     if (fthr && farr > 0) reinterpret_cast<f4*>(cst + (size_t)(4 + 4 * farr) * R)[frest] = v;
   };
 
+  using WS = WideStage<NT, CK, ROT, RT, true>;
+  const bool wide = WS::usable(g);
+  WS wst;
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
   const int nrounds = (g.p + 3) / 4;
@@ -310,11 +424,12 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     float* dbase = Db + ((size_t)bh * g.NK + nc) * g.p * g.r;  // D(n) rows of this chunk
     __syncthreads();
     // ---- chunk staging --------------------------------------------------
+    float dav = 0.0f;
+    if (tid < 32 && nc * ELL + tid < g.V) dav = (float)da[((size_t)bi * g.s + nc * ELL + tid) * g.h + hi];
+    if (wide) wst.load(g, xhat, bhat, rot, nc, bi, hi, tid);
     if (tid < 64) {
       const int tk = tid & 31;
-      const int pos = nc * ELL + tk;
-      float v = 0.0f;
-      if (tid < 32 && pos < g.V) v = (float)da[((size_t)bi * g.s + pos) * g.h + hi];
+      float v = dav;
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) {
         const float up = __shfl_up(v, off, 32);
@@ -325,6 +440,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         s_d[tk] = expf(v);
       }
     }
+    if (wide) {
+      wst.store(g, bsT, bsY, xs, rt, tid);
+    } else {
     for (int idx = tid; idx < K * R; idx += NTT) {
       const int k = idx / R, col = idx % R;
       const int j = k / CK, ci = k % CK;
@@ -356,6 +474,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       }
     }
     stage_x(nc, 0);
+    }
     {
       const f4 v0 = fetch_round(0);
       store_carry(v0, 0);
@@ -413,7 +532,12 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         __syncthreads();  // the previous round's d_bhat work read the old block
         flush_dx(nc, pblk - XPB);
         __syncthreads();
-        stage_x(nc, pblk);
+        if (wide) {
+          wst.load_x(g, xhat, nc, pblk, bi, hi, tid);
+          wst.store_x(xs, tid);
+        } else {
+          stage_x(nc, pblk);
+        }
         __syncthreads();
       }
       const int p = pr0 + u;

@@ -139,14 +139,18 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
   const int nrounds = (g.p + 3) / 4;
+  using WS = WideStage<NT, CK, ROT, RT, false>;
+  const bool wide = WS::usable(g);
+  WS wst;
   for (int nc = n0; nc < n1; nc++) {
     __syncthreads();
     // ---- chunk staging --------------------------------------------------
+    float dav = 0.0f;
+    if (tid < 32 && nc * ELL + tid < g.V) dav = (float)da[((size_t)bi * g.s + nc * ELL + tid) * g.h + hi];
+    if (wide) wst.load(g, xhat, bhat, rot, nc, bi, hi, tid);
     if (tid < 64) {
       const int tk = tid & 31;
-      const int pos = nc * ELL + tk;
-      float v = 0.0f;
-      if (tid < 32 && pos < g.V) v = (float)da[((size_t)bi * g.s + pos) * g.h + hi];
+      float v = dav;
 #pragma unroll
       for (int off = 1; off < 32; off <<= 1) {
         const float up = __shfl_up(v, off, 32);
@@ -157,6 +161,9 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
         s_d[tk] = expf(v);
       }
     }
+    if (wide) {
+      wst.store(g, bsT, nullptr, xs, rt, tid);
+    } else {
     for (int idx = tid; idx < K * R; idx += NTT) {
       const int k = idx / R, col = idx % R;
       const int j = k / CK, ci = k % CK;
@@ -187,6 +194,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
       }
     }
     stage_x(nc, 0);
+    }
     store_round(fetch_round(nc, 0), 0);
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
@@ -211,7 +219,12 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
       const int pr0 = 4 * round;
       const int pblk = pr0 - pr0 % XPB;
       if (round > 0 && pr0 % XPB == 0) {
-        stage_x(nc, pblk);
+        if (wide) {
+          wst.load_x(g, xhat, nc, pblk, bi, hi, tid);
+          wst.store_x(xs, tid);
+        } else {
+          stage_x(nc, pblk);
+        }
         __syncthreads();
       }
       const int p = pr0 + u;
