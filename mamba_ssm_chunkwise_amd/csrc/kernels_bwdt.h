@@ -174,11 +174,14 @@ struct WideStage {
     const bool rot_ok = ROT == 0 || (ROT == 1 ? (g.A % 2) == 0 : (g.J % 2) == 0);
     return (g.r % 8) == 0 && (g.p % 8) == 0 && rot_ok;
   }
+  // Work items run over (j,c) fastest: the lanes of a wave then write
+  // consecutive (j,c) of one LDS tile column (free of bank conflicts; with
+  // the columns fastest, 16 lanes would hit one bank).
   __device__ void load_x(const Geo& g, const bf16* __restrict__ xhat, int nc, int pblk, int bi, int hi, int tid) {
 #pragma unroll
     for (int i = 0; i < NXL; i++) {
       const int idx = tid + i * NTT;
-      const int k = idx / (XPB / 8), c8 = idx % (XPB / 8);
+      const int k = idx % K, c8 = idx / K;
       const int j = k / CK, ci = k % CK, pos = nc * ELL + j;
       xv[i] = u4{0u, 0u, 0u, 0u};
       if (idx < NXU && pblk + 8 * c8 < g.p && ci < g.c && pos < g.V)
@@ -190,7 +193,7 @@ struct WideStage {
     for (int i = 0; i < NXL; i++) {
       const int idx = tid + i * NTT;
       if (idx >= NXU) continue;
-      const int k = idx / (XPB / 8), c8 = idx % (XPB / 8);
+      const int k = idx % K, c8 = idx / K;
       const bf16* v = reinterpret_cast<const bf16*>(&xv[i]);
 #pragma unroll
       for (int e = 0; e < 8; e++) xs[(8 * c8 + e) * KP + k] = v[e];
@@ -201,7 +204,7 @@ struct WideStage {
 #pragma unroll
     for (int i = 0; i < NBL; i++) {
       const int idx = tid + i * NTT;
-      const int k = idx / (R / 8), c8 = idx % (R / 8);
+      const int k = idx % K, c8 = idx / K;
       const int j = k / CK, ci = k % CK, pos = nc * ELL + j;
       bv[i] = u4{0u, 0u, 0u, 0u};
       if (idx < NBU && 8 * c8 < g.r && ci < g.c && pos < g.V)
@@ -230,14 +233,28 @@ struct WideStage {
     for (int i = 0; i < NBL; i++) {
       const int idx = tid + i * NTT;
       if (idx >= NBU) continue;
-      const int k = idx / (R / 8), c8 = idx % (R / 8);
+      const int k = idx % K, c8 = idx / K;
       const bf16* v = reinterpret_cast<const bf16*>(&bv[i]);
+      if (!g.half) {
+        // internal columns 8c8.. = caller columns: their K-slots in the (j,c)-row
+        // tile are two runs of four, 32ks + 8q + 4h + (0..3) for q = c8 % 2 * 2,
+        // +1 (columns 16h + 4q.. of K-step ks = c8 / 4, h = c8 / 2 % 2)
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const int cc = 8 * c8 + e;                      // caller column
-        const int col = cc < g.r ? inv_perm_rc(g, cc) : cc;  // internal column
-        bsT[col * KP + k] = v[e];
-        if constexpr (BY) bsY[k * SP + slot_of_col(col)] = v[e];
+        for (int e = 0; e < 8; e++) bsT[(8 * c8 + e) * KP + k] = v[e];
+        if constexpr (BY) {
+          const int s0 = slot_of_col(8 * c8), s1 = slot_of_col(8 * c8 + 4);
+          const unsigned lo[2] = {bv[i][0], bv[i][1]}, hi[2] = {bv[i][2], bv[i][3]};
+          *reinterpret_cast<unsigned long long*>(bsY + k * SP + s0) = __builtin_bit_cast(unsigned long long, lo);
+          *reinterpret_cast<unsigned long long*>(bsY + k * SP + s1) = __builtin_bit_cast(unsigned long long, hi);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int cc = 8 * c8 + e;                           // caller column
+          const int col = cc < g.r ? inv_perm_rc(g, cc) : cc;  // internal column
+          bsT[col * KP + k] = v[e];
+          if constexpr (BY) bsY[k * SP + slot_of_col(col)] = v[e];
+        }
       }
     }
     store_x(xs, tid);
@@ -400,9 +417,18 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   using WS = WideStage<NT, CK, ROT, RT, true>;
   const bool wide = WS::usable(g);
   WS wst;
+  float dav = 0.0f;
+  // the global loads of a chunk's inputs: issued for the next chunk of the walk
+  // before the current chunk's closing work, which then covers their latency
+  auto load_chunk = [&](int ncl) {
+    dav = 0.0f;
+    if (tid < 32 && ncl * ELL + tid < g.V) dav = (float)da[((size_t)bi * g.s + ncl * ELL + tid) * g.h + hi];
+    if (wide) wst.load(g, xhat, bhat, rot, ncl, bi, hi, tid);
+  };
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
   const int nrounds = (g.p + 3) / 4;
+  if (n1 > n0) load_chunk(n1 - 1);
   for (int nc = n1 - 1; nc >= n0; nc--) {
     const bool has_next = nc + 1 < n1;  // D(n+1) comes from this walk; zero at the group's end
     if (farr == 0) {
@@ -423,10 +449,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
     float* dbase = Db + ((size_t)bh * g.NK + nc) * g.p * g.r;  // D(n) rows of this chunk
     __syncthreads();
-    // ---- chunk staging --------------------------------------------------
-    float dav = 0.0f;
-    if (tid < 32 && nc * ELL + tid < g.V) dav = (float)da[((size_t)bi * g.s + nc * ELL + tid) * g.h + hi];
-    if (wide) wst.load(g, xhat, bhat, rot, nc, bi, hi, tid);
+    // ---- chunk staging (its global loads were issued one step of the walk earlier)
     if (tid < 64) {
       const int tk = tid & 31;
       float v = dav;
@@ -872,6 +895,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       }
     }
     __syncthreads();  // the last round's d_bhat reads are done
+    if (nc > n0) load_chunk(nc - 1);
     flush_dx(nc, (nrounds - 1) * 4 - ((nrounds - 1) * 4) % XPB);
 
     // ---- chunk end: d_bhat through LDS, written row by row --------------------
