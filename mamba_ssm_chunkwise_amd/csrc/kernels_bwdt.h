@@ -361,6 +361,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
   }
 
+  using WS = WideStage<NT, CK, ROT, RT, true>;
+  const bool wide = WS::usable(g);
+  WS wst;
   auto stage_x = [&](int nc, int pblk) {
     for (int idx = tid; idx < K * XPB; idx += NTT) {
       const int k = idx / XPB, pl = idx % XPB;
@@ -374,6 +377,25 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   };
   auto flush_dx = [&](int nc, int pblk) {
     if (d_xhat == nullptr) return;
+    if (wide) {
+      // 16-byte stores of 8 rows p; work items over (j,c) fastest (LDS reads
+      // of one row free of bank conflicts)
+      constexpr int NXU = K * XPB / 8;
+      for (int idx = tid; idx < NXU; idx += NTT) {
+        const int k = idx % K, c8 = idx / K;
+        const int j = k / CK, ci = k % CK;
+        const int pos = nc * ELL + j;
+        if (ci < g.c && pos < g.s && pblk + 8 * c8 < g.p) {
+          u4 v;
+#pragma unroll
+          for (int e = 0; e < 4; e++)
+            v[e] = (unsigned)__builtin_bit_cast(unsigned short, dXs[(8 * c8 + 2 * e) * KP + k]) |
+                   ((unsigned)__builtin_bit_cast(unsigned short, dXs[(8 * c8 + 2 * e + 1) * KP + k]) << 16);
+          *reinterpret_cast<u4*>(d_xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + 8 * c8) = v;
+        }
+      }
+      return;
+    }
     const int rows = g.p - pblk < XPB ? g.p - pblk : XPB;
     for (int idx = tid; idx < K * rows; idx += NTT) {
       const int k = idx / rows, pl = idx % rows;
@@ -414,9 +436,6 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     if (fthr && farr > 0) reinterpret_cast<f4*>(cst + (size_t)(4 + 4 * farr) * R)[frest] = v;
   };
 
-  using WS = WideStage<NT, CK, ROT, RT, true>;
-  const bool wide = WS::usable(g);
-  WS wst;
   float dav = 0.0f;
   // the global loads of a chunk's inputs: issued for the next chunk of the walk
   // before the current chunk's closing work, which then covers their latency
@@ -909,6 +928,18 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           for (int i = 0; i < 4; i++)
             DBs[(16 * (kq * KH + kb) + 4 * q + i) * SP + 16 * (cq * CH + cb) + n] = (bf16)dbacc[kb][cb][i];
       __syncthreads();
+      if (wide && !g.half) {
+        // internal columns are the caller's: 16-byte pieces of 8 columns, a row's
+        // pieces on consecutive lanes
+        for (int idx = tid; idx < K * (R / 8); idx += NTT) {
+          const int k = idx / (R / 8), c8 = idx % (R / 8);
+          const int j = k / CK, ci = k % CK;
+          const int pos = nc * ELL + j;
+          if (pos < g.s && ci < g.c && 8 * c8 < g.r)
+            *reinterpret_cast<u4*>(d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8) =
+                *reinterpret_cast<const u4*>(DBs + k * SP + 8 * c8);
+        }
+      } else
       for (int idx = tid; idx < K * g.r; idx += NTT) {
         const int k = idx / g.r, ra = idx - k * g.r;
         const int j = k / CK, ci = k % CK;
