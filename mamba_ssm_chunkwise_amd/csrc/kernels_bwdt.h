@@ -437,8 +437,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   };
 
   float dav = 0.0f;
-  // the global loads of a chunk's inputs: issued for the next chunk of the walk
-  // before the current chunk's closing work, which then covers their latency
+  // the global loads of a chunk's inputs, all issued before the first is used
   auto load_chunk = [&](int ncl) {
     dav = 0.0f;
     if (tid < 32 && ncl * ELL + tid < g.V) dav = (float)da[((size_t)bi * g.s + ncl * ELL + tid) * g.h + hi];
@@ -447,7 +446,6 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
   const int nrounds = (g.p + 3) / 4;
-  if (n1 > n0) load_chunk(n1 - 1);
   for (int nc = n1 - 1; nc >= n0; nc--) {
     const bool has_next = nc + 1 < n1;  // D(n+1) comes from this walk; zero at the group's end
     if (farr == 0) {
@@ -467,8 +465,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       fon = fthr && has_next;
     }
     float* dbase = Db + ((size_t)bh * g.NK + nc) * g.p * g.r;  // D(n) rows of this chunk
+    load_chunk(nc);  // in flight while the waves meet at the barrier
     __syncthreads();
-    // ---- chunk staging (its global loads were issued one step of the walk earlier)
+    // ---- chunk staging
     if (tid < 64) {
       const int tk = tid & 31;
       float v = dav;
@@ -914,7 +913,6 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       }
     }
     __syncthreads();  // the last round's d_bhat reads are done
-    if (nc > n0) load_chunk(nc - 1);
     flush_dx(nc, (nrounds - 1) * 4 - ((nrounds - 1) * 4) % XPB);
 
     // ---- chunk end: d_bhat through LDS, written row by row --------------------
@@ -981,7 +979,6 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     float* rg = red;                      // [w][q][16] partial <G[t], h_->
     float* rwp = rg + NWT * 4 * 16;       // [w][16] partial row sums Rw
     float* csum = rwp + NWT * 16;         // [rr][(j,c)] partial column sums
-    float* ddv = csum + 4 * K;            // [t]
     rg[(w * 4 + q) * 16 + n] = gcar;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -1014,16 +1011,12 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         if (tk >= off) y += yu;
       }
       const float yex = __shfl_up(y, 1, 32);
-      if (tid < ELL) {
+      if (tid < ELL && d_da != nullptr) {
         const float pre = tk > 0 ? yex : 0.0f;
         // past valid_len every term vanishes; C - Rw cancels there only up to rounding
-        ddv[tk] = tk < tv ? x + pre : 0.0f;
+        const int pos = nc * ELL + tid;
+        if (pos < g.s) d_da[((size_t)bi * g.s + pos) * g.h + hi] = (bf16)(tk < tv ? x + pre : 0.0f);
       }
-    }
-    __syncthreads();
-    if (tid < ELL && d_da != nullptr) {
-      const int pos = nc * ELL + tid;
-      if (pos < g.s) d_da[((size_t)bi * g.s + pos) * g.h + hi] = (bf16)ddv[tid];
     }
   }
 }
