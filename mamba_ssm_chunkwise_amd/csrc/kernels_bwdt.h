@@ -998,8 +998,11 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           for (int qq = 0; qq < 4; qq++) gt += rg[((4 * half + uu) * 4 + qq) * 16 + (tk & 15)];
           rw += rwp[(4 * half + uu) * 16 + (tk & 15)];
         }
+        // channels ci >= c hold exact zeros (their xhat is staged as zero)
+#pragma unroll
         for (int rr = 0; rr < 4; rr++)
-          for (int ci = 0; ci < g.c; ci++) cj += csum[rr * K + tk * CK + ci];
+#pragma unroll
+          for (int ci = 0; ci < CK; ci++) cj += csum[rr * K + tk * CK + ci];
         x = s_d[tk] * gt;
         y = cj - rw;
       }
