@@ -446,6 +446,50 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int n0 = gi * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
   const int nrounds = (g.p + 3) / 4;
+  // ---- d_da of chunk ncs: sum_{t>=s} d_t <G[t], h_-> + sum_{s'<s} (C[s'] - Rw[s']),
+  // from the per-wave partials the chunk left in LDS (and its s_d, which the
+  // first wave alone rewrites, after this scan)
+  float* rg = (float*)(smem + L::red);  // [w][q][16] partial <G[t], h_->
+  float* rwp = rg + NWT * 4 * 16;       // [w][16] partial row sums Rw
+  float* csum = rwp + NWT * 16;         // [rr][(j,c)] partial column sums
+  auto dda_scan = [&](int ncs) {
+    if (tid >= 64) return;
+    // lane t < 32: x = d_t <G[t], h_->, y = C[t] - Rw[t]; then a suffix scan of x
+    // and an exclusive prefix scan of y across the lanes (fixed order)
+    const int tvs = g.V - ncs * ELL;
+    const int tk = tid & 31, half = tk >> 4;
+    float x = 0.0f, y = 0.0f;
+    if (tid < ELL) {
+      float gt = 0.0f, rw = 0.0f, cj = 0.0f;
+#pragma unroll
+      for (int uu = 0; uu < 4; uu++) {
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) gt += rg[((4 * half + uu) * 4 + qq) * 16 + (tk & 15)];
+        rw += rwp[(4 * half + uu) * 16 + (tk & 15)];
+      }
+      // channels ci >= c hold exact zeros (their xhat is staged as zero)
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++)
+#pragma unroll
+        for (int ci = 0; ci < CK; ci++) cj += csum[rr * K + tk * CK + ci];
+      x = s_d[tk] * gt;
+      y = cj - rw;
+    }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      const float xd = __shfl_down(x, off, 32);
+      const float yu = __shfl_up(y, off, 32);
+      if (tk + off < 32) x += xd;
+      if (tk >= off) y += yu;
+    }
+    const float yex = __shfl_up(y, 1, 32);
+    if (tid < ELL && d_da != nullptr) {
+      const float pre = tk > 0 ? yex : 0.0f;
+      // past valid_len every term vanishes; C - Rw cancels there only up to rounding
+      const int pos = ncs * ELL + tid;
+      if (pos < g.s) d_da[((size_t)bi * g.s + pos) * g.h + hi] = (bf16)(tk < tvs ? x + pre : 0.0f);
+    }
+  };
   for (int nc = n1 - 1; nc >= n0; nc--) {
     const bool has_next = nc + 1 < n1;  // D(n+1) comes from this walk; zero at the group's end
     if (farr == 0) {
@@ -467,6 +511,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     float* dbase = Db + ((size_t)bh * g.NK + nc) * g.p * g.r;  // D(n) rows of this chunk
     load_chunk(nc);  // in flight while the waves meet at the barrier
     __syncthreads();
+    if (nc + 1 < n1) dda_scan(nc + 1);  // the previous step's d_da
     // ---- chunk staging
     if (tid < 64) {
       const int tk = tid & 31;
@@ -975,10 +1020,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
       }
     }
-    // ---- d_da: sum_{t>=s} d_t <G[t], h_-> + sum_{s'<s} (C[s'] - Rw[s']) ------------
-    float* rg = red;                      // [w][q][16] partial <G[t], h_->
-    float* rwp = rg + NWT * 4 * 16;       // [w][16] partial row sums Rw
-    float* csum = rwp + NWT * 16;         // [rr][(j,c)] partial column sums
+    // ---- d_da partials of the chunk (scanned at the next step of the walk) --------
     rg[(w * 4 + q) * 16 + n] = gcar;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -986,42 +1028,11 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       if (n == 0) rwp[w * 16 + 4 * q + i] = r;
     }
     if (tid < 4 * K) csum[tid] = cct;
-    __syncthreads();
-    if (tid < 64) {
-      // lane t < 32: x = d_t <G[t], h_->, y = C[t] - Rw[t]; then a suffix scan of x
-      // and an exclusive prefix scan of y across the lanes (fixed order)
-      const int tk = tid & 31, half = tk >> 4;
-      float x = 0.0f, y = 0.0f;
-      if (tid < ELL) {
-        float gt = 0.0f, rw = 0.0f, cj = 0.0f;
-        for (int uu = 0; uu < 4; uu++) {
-          for (int qq = 0; qq < 4; qq++) gt += rg[((4 * half + uu) * 4 + qq) * 16 + (tk & 15)];
-          rw += rwp[(4 * half + uu) * 16 + (tk & 15)];
-        }
-        // channels ci >= c hold exact zeros (their xhat is staged as zero)
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++)
-#pragma unroll
-          for (int ci = 0; ci < CK; ci++) cj += csum[rr * K + tk * CK + ci];
-        x = s_d[tk] * gt;
-        y = cj - rw;
-      }
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const float xd = __shfl_down(x, off, 32);
-        const float yu = __shfl_up(y, off, 32);
-        if (tk + off < 32) x += xd;
-        if (tk >= off) y += yu;
-      }
-      const float yex = __shfl_up(y, 1, 32);
-      if (tid < ELL && d_da != nullptr) {
-        const float pre = tk > 0 ? yex : 0.0f;
-        // past valid_len every term vanishes; C - Rw cancels there only up to rounding
-        const int pos = nc * ELL + tid;
-        if (pos < g.s) d_da[((size_t)bi * g.s + pos) * g.h + hi] = (bf16)(tk < tv ? x + pre : 0.0f);
-      }
-    }
+    // the scan of these partials runs at the start of the next step of the walk,
+    // behind the barrier there, while the next chunk's loads are in flight
   }
+  __syncthreads();
+  if (n1 > n0) dda_scan(n0);
 }
 
 }  // namespace mom
