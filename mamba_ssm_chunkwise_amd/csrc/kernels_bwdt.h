@@ -510,6 +510,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
     float* dbase = Db + ((size_t)bh * g.NK + nc) * g.p * g.r;  // D(n) rows of this chunk
     load_chunk(nc);  // in flight while the waves meet at the barrier
+    const f4 v0 = fetch_round(0);
     __syncthreads();
     if (nc + 1 < n1) dda_scan(nc + 1);  // the previous step's d_da
     // ---- chunk staging
@@ -561,11 +562,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
     stage_x(nc, 0);
     }
-    {
-      const f4 v0 = fetch_round(0);
-      store_carry(v0, 0);
-      store_dmdp(v0);
-    }
+    store_carry(v0, 0);
+    store_dmdp(v0);
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, tk = idx % ELL;
@@ -960,9 +958,14 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     __syncthreads();  // the last round's d_bhat reads are done
     flush_dx(nc, (nrounds - 1) * 4 - ((nrounds - 1) * 4) % XPB);
 
-    // ---- chunk end: d_bhat through LDS, written row by row --------------------
+    // ---- chunk end: d_bhat, the rotation gradient and the d_da partials go
+    // through LDS behind one barrier: d_bhat in the G space, the rotation-gradient
+    // partials in the (now dead) bhat tiles when they fit there
+    constexpr int rw = ROT == 3 ? 16 * RTA : 8 * RTA;
+    constexpr bool RB_IN_B = (size_t)NWT * 16 * rw * 4 <= L::xs - L::bsT;
+    float* RB = RB_IN_B ? (float*)(smem + L::bsT) : (float*)Gs;  // [w][16 tokens][rw]
+    bf16* DBs = Gs;  // [K][SP]
     if (d_bhat != nullptr) {
-      bf16* DBs = Gs;  // [K][SP]
 #pragma unroll
       for (int kb = 0; kb < KH; kb++)
 #pragma unroll
@@ -970,7 +973,32 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
           for (int i = 0; i < 4; i++)
             DBs[(16 * (kq * KH + kb) + 4 * q + i) * SP + 16 * (cq * CH + cb) + n] = (bf16)dbacc[kb][cb][i];
-      __syncthreads();
+    }
+    auto rb_write = [&]() {
+#pragma unroll
+      for (int ct = 0; ct < RTA; ct++) {
+        float* dst = RB + (w * 16 + n) * rw;
+        if constexpr (ROT == 1) {
+          dst[8 * ct + 2 * q] = racc[ct][0];
+          dst[8 * ct + 2 * q + 1] = racc[ct][1];
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; v++) dst[4 * (4 * ct + q) + v] = racc[ct][v];
+        }
+      }
+    };
+    if constexpr (ROT != 0 && RB_IN_B) {
+      if (d_rot != nullptr) rb_write();
+    }
+    rg[(w * 4 + q) * 16 + n] = gcar;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float r = row16_sum(rwa[i]);
+      if (n == 0) rwp[w * 16 + 4 * q + i] = r;
+    }
+    if (tid < 4 * K) csum[tid] = cct;
+    __syncthreads();
+    if (d_bhat != nullptr) {
       if (wide && !g.half) {
         // internal columns are the caller's: 16-byte pieces of 8 columns, a row's
         // pieces on consecutive lanes
@@ -982,33 +1010,24 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             *reinterpret_cast<u4*>(d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8) =
                 *reinterpret_cast<const u4*>(DBs + k * SP + 8 * c8);
         }
-      } else
-      for (int idx = tid; idx < K * g.r; idx += NTT) {
-        const int k = idx / g.r, ra = idx - k * g.r;
-        const int j = k / CK, ci = k % CK;
-        const int pos = nc * ELL + j;
-        if (pos < g.s && ci < g.c)
-          d_bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + ra] = DBs[k * SP + inv_perm_rc(g, ra)];
+      } else {
+        for (int idx = tid; idx < K * g.r; idx += NTT) {
+          const int k = idx / g.r, ra = idx - k * g.r;
+          const int j = k / CK, ci = k % CK;
+          const int pos = nc * ELL + j;
+          if (pos < g.s && ci < g.c)
+            d_bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + ra] = DBs[k * SP + inv_perm_rc(g, ra)];
+        }
       }
-      __syncthreads();
     }
     // ---- rotation gradient: fixed-order sum over the waves of a token half -----
     if constexpr (ROT != 0) {
       if (d_rot != nullptr) {
-        constexpr int rw = ROT == 3 ? 16 * RTA : 8 * RTA;
-        float* RB = (float*)Gs;  // [w][16 tokens][rw]
-#pragma unroll
-        for (int ct = 0; ct < RTA; ct++) {
-          float* dst = RB + (w * 16 + n) * rw;
-          if constexpr (ROT == 1) {
-            dst[8 * ct + 2 * q] = racc[ct][0];
-            dst[8 * ct + 2 * q + 1] = racc[ct][1];
-          } else {
-#pragma unroll
-            for (int v = 0; v < 4; v++) dst[4 * (4 * ct + q) + v] = racc[ct][v];
-          }
+        if constexpr (!RB_IN_B) {
+          __syncthreads();  // the d_bhat reads of the shared space are done
+          rb_write();
+          __syncthreads();
         }
-        __syncthreads();
         for (int idx = tid; idx < ELL * g.RW; idx += NTT) {
           const int tk = idx / g.RW, e = idx % g.RW;
           const int half = tk >> 4;
@@ -1020,14 +1039,6 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
       }
     }
-    // ---- d_da partials of the chunk (scanned at the next step of the walk) --------
-    rg[(w * 4 + q) * 16 + n] = gcar;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const float r = row16_sum(rwa[i]);
-      if (n == 0) rwp[w * 16 + 4 * q + i] = r;
-    }
-    if (tid < 4 * K) csum[tid] = cct;
     // the scan of these partials runs at the start of the next step of the walk,
     // behind the barrier there, while the next chunk's loads are in flight
   }
