@@ -213,13 +213,15 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
     }
     __syncthreads();
     const int tv = g.V - nc * ELL;  // valid tokens of this chunk (>= 1)
-    if (w == 0) {
+    if (w < LWE) {  // W factor entry w (four of the flattened f = (h*CK+ks)*(8/CK)+v)
+      f4 v;
 #pragma unroll
-      for (int f = 0; f < 16; f++) {
-        const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), v = rest % (8 / CK);
-        reinterpret_cast<float*>(LWt + (f >> 2) * 64 + lane)[f & 3] =
-            LT[((32 * ks + 8 * q) / CK + v) * LTP + 16 * hh + n];
+      for (int i = 0; i < 4; i++) {
+        const int f = 4 * w + i;
+        const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), vv = rest % (8 / CK);
+        v[i] = LT[((32 * ks + 8 * q) / CK + vv) * LTP + 16 * hh + n];
       }
+      LWt[w * 64 + lane] = v;
     }
     __syncthreads();
     const float dtl = s_d[t];
