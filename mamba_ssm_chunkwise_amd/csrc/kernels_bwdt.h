@@ -509,10 +509,10 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       fon = fthr && has_next;
     }
     float* dbase = Db + ((size_t)bh * g.NK + nc) * g.p * g.r;  // D(n) rows of this chunk
-    load_chunk(nc);  // in flight while the waves meet at the barrier
-    const f4 v0 = fetch_round(0);
     __syncthreads();
     if (nc + 1 < n1) dda_scan(nc + 1);  // the previous step's d_da
+    load_chunk(nc);
+    const f4 v0 = fetch_round(0);
     // ---- chunk staging
     if (tid < 64) {
       const int tk = tid & 31;
