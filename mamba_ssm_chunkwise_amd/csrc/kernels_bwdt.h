@@ -339,7 +339,10 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
-  const int tid = threadIdx.x;
+  // tid is refreshed through an empty asm at every chunk: the per-thread
+  // addresses of the chunk-boundary work are then recomputed per chunk instead
+  // of being hoisted out of the chunk loop and held (spilled) across the rounds
+  int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform in the wave
   const int lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int u = w & 3, tt = w >> 2;       // row slot of the round, token half
@@ -491,6 +494,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
   };
   for (int nc = n1 - 1; nc >= n0; nc--) {
+    asm volatile("" : "+v"(tid));
     const bool has_next = nc + 1 < n1;  // D(n+1) comes from this walk; zero at the group's end
     if (farr == 0) {
       frow0 = carry + (((size_t)bh * g.NK + nc) * g.p + frr) * g.r;
