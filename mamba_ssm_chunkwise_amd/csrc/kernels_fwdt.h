@@ -61,7 +61,10 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
-  const int tid = threadIdx.x;
+  // tid is refreshed through an empty asm at every chunk, so the per-thread
+  // addresses of the chunk staging are recomputed per chunk rather than held
+  // (spilled) across the rounds
+  int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform in the wave
   const int lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int u = w & 3, tt = w >> 2;
@@ -156,6 +159,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   const int pfr = nrounds - PFR > lxr ? nrounds - PFR : lxr;
   if (n1 > n0) load_chunk(n0);
   for (int nc = n0; nc < n1; nc++) {
+    asm volatile("" : "+v"(tid));
     __syncthreads();
     // ---- chunk staging (its global loads were issued during the previous chunk)
     if (tid < 64) {
