@@ -55,6 +55,12 @@ SMALL = [
     (W.ROT_QUAT, "bf16", dict(c=2, p=33, r=128, quat_blocks=32, valid_len=70)),
     # 128 state rows: 32 rounds of the transposed kernels (second m1 tile of the forward)
     (W.ROT_PAIRWISE, "bf16", dict(c=2, p=128, r=128, rope_dim=64, valid_len=96)),
+    # rows that allow 16-byte staging except for the rotation input: an odd number
+    # of angles, an odd number of quaternion blocks (element-wise staging)
+    (W.ROT_PAIRWISE, "bf16", dict(c=2, p=16, r=32, rope_dim=6, valid_len=90)),
+    (W.ROT_QUAT, "bf16", dict(c=1, p=16, r=32, quat_blocks=3, valid_len=96)),
+    # half-split with 16-byte staging: caller columns scattered to the interleaved order
+    (W.ROT_HALF, "bf16", dict(c=2, p=32, r=128, rope_dim=64, valid_len=96)),
 ]
 
 
