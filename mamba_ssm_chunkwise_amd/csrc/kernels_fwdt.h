@@ -351,6 +351,10 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
       // all four rows present: their fragments are loaded up front (one LDS
       // latency for the round); otherwise row by row
       const int nrr = g.p - pr0 < 4 ? g.p - pr0 : 4;
+      // the second token half has the longer row work ahead of it: its waves get
+      // issue priority for their m2 work, so the first half's m2 work fills in
+      // under their row work instead of the other way round
+      if (tt == 1) __builtin_amdgcn_s_setprio(2);
       if (nrr == 4) {
         bf8 fa[4][MA], fb[4][MB];
 #pragma unroll
@@ -386,6 +390,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
           for (int b = 0; b < MB; b++) m2acc[a][b] = MM<bf16>::mma(fa[a], fb[b], m2acc[a][b]);
         if ((w >> 1) == rr) m1_add(round, fb);  // m1 of this row over this wave's column tiles
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   }
   __syncthreads();
