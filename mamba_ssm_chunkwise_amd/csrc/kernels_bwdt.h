@@ -863,6 +863,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           cct += v * (float)xs[pl * KP + k];
         }
       }
+      // the second token half has the longer row work ahead of it: its waves get
+      // issue priority for the d_bhat work, the first half's fills in under their rows
+      if (tt == 1) __builtin_amdgcn_s_setprio(2);
       // ---- d_bhat[(j,c)][col] += sum_t L[t,j] xhat[(j,c)][p] G[t][col]; local ----
       float LB[KH][8];  // L[tslot(8q+e)][j of (j,c) = 16(kq*KH+kb)+n]
 #pragma unroll
@@ -958,6 +961,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();  // the last round's d_bhat reads are done
     flush_dx(nc, (nrounds - 1) * 4 - ((nrounds - 1) * 4) % XPB);
