@@ -178,36 +178,36 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
     if (wide) {
       wst.store(g, bsT, nullptr, xs, rt, tid);
     } else {
-    for (int idx = tid; idx < K * R; idx += NTT) {
-      const int k = idx / R, col = idx % R;
-      const int j = k / CK, ci = k % CK;
-      const int pos = nc * ELL + j;
-      bf16 v = (bf16)0.0f;
-      if (col < g.r && pos < g.V && ci < g.c)
-        v = bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, col)];
-      bsT[col * KP + k] = v;
-    }
-    if constexpr (ROT == 1) {
-      for (int idx = tid; idx < ELL * 8 * RT; idx += NTT) {
-        const int tk = idx / (8 * RT), a = idx % (8 * RT);
-        const int pos = nc * ELL + tk;
-        float th = 0.0f;
-        if (a < g.A && pos < g.V) th = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + a];
-        float sv, cv;
-        sincosf(th, &sv, &cv);
-        rt[tk * RTP + 2 * a] = cv;
-        rt[tk * RTP + 2 * a + 1] = sv;
+      for (int idx = tid; idx < K * R; idx += NTT) {
+        const int k = idx / R, col = idx % R;
+        const int j = k / CK, ci = k % CK;
+        const int pos = nc * ELL + j;
+        bf16 v = (bf16)0.0f;
+        if (col < g.r && pos < g.V && ci < g.c)
+          v = bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, col)];
+        bsT[col * KP + k] = v;
       }
-    } else if constexpr (ROT == 3) {
-      for (int idx = tid; idx < ELL * 16 * RT; idx += NTT) {
-        const int tk = idx / (16 * RT), e = idx % (16 * RT);
-        const int pos = nc * ELL + tk;
-        float v = (e & 3) == 0 ? 1.0f : 0.0f;
-        if ((e >> 2) < g.J && pos < g.V) v = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e];
-        rt[tk * RTP + e] = v;
+      if constexpr (ROT == 1) {
+        for (int idx = tid; idx < ELL * 8 * RT; idx += NTT) {
+          const int tk = idx / (8 * RT), a = idx % (8 * RT);
+          const int pos = nc * ELL + tk;
+          float th = 0.0f;
+          if (a < g.A && pos < g.V) th = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + a];
+          float sv, cv;
+          sincosf(th, &sv, &cv);
+          rt[tk * RTP + 2 * a] = cv;
+          rt[tk * RTP + 2 * a + 1] = sv;
+        }
+      } else if constexpr (ROT == 3) {
+        for (int idx = tid; idx < ELL * 16 * RT; idx += NTT) {
+          const int tk = idx / (16 * RT), e = idx % (16 * RT);
+          const int pos = nc * ELL + tk;
+          float v = (e & 3) == 0 ? 1.0f : 0.0f;
+          if ((e >> 2) < g.J && pos < g.V) v = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e];
+          rt[tk * RTP + e] = v;
+        }
       }
-    }
-    stage_x(nc, 0);
+      stage_x(nc, 0);
     }
     store_round(fetch_round(nc, 0), 0);
     __syncthreads();
