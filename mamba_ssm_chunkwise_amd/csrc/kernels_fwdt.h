@@ -146,22 +146,17 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   const bool wide = WS::usable(g);
   WS wst;
   float dav = 0.0f;
-  // the global loads of a chunk's inputs: issued for the next chunk a few
-  // rounds before the current one ends, which then covers their latency
+  // the global loads of a chunk's inputs, all issued before the first is used
   auto load_chunk = [&](int ncl) {
     dav = 0.0f;
     if (tid < 32 && ncl * ELL + tid < g.V) dav = (float)da[((size_t)bi * g.s + ncl * ELL + tid) * g.h + hi];
     if (wide) wst.load(g, xhat, bhat, rot, ncl, bi, hi, tid);
   };
-  constexpr int PFR = 3;  // rounds before the chunk's end at which the next chunk's loads go out
-  // not before the round that stages the chunk's last xhat block (that reuses the registers)
-  const int lxr = XPB / 4 * ((nrounds - 1) / (XPB / 4));
-  const int pfr = nrounds - PFR > lxr ? nrounds - PFR : lxr;
-  if (n1 > n0) load_chunk(n0);
   for (int nc = n0; nc < n1; nc++) {
     asm volatile("" : "+v"(tid));
+    load_chunk(nc);  // in flight while the waves meet at the barrier
     __syncthreads();
-    // ---- chunk staging (its global loads were issued during the previous chunk)
+    // ---- chunk staging
     if (tid < 64) {
       const int tk = tid & 31;
       float v = dav;
@@ -243,7 +238,6 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
         }
         __syncthreads();
       }
-      if (round == pfr && nc + 1 < n1) load_chunk(nc + 1);
       const int p = pr0 + u;
       bf16* Gsb = Gs + (size_t)(round & 1) * 4 * ELL * GTP;  // this round's c blocks
       const f4 pf = fetch_round(nc, pr0 + 4);
