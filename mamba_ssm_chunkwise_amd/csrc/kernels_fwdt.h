@@ -23,8 +23,7 @@ struct LdsF {
   static constexpr int R = 16 * NT, K = ELL * CK, KP = cf_pitch(K), GTP = R + 16;
   static constexpr size_t bsT = 0;                                    // bhat^T [col][(j,c)]
   static constexpr size_t xs = bsT + (size_t)R * KP * 2;              // xhat block [p][(j,c)]
-  static constexpr size_t LT = xs + (size_t)XPB * KP * 2;             // L^T [j][t]
-  static constexpr size_t a = LT + (size_t)ELL * LTP * 4;
+  static constexpr size_t a = xs + (size_t)XPB * KP * 2;
   static constexpr size_t d = a + ELL * 4;
   static constexpr size_t lw = d + ELL * 4;                           // W factors [LWE][64] float4
   // carry rows and c blocks of a round, double-buffered by round parity
@@ -51,7 +50,6 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* bsT = (bf16*)(smem + L::bsT);
   bf16* xs = (bf16*)(smem + L::xs);
-  float* LT = (float*)(smem + L::LT);
   float* s_a = (float*)(smem + L::a);
   float* s_d = (float*)(smem + L::d);
   f4* LWt = (f4*)(smem + L::lw);
@@ -206,19 +204,17 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
     }
     store_round(fetch_round(nc, 0), 0);
     __syncthreads();
-    for (int idx = tid; idx < ELL * ELL; idx += NTT) {
-      const int j = idx / ELL, tk = idx % ELL;
-      LT[j * LTP + tk] = (j <= tk) ? expf(s_a[tk] - s_a[j]) : 0.0f;
-    }
-    __syncthreads();
     const int tv = g.V - nc * ELL;  // valid tokens of this chunk (>= 1)
-    if (w < LWE) {  // W factor entry w (four of the flattened f = (h*CK+ks)*(8/CK)+v)
+    if (w < LWE) {
+      // W factor entry w: L[t][j] = exp(a_t - a_j) for j <= t (else 0) at the
+      // four flattened f = (h*CK+ks)*(8/CK)+v, t = 16h + n, j of slot 32ks+8q+v
       f4 v;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int f = 4 * w + i;
         const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), vv = rest % (8 / CK);
-        v[i] = LT[((32 * ks + 8 * q) / CK + vv) * LTP + 16 * hh + n];
+        const int j = (32 * ks + 8 * q) / CK + vv, tk = 16 * hh + n;
+        v[i] = (j <= tk) ? expf(s_a[tk] - s_a[j]) : 0.0f;
       }
       LWt[w * 64 + lane] = v;
     }
