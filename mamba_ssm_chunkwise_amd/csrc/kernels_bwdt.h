@@ -1005,6 +1005,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       if (n == 0) rwp[w * 16 + 4 * q + i] = r;
     }
     if (tid < 4 * K) csum[tid] = cct;
+    // (the d_da partials are scanned at the start of the next step of the walk,
+    // behind the barrier there, while the next chunk's loads are in flight)
     __syncthreads();
     if (d_bhat != nullptr) {
       if (wide && !g.half) {
@@ -1047,11 +1049,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
       }
     }
-    // the scan of these partials runs at the start of the next step of the walk,
-    // behind the barrier there, while the next chunk's loads are in flight
   }
   __syncthreads();
-  if (n1 > n0) dda_scan(n0);
+  if (n1 > n0) dda_scan(n0);  // the last chunk's d_da
 }
 
 }  // namespace mom
