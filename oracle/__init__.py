@@ -9,10 +9,11 @@ Two independent CPU implementations live here:
 * ``moments_oracle.c`` (fp64, threaded over (b,h) chains): the per-token
   recurrence the chunked method reaches exactly, with its own reverse-time
   matrix-form adjoint. It is the reference every GPU result is compared with.
-* ``pages_form.py`` (numpy fp64): a loop transcription of the pages' chunkwise
-  algebra (chunk decay, triangular chunk states, boundary carries, the reverse
-  chunk loop with G, d_W = L^T G and the rev-cumsum d_da identity). It exists to
-  pin the oracle: chunk-length invariance and the d_da identity.
+* ``chunk_form.py`` (numpy fp64): the chunkwise block form of the same
+  computation at any chunk length l, written from the equations with the chunks
+  as an array axis, and its adjoint with three forms of the decay gradient. It
+  exists to pin the oracle: chunk-length invariance (including the oracle's
+  checkpointed backward over several 256-token segments) and the d_da identity.
 
 Parity pins (see ``tests/test_oracle_pins.py``): finite differences, torch
 float64 autograd, chunk-length invariance, the rotation-orthogonality trace

@@ -12,7 +12,7 @@ import torch
 
 import workloads as W
 from oracle import ROT_HALF, ROT_NONE, ROT_PAIRWISE, ROT_QUAT, oracle_bwd, oracle_fwd
-from oracle import pages_form as pf
+from oracle import chunk_form as cf
 
 
 def _np(t):
@@ -52,17 +52,17 @@ MODES = [(ROT_PAIRWISE, 12), (ROT_HALF, 12), (ROT_QUAT, 12), (ROT_NONE, 12)]
 @pytest.mark.parametrize("rot_kind,r", MODES)
 @pytest.mark.parametrize("l", [1, 2, 4, 8, 20, 40])
 def test_chunk_length_invariance(rot_kind, r, l):
-    """The pages' chunkwise forward and recompute backward, at any chunk length,
-    equal the per-token recurrence (backward.rs, "Gradient math": d_t and L[t,j]
-    are products of exp(da) over the tokens in between)."""
+    """The chunkwise block form (forward and its adjoint), at any chunk length,
+    equals the per-token recurrence ("backward.rs", "Gradient math": d_t and
+    L[t,j] are products of exp(da) over the tokens in between)."""
     w, a = _case(rot_kind, r=r, valid_len=37)
     m2, m1 = _fwd(w, a)
-    q2, q1 = pf.moments_fwd(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], w.valid_len,
-                            w.rot_kind, w.rope_dim, l)
+    q2, q1 = cf.moments_fwd_chunked(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], w.valid_len,
+                                    w.rot_kind, w.rope_dim, l)
     assert _rel(q2, m2) < 1e-12 and _rel(q1, m1) < 1e-12
     go = _bwd(w, a)
-    gp = pf.moments_bwd(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], a["d_m2"], a["d_m1"],
-                        w.valid_len, w.rot_kind, w.rope_dim, l)
+    gp = cf.moments_bwd_chunked(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], a["d_m2"], a["d_m1"],
+                                w.valid_len, w.rot_kind, w.rope_dim, l)
     for k, v in go.items():
         if v is not None:
             assert _rel(gp[k], v) < 1e-11, k
@@ -70,17 +70,52 @@ def test_chunk_length_invariance(rot_kind, r, l):
 
 @pytest.mark.parametrize("rot_kind,r", MODES[:3])
 def test_dda_identity_brute_force(rot_kind, r):
-    """backward.rs, "Gradient math": sum_{t>=s} scal_t + sum_{j<s<=t} A[t,j] equals
-    rev_cumsum(scal + rowsum A) - rev_cumsum(colsum A); both equal the
-    recurrence's exp(da_t) <dH_t, H_{t-1}>."""
+    """"backward.rs", "Gradient math": sum_{t>=s} scal_t + sum_{j<s<=t} A[t,j]
+    (brute force) equals rev_cumsum(scal + rowsum A) - rev_cumsum(colsum A), and
+    the log-decay cotangent form; all equal the recurrence's exp(da_t) <dH_t, H_{t-1}>."""
     w, a = _case(rot_kind, r=r, s=24, valid_len=21)
     args = (a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], a["d_m2"], a["d_m1"], w.valid_len,
             w.rot_kind, w.rope_dim, 8)
-    gi = pf.moments_bwd(*args, dda_form="identity")
-    gd = pf.moments_bwd(*args, dda_form="double_sum")
+    gi = cf.moments_bwd_chunked(*args, dda="identity")
+    gd = cf.moments_bwd_chunked(*args, dda="double_sum")
+    gl = cf.moments_bwd_chunked(*args, dda="log")
     go = _bwd(w, a)
     assert _rel(gi["d_da"], gd["d_da"]) < 1e-12
+    assert _rel(gl["d_da"], gd["d_da"]) < 1e-12
     assert _rel(go["d_da"], gd["d_da"]) < 1e-12
+
+
+CKPT_CASES = [
+    dict(rot_kind=ROT_PAIRWISE, r=8, rope_dim=6),
+    dict(rot_kind=ROT_HALF, r=8, rope_dim=8),
+    dict(rot_kind=ROT_QUAT, r=8, quat_blocks=2),
+    dict(rot_kind=ROT_NONE, r=8),
+]
+
+
+@pytest.mark.parametrize("kw", CKPT_CASES)
+def test_backward_across_checkpoint_segments(kw):
+    """The oracle's backward replays the states from checkpoints every 256 tokens:
+    at V = 577 it walks three segments (the last one partial). Its gradients equal
+    the block form's adjoint at l = 1, 8 and 24 (no checkpoints there), and central
+    differences along random directions."""
+    w, a = _case(s=600, valid_len=577, p=3, c=2, h=1, seed=9, **kw)
+    go = _bwd(w, a)
+    for l in (1, 8, 24):
+        gp = cf.moments_bwd_chunked(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], a["d_m2"],
+                                    a["d_m1"], w.valid_len, w.rot_kind, w.rope_dim, l)
+        for k, v in go.items():
+            if v is not None:
+                assert _rel(gp[k], v) < 1e-10, (l, k)
+    rng = np.random.default_rng(13)
+    eps = 1e-6
+    for name in ("xhat", "bhat", "da", "rot", "h0"):
+        if a[name] is None or go["d_" + name] is None:
+            continue
+        v = rng.standard_normal(a[name].shape)
+        fd = (_objective(w, a, {name: a[name] + eps * v}) - _objective(w, a, {name: a[name] - eps * v})) / (2 * eps)
+        an = (go["d_" + name] * v).sum()
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
 
 
 # ---------------------------------------------------------------- rotation invariants
@@ -196,8 +231,8 @@ def test_pooled_m1_form():
     d_m1 expanded over per_head_dim)."""
     w, a = _case(ROT_PAIRWISE)
     _, m1 = _fwd(w, a)
-    q2, q1 = pf.moments_fwd(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], w.valid_len,
-                            w.rot_kind, w.rope_dim, 8)
+    q2, q1 = cf.moments_fwd_chunked(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], w.valid_len,
+                                    w.rot_kind, w.rope_dim, 8)
     assert _rel(m1.sum(2), q1.sum(2)) < 1e-12
     pooled = np.random.default_rng(0).standard_normal((w.b, w.h, w.r))
     a["d_m1"] = np.broadcast_to(pooled[:, :, None, :], a["d_m1"].shape).copy()
