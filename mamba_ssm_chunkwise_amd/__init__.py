@@ -41,9 +41,65 @@ def moments_workspace_size(desc: Desc, is_bwd: bool) -> int:
 def _ptr(t):
     if t is None:
         return None
-    if not t.is_cuda or not t.is_contiguous():
-        raise ValueError("tensors must be contiguous device tensors")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _expect(name, t, shape, dtype, device, optional=False):
+    """Raises ValueError unless t is a contiguous tensor of exactly this shape and
+    dtype on this device (the kernels index every buffer from the descriptor)."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, the descriptor needs {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, the descriptor needs {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _input_specs(desc: Desc):
+    """Expected shapes and dtype of the five inputs (rot: None when there is no rotation)."""
+    b, s, c, h, p, r = desc.b, desc.s, desc.c, desc.h, desc.p, desc.r
+    if desc.rot_kind in (ROT_PAIRWISE, ROT_HALF):
+        rot = (b, s, h, desc.rope_dim // 2)
+    elif desc.rot_kind == ROT_QUAT:
+        rot = (b, s, h, desc.quat_blocks, 4)
+    else:
+        rot = None
+    dt = torch.bfloat16 if desc.dtype == BF16 else torch.float32
+    return {"xhat": (b, s, c, h, p), "bhat": (b, s, c, h, r), "da": (b, s, h), "rot": rot,
+            "h0": (b, h, p, r)}, dt
+
+
+def _check_inputs(desc: Desc, xhat, bhat, da, rot, h0):
+    """Shapes, dtypes and devices of the inputs against the descriptor (all on
+    xhat's device, which must be a GPU)."""
+    if not isinstance(xhat, torch.Tensor):
+        raise ValueError("xhat must be a torch.Tensor")
+    dev = xhat.device
+    specs, dt = _input_specs(desc)
+    _expect("xhat", xhat, specs["xhat"], dt, dev)
+    _expect("bhat", bhat, specs["bhat"], dt, dev)
+    _expect("da", da, specs["da"], dt, dev)
+    if specs["rot"] is None:
+        if rot is not None:
+            raise ValueError("rot must be None when the descriptor has no rotation")
+    else:
+        _expect("rot", rot, specs["rot"], dt, dev)
+    _expect("h0", h0, specs["h0"], dt, dev, optional=True)
+    return dev, specs, dt
+
+
+def _require_gpu(dev):
+    if dev.type != "cuda":
+        raise ValueError(f"the inputs are on {dev}; the kernels need GPU tensors")
+    _lib.load()
 
 
 def _stream(device):
@@ -52,21 +108,30 @@ def _stream(device):
 
 def _workspace(desc, is_bwd, device, workspace):
     n = moments_workspace_size(desc, is_bwd)
-    if workspace is None or workspace.numel() < n:
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    if workspace is None:
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if workspace.numel() * workspace.element_size() < n:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"the descriptor needs {n}")
     return workspace
 
 
 def moments_fwd(desc: Desc, xhat, bhat, da, rot, h0, m2=None, m1=None, workspace=None):
     """Returns (m2 [b,h,r,r], m1 [b,h,p,r]) float32."""
-    dev = xhat.device
+    dev, _, _ = _check_inputs(desc, xhat, bhat, da, rot, h0)
+    _expect("m2", m2, (desc.b, desc.h, desc.r, desc.r), torch.float32, dev, optional=True)
+    _expect("m1", m1, (desc.b, desc.h, desc.p, desc.r), torch.float32, dev, optional=True)
+    _require_gpu(dev)
     if m2 is None:
         m2 = torch.empty(desc.b, desc.h, desc.r, desc.r, dtype=torch.float32, device=dev)
     if m1 is None:
         m1 = torch.empty(desc.b, desc.h, desc.p, desc.r, dtype=torch.float32, device=dev)
     ws = _workspace(desc, False, dev, workspace)
     rc = _lib.load().moments_fwd(ctypes.byref(desc), _ptr(xhat), _ptr(bhat), _ptr(da), _ptr(rot),
-                                 _ptr(h0), _ptr(m2), _ptr(m1), _ptr(ws), ws.numel(), _stream(dev))
+                                 _ptr(h0), _ptr(m2), _ptr(m1), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(dev))
     _lib.check(rc)
     return m2, m1
 
@@ -75,24 +140,26 @@ def moments_bwd(desc: Desc, xhat, bhat, da, rot, h0, d_m2, d_m1, want=("xhat", "
                 out=None, workspace=None):
     """Returns dict d_xhat, d_bhat, d_da, d_rot, d_h0 (input dtype; None when
     not wanted or not defined)."""
-    dev = xhat.device
-    dt = xhat.dtype
+    dev, specs, dt = _check_inputs(desc, xhat, bhat, da, rot, h0)
+    _expect("d_m2", d_m2, (desc.b, desc.h, desc.r, desc.r), torch.float32, dev)
+    _expect("d_m1", d_m1, (desc.b, desc.h, desc.p, desc.r), torch.float32, dev)
     out = dict(out or {})
-    shapes = {"xhat": xhat.shape, "bhat": bhat.shape, "da": da.shape,
-              "rot": None if rot is None else rot.shape,
-              "h0": (desc.b, desc.h, desc.p, desc.r)}
     for k in ("xhat", "bhat", "da", "rot", "h0"):
         key = "d_" + k
-        if k in want and shapes[k] is not None and not (k == "rot" and desc.rot_kind == ROT_NONE):
-            if out.get(key) is None:
-                out[key] = torch.empty(shapes[k], dtype=dt, device=dev)
+        if k in want and specs[k] is not None:
+            _expect(key, out.get(key), specs[k], dt, dev, optional=True)
         else:
             out[key] = None
+    _require_gpu(dev)
+    for k in ("xhat", "bhat", "da", "rot", "h0"):
+        key = "d_" + k
+        if k in want and specs[k] is not None and out.get(key) is None:
+            out[key] = torch.empty(specs[k], dtype=dt, device=dev)
     ws = _workspace(desc, True, dev, workspace)
     rc = _lib.load().moments_bwd(ctypes.byref(desc), _ptr(xhat), _ptr(bhat), _ptr(da), _ptr(rot),
                                  _ptr(h0), _ptr(d_m2), _ptr(d_m1), _ptr(out["d_xhat"]),
                                  _ptr(out["d_bhat"]), _ptr(out["d_da"]), _ptr(out["d_rot"]),
-                                 _ptr(out["d_h0"]), _ptr(ws), ws.numel(), _stream(dev))
+                                 _ptr(out["d_h0"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _lib.check(rc)
     return out
 

@@ -86,3 +86,70 @@ def test_null_and_workspace_errors_without_gpu():
     rc = lib.moments_bwd(ctypes.byref(dn), fake, fake, fake, null, null, fake, fake, fake, fake, fake,
                          fake, fake, fake, 1 << 40, null)
     assert rc == _lib.EINVAL  # d_rot given without a rotation
+
+
+# ---------------------------------------------------------------- binding argument checks
+def _tensors(d, dtype=None):
+    import torch
+    dt = dtype or (torch.bfloat16 if d.dtype == M.BF16 else torch.float32)
+    t = {"xhat": torch.zeros(d.b, d.s, d.c, d.h, d.p, dtype=dt),
+         "bhat": torch.zeros(d.b, d.s, d.c, d.h, d.r, dtype=dt),
+         "da": torch.zeros(d.b, d.s, d.h, dtype=dt),
+         "rot": torch.zeros(d.b, d.s, d.h, d.rope_dim // 2, dtype=dt),
+         "h0": torch.zeros(d.b, d.h, d.p, d.r, dtype=dt),
+         "d_m2": torch.zeros(d.b, d.h, d.r, d.r), "d_m1": torch.zeros(d.b, d.h, d.p, d.r)}
+    return t
+
+
+def _call(kind, d, t):
+    if kind == "fwd":
+        return M.moments_fwd(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"])
+    return M.moments_bwd(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], t["d_m2"], t["d_m1"])
+
+
+@pytest.mark.parametrize("kind", ["fwd", "bwd"])
+@pytest.mark.parametrize("bad,match", [
+    (dict(xhat=(2, 64, 2, 3, 9)), "xhat has shape"),
+    (dict(bhat=(2, 64, 2, 3, 8)), "bhat has shape"),
+    (dict(da=(2, 64, 1)), "da has shape"),
+    (dict(rot=(2, 64, 3, 3)), "rot has shape"),
+    (dict(h0=(2, 3, 8)), "h0 has shape"),
+])
+def test_binding_rejects_mismatched_shapes(kind, bad, match):
+    """Every tensor is checked against the descriptor before the C ABI is called:
+    a mismatched buffer would make the kernels read or write out of bounds."""
+    import torch
+    d = _desc()
+    t = _tensors(d)
+    for k, shape in bad.items():
+        t[k] = torch.zeros(shape, dtype=t[k].dtype)
+    with pytest.raises(ValueError, match=match):
+        _call(kind, d, t)
+
+
+def test_binding_rejects_dtypes_devices_and_pooled_cotangent():
+    import torch
+    d = _desc(dtype=M.BF16)
+    t = _tensors(d, dtype=torch.float32)          # fp32 tensors with a bf16 descriptor
+    with pytest.raises(ValueError, match="dtype"):
+        _call("fwd", d, t)
+    t = _tensors(d)
+    t["d_m1"] = torch.zeros(d.b, d.h, d.r)        # the pages' pooled [b,h,r] cotangent
+    with pytest.raises(ValueError, match="d_m1 has shape"):
+        _call("bwd", d, t)
+    t = _tensors(d)
+    t["d_m2"] = t["d_m2"].to(torch.float64)
+    with pytest.raises(ValueError, match="d_m2 has dtype"):
+        _call("bwd", d, t)
+    t = _tensors(d)
+    t["rot"] = t["rot"].transpose(0, 1).contiguous().transpose(0, 1)   # right shape, not contiguous
+    with pytest.raises(ValueError, match="contiguous"):
+        _call("fwd", d, t)
+    dn = _desc(rot_kind=M.ROT_NONE, rope_dim=0)
+    t = _tensors(dn)
+    t["rot"] = torch.zeros(2, 64, 3, 1)
+    with pytest.raises(ValueError, match="no rotation"):
+        _call("fwd", dn, t)
+    t = _tensors(d)                                # everything right, but on the host
+    with pytest.raises(ValueError, match="GPU"):
+        _call("bwd", d, t)
