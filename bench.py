@@ -19,29 +19,30 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-ELL = 32                     # tokens per kernel chunk
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3      # MI355X fp32 MFMA / vector
 PEAK_HBM_GBS = 8000.0
 
 
-def algorithmic(w):
+def algorithmic(w, ell, l=None):
     """Algorithmic flops and HBM bytes per launch of each kernel, counted as the
-    method's contractions over the causal triangle with the caller's chunk
-    length l (per token-head: states c*p*r*(l+1), m2 and d_c 2*p*r^2 each,
-    d_W and <G, W> p*r*(l+1) each). Bytes count every input read once and every
-    output written once; the fp32 carries are the implementation's own extra
-    (p*r*4 per 32-token kernel chunk, written by the carry pass and read back)."""
+    method's contractions over the causal triangle at chunk length l (the
+    caller's chunk_len by default; per token-head: states c*p*r*(l+1), m2 and d_c
+    2*p*r^2 each, d_W and <G, W> p*r*(l+1) each). Bytes count every input read
+    once and every output written once; the fp32 carries are the implementation's
+    own extra (p*r*4 per kernel chunk of ell tokens, written by the carry pass and
+    read back)."""
     V = min(w.valid_len, w.s)
     th = w.b * V * w.h                         # token-heads
-    p, r, c, l = w.p, w.r, w.c, w.chunk_len
+    p, r, c = w.p, w.r, w.c
+    l = w.chunk_len if l is None else l
     e = 2 if w.dtype == "bf16" else 4
     states = c * p * r * (l + 1)
     gram = 2 * p * r * r
     dw = p * r * (l + 1)
     rw = w.rot_width
     tok_in = (c * p + c * r + 1 + rw) * e          # xhat, bhat, da, rot per token-head
-    nk = -(-V // ELL)
+    nk = -(-V // ell)
     carry_b = w.b * w.h * nk * p * r * 4          # one fp32 carry per kernel chunk
     small = w.b * w.h * (2 * p * r + r * r) * 4   # h0 in, m2/m1 out or d_m2/d_m1 in, d_h0 out
     fwd_b = th * tok_in + small
@@ -91,38 +92,44 @@ def stored_traffic(kernel, workload):
         return None
 
 
-def cpu_baseline(w, seconds_hint=15.0):
-    """The oracle (as it stands) on a bounded sample: whole (b,h) chains of the
-    workload's shapes over its valid length, fwd + bwd, all host cores; the number
-    of chains is a multiple of the thread count chosen for about seconds_hint of
-    work. Workload tokens/s = (chains * T / h) / time (a token carries h chains)."""
-    import torch
-
-    import workloads as W
+def cpu_baseline(w, t, seconds_hint=15.0):
+    """The oracle (as it stands) on a bounded sample of the workload's own draw:
+    the first k (b,h) chains of the tensors the GPU runs on, whole valid length,
+    fwd + bwd in fp64 on all host cores, k a multiple of the thread count chosen
+    for about seconds_hint of work; plus one chain on a single thread over a
+    prefix of the sequence. Workload tokens/s = (chains * V / h) / time (a token
+    of the workload carries h chains)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle import oracle_bwd, oracle_fwd
     from oracle.oracle import default_threads
+    from parity_util import sub_chains
 
     nt = default_threads()
-    T = min(w.valid_len, w.s)
+    V = min(w.valid_len, w.s)
 
-    def run(nch, Tn):
-        ws = w.replace(b=1, h=nch, s=Tn, valid_len=Tn, chunk_len=1, seed=w.seed + 17)
-        t = {k: (None if v is None else v.double().numpy()) for k, v in W.generate(ws, device="cpu").items()}
+    def run(nch, T, threads):
+        sub = sub_chains(t, list(range(nch)), w.h)
+        a = {k: (None if v is None else v[:, :T].double().cpu().numpy() if k in ("xhat", "bhat", "da", "rot")
+                 else v.double().cpu().numpy()) for k, v in sub.items()}
         t0 = time.perf_counter()
-        oracle_fwd(t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], Tn, w.rot_kind, w.rope_dim, nthreads=nt)
-        oracle_bwd(t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], t["d_m2"], t["d_m1"], Tn, w.rot_kind,
-                   w.rope_dim, nthreads=nt)
+        oracle_fwd(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], T, w.rot_kind, w.rope_dim,
+                   nthreads=threads)
+        oracle_bwd(a["xhat"], a["bhat"], a["da"], a["rot"], a["h0"], a["d_m2"], a["d_m1"], T, w.rot_kind,
+                   w.rope_dim, nthreads=threads)
         return time.perf_counter() - t0
-    Tp = min(T, 256)
-    dt = run(nt, Tp)                                  # calibration on a short prefix
-    per_round = dt * T / Tp                           # nt chains of T tokens
+    T1 = min(V, 512)
+    dt1 = run(1, T1, 1)                               # one chain, one thread, a prefix
+    single = T1 / w.h / dt1
+    per_round = dt1 * V / T1                          # about nt chains of V tokens on nt threads
     k = int(max(1, min(64, round(seconds_hint / max(per_round, 1e-3)))))
-    nch = nt * k
-    dt = run(nch, T)
-    rate = nch * T / w.h / dt
+    nch = min(nt * k, w.b * w.h)
+    dt = run(nch, V, nt)
+    rate = nch * V / w.h / dt
     return {"value": rate, "unit": "tokens/s", "cores": nt, "kind": "oracle",
-            "sample": f"{nch} (b,h) chains x {T} tokens of {w.name} shapes (p={w.p}, r={w.r}, c={w.c}), "
-                      f"fwd+bwd fp64 on {nt} threads, {dt:.1f} s; tokens/s = chains*tokens/h/time"}
+            "single_thread_value": single,
+            "sample": f"the first {nch} (b,h) chains of the {w.name} draw, {V} tokens each, fwd+bwd fp64 on "
+                      f"{nt} threads in {dt:.1f} s; single thread: 1 chain x {T1} tokens in {dt1:.2f} s; "
+                      f"tokens/s = chains*tokens/h/time"}
 
 
 def main():
@@ -186,7 +193,9 @@ def main():
     tokens = w.b * V
     value = tokens / (ms / 1e3)
 
-    alg = algorithmic(w)
+    ell = M.kernel_chunk_len()
+    alg = algorithmic(w, ell)
+    alg_k = algorithmic(w, ell, l=ell)          # the same contractions at the kernels' chunk length
     # per-kernel names as the library reports them (the transposed bf16 kernels
     # report under the same names as the general ones)
     per_kernel = {k: (n, tot / max(n, 1)) for k, (n, tot) in prof.items() if n > 0}
@@ -198,9 +207,13 @@ def main():
     if a["flops"] > 0:
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
         achieved = a["flops"] / (avg_ms / 1e3) / 1e12
+        ak = alg_k[dom]["flops"] / (avg_ms / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kname,
-                "avg_ms": round(avg_ms, 4)}
+                "avg_ms": round(avg_ms, 4),
+                "count": f"method contractions over the causal triangle at the caller's chunk length l={w.chunk_len}",
+                "at_kernel_chunk": {"l": ell, "flops": alg_k[dom]["flops"], "achieved": round(ak, 2),
+                                    "frac": round(ak / peak, 4)}}
     else:
         achieved = a["bytes"] / (avg_ms / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -210,8 +223,12 @@ def main():
     st = alg["step"]
     pk = (PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS) * 1e12
     t_roof = max(st["flops"] / pk, st["bytes"] / (PEAK_HBM_GBS * 1e9))
+    stk = alg_k["step"]
+    t_roof_k = max(stk["flops"] / pk, stk["bytes"] / (PEAK_HBM_GBS * 1e9))
     step_roof = {"flops": st["flops"], "bytes": st["bytes"], "roofline_ms": round(t_roof * 1e3, 3),
-                 "frac": round(t_roof * 1e3 / ms, 4)}
+                 "frac": round(t_roof * 1e3 / ms, 4),
+                 "at_kernel_chunk": {"l": ell, "flops": stk["flops"], "roofline_ms": round(t_roof_k * 1e3, 3),
+                                     "frac": round(t_roof_k * 1e3 / ms, 4)}}
     for k, (n, avg) in sorted(per_kernel.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
         fl = alg.get(k, {}).get("flops", 0)
         by = alg.get(k, {}).get("bytes", 0)
@@ -230,7 +247,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w)
+        cpu = cpu_baseline(w, t)
 
     out = {
         "metric": "moments fwd+bwd tokens/sec on 1 MI355X; % MFMA/HBM roofline",

@@ -107,6 +107,13 @@ int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, co
 const char* moments_strerror(int code);
 int moments_last_hip_error(void);
 
+/* Tokens per kernel chunk. The kernels split every chain into chunks of this
+ * many tokens whatever desc->chunk_len is: the chunked states equal the per-token
+ * recurrence at any chunk length ("backward.rs" page, module doc "Gradient
+ * math": the decays are products of exp(da) over the tokens in between), so
+ * only the rounding differs. Host-only. */
+int64_t moments_kernel_chunk_len(void);
+
 /* Diagnostics: per-kernel timing. While enabled (on != 0), each kernel launch
  * of moments_fwd / moments_bwd is bracketed by two HIP events recorded on the
  * caller's stream (the stream the kernel runs on); disabled by default.

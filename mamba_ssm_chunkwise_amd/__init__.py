@@ -15,6 +15,7 @@ from ._lib import (BF16, F32, ROT_HALF, ROT_NONE, ROT_PAIRWISE, ROT_QUAT, Desc, 
                    MomentsError)
 
 __all__ = ["make_desc", "moments_validate", "moments_workspace_size", "moments_fwd", "moments_bwd",
+           "kernel_chunk_len",
            "Desc", "MomentsError", "ROT_NONE", "ROT_PAIRWISE", "ROT_HALF", "ROT_QUAT"]
 
 
@@ -162,6 +163,11 @@ def moments_bwd(desc: Desc, xhat, bhat, da, rot, h0, d_m2, d_m1, want=("xhat", "
                                  _ptr(out["d_h0"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _lib.check(rc)
     return out
+
+
+def kernel_chunk_len() -> int:
+    """Tokens per kernel chunk (the kernels' own chunking, whatever chunk_len is)."""
+    return int(_lib.load().moments_kernel_chunk_len())
 
 
 def profile_enable(on: bool) -> bool:

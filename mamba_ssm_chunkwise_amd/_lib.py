@@ -17,8 +17,8 @@ F32, BF16 = 0, 1
 ROT_NONE, ROT_PAIRWISE, ROT_HALF, ROT_QUAT = 0, 1, 2, 3
 
 EXPORTS = ("moments_validate", "moments_workspace_size", "moments_fwd", "moments_bwd",
-           "moments_strerror", "moments_last_hip_error", "moments_profile_enable",
-           "moments_profile_read", "moments_profile_reset")
+           "moments_strerror", "moments_last_hip_error", "moments_kernel_chunk_len",
+           "moments_profile_enable", "moments_profile_read", "moments_profile_reset")
 
 
 class Desc(ctypes.Structure):
@@ -60,6 +60,8 @@ def load():
         lib.moments_strerror.restype = ctypes.c_char_p
         lib.moments_last_hip_error.argtypes = []
         lib.moments_last_hip_error.restype = ctypes.c_int
+        lib.moments_kernel_chunk_len.argtypes = []
+        lib.moments_kernel_chunk_len.restype = ctypes.c_int64
         lib.moments_profile_enable.argtypes = [ctypes.c_int]
         lib.moments_profile_enable.restype = ctypes.c_int
         lib.moments_profile_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),

@@ -548,6 +548,8 @@ const char* moments_strerror(int code) {
 
 int moments_last_hip_error(void) { return g_last_hip.load(); }
 
+int64_t moments_kernel_chunk_len(void) { return ELL; }
+
 int moments_profile_enable(int on) {
   Prof& P = prof();
   std::lock_guard<std::mutex> g(P.mu);

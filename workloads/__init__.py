@@ -46,7 +46,8 @@ class Workload:
     quat_blocks: int = 0  # quaternion mode: J
     angle_step: float = 0.05   # increments U(-angle_step, angle_step)
     quat_sd: float = 0.05      # axis-angle standard deviation
-    da_mu: float = -1.0        # da = -softplus(N(da_mu, 1))
+    da_mu: float = -1.0        # da = -softplus(N(da_mu, 1)) + da_shift
+    da_shift: float = 0.0
     h0_sd: Optional[float] = 0.1  # None -> h0 is absent (zero initial state)
     seed: int = 1000
 
@@ -122,7 +123,7 @@ def generate(w: Workload, device="cpu", with_cotangents=True):
     inv = 1.0 / math.sqrt(w.r)
     out["xhat"] = (torch.randn(w.b, w.s, w.c, w.h, w.p, **f32) * inv).to(dt)
     out["bhat"] = (torch.randn(w.b, w.s, w.c, w.h, w.r, **f32) * inv).to(dt)
-    out["da"] = (-torch.nn.functional.softplus(torch.randn(w.b, w.s, w.h, **f32) + w.da_mu)).to(dt)
+    out["da"] = (w.da_shift - torch.nn.functional.softplus(torch.randn(w.b, w.s, w.h, **f32) + w.da_mu)).to(dt)
     if w.rot_kind in (ROT_PAIRWISE, ROT_HALF):
         a = w.rope_dim // 2
         inc = (torch.rand(w.b, w.s, w.h, a, **f32) * 2.0 - 1.0) * w.angle_step
@@ -146,9 +147,9 @@ def generate(w: Workload, device="cpu", with_cotangents=True):
 
 def small(name, dtype="f32", b=1, s=48, c=2, h=2, p=24, r=40, chunk_len=16, valid_len=None,
           rot_kind=ROT_PAIRWISE, rope_dim=16, quat_blocks=0, seed=7, h0_sd=0.1, da_mu=-0.5,
-          angle_step=0.3, quat_sd=0.3):
+          angle_step=0.3, quat_sd=0.3, da_shift=0.0):
     """A small workload for tests (odd sizes, ragged tails)."""
     return Workload(name, dtype, b=b, s=s, c=c, h=h, p=p, r=r, chunk_len=chunk_len,
                     valid_len=s if valid_len is None else valid_len, rot_kind=rot_kind,
                     rope_dim=rope_dim, quat_blocks=quat_blocks, angle_step=angle_step,
-                    quat_sd=quat_sd, da_mu=da_mu, h0_sd=h0_sd, seed=seed)
+                    quat_sd=quat_sd, da_mu=da_mu, da_shift=da_shift, h0_sd=h0_sd, seed=seed)
