@@ -59,7 +59,8 @@ enum {
   MOMENTS_EINVAL = -1,     /* bad descriptor, NULL required pointer, misalignment */
   MOMENTS_ENOTSUP = -2,    /* shape outside what the compiled kernels cover */
   MOMENTS_EWORKSPACE = -3, /* workspace_bytes below moments_workspace_size() */
-  MOMENTS_EHIP = -4        /* a HIP launch or runtime call failed */
+  MOMENTS_EHIP = -4,       /* a HIP launch or runtime call failed */
+  MOMENTS_ESCRATCH = -5    /* moments_fwd_static: the problem needs more scratch than it has */
 };
 
 typedef enum { MOMENTS_F32 = 0, MOMENTS_BF16 = 1 } moments_dtype;
@@ -95,6 +96,22 @@ int64_t moments_workspace_size(const moments_desc* desc, int is_bwd);
 int moments_fwd(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
                 const void* rot, const void* h0, float* m2, float* m1, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* Allocation-free forward, for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same operation, arguments and results as moments_fwd,
+ * but the kernels' scratch (boundary carries and per-workgroup partial moments)
+ * lives in a static device array of MOMENTS_STATIC_SCRATCH_BYTES (64 MiB), one
+ * copy per GPU, held until the process ends. Calls no hipMalloc, hipFree or
+ * allocating library routine. Problems whose forward workspace
+ * (moments_workspace_size(desc, 0)) exceeds that size return MOMENTS_ESCRATCH
+ * without launching anything. Every call on one GPU shares that GPU's array, so
+ * calls that overlap on one GPU (concurrent streams or host threads) race; calls
+ * ordered on one stream are safe. The first call on a device looks up the
+ * array's address there. With per-kernel timing enabled it creates HIP events. */
+#define MOMENTS_STATIC_SCRATCH_BYTES (64ull << 20)
+int moments_fwd_static(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                       const void* rot, const void* h0, float* m2, float* m1, void* stream);
 
 /* Backward: the VJP of (m2, m1) with cotangents d_m2 [b,h,r,r] (need not be
  * symmetric; only d_m2 + d_m2^T enters) and d_m1 [b,h,p,r]. Any gradient

@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import (BF16, F32, ROT_HALF, ROT_NONE, ROT_PAIRWISE, ROT_QUAT, Desc,  # noqa: F401
                    MomentsError)
 
-__all__ = ["make_desc", "moments_validate", "moments_workspace_size", "moments_fwd", "moments_bwd",
+__all__ = ["make_desc", "moments_validate", "moments_workspace_size", "moments_fwd", "moments_fwd_static",
+           "moments_bwd",
            "kernel_chunk_len",
            "Desc", "MomentsError", "ROT_NONE", "ROT_PAIRWISE", "ROT_HALF", "ROT_QUAT"]
 
@@ -133,6 +134,20 @@ def moments_fwd(desc: Desc, xhat, bhat, da, rot, h0, m2=None, m1=None, workspace
     rc = _lib.load().moments_fwd(ctypes.byref(desc), _ptr(xhat), _ptr(bhat), _ptr(da), _ptr(rot),
                                  _ptr(h0), _ptr(m2), _ptr(m1), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(dev))
+    _lib.check(rc)
+    return m2, m1
+
+
+def moments_fwd_static(desc: Desc, xhat, bhat, da, rot, h0, m2, m1):
+    """moments_fwd without a workspace: the library's static device scratch
+    (64 MiB per GPU) holds the kernels' intermediates. m2 and m1 are the
+    caller's float32 output tensors; nothing is allocated here."""
+    dev, _, _ = _check_inputs(desc, xhat, bhat, da, rot, h0)
+    _expect("m2", m2, (desc.b, desc.h, desc.r, desc.r), torch.float32, dev)
+    _expect("m1", m1, (desc.b, desc.h, desc.p, desc.r), torch.float32, dev)
+    _require_gpu(dev)
+    rc = _lib.load().moments_fwd_static(ctypes.byref(desc), _ptr(xhat), _ptr(bhat), _ptr(da), _ptr(rot),
+                                        _ptr(h0), _ptr(m2), _ptr(m1), _stream(dev))
     _lib.check(rc)
     return m2, m1
 

@@ -12,11 +12,12 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_build", "libmoments.so")
 
-OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5
+STATIC_SCRATCH_BYTES = 64 << 20
 F32, BF16 = 0, 1
 ROT_NONE, ROT_PAIRWISE, ROT_HALF, ROT_QUAT = 0, 1, 2, 3
 
-EXPORTS = ("moments_validate", "moments_workspace_size", "moments_fwd", "moments_bwd",
+EXPORTS = ("moments_validate", "moments_workspace_size", "moments_fwd", "moments_fwd_static", "moments_bwd",
            "moments_strerror", "moments_last_hip_error", "moments_kernel_chunk_len",
            "moments_profile_enable", "moments_profile_read", "moments_profile_reset")
 
@@ -54,6 +55,8 @@ def load():
         lib.moments_workspace_size.restype = ctypes.c_int64
         lib.moments_fwd.argtypes = [dp] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
         lib.moments_fwd.restype = ctypes.c_int
+        lib.moments_fwd_static.argtypes = [dp] + [vp] * 7 + [vp]
+        lib.moments_fwd_static.restype = ctypes.c_int
         lib.moments_bwd.argtypes = [dp] + [vp] * 12 + [vp, ctypes.c_size_t, vp]
         lib.moments_bwd.restype = ctypes.c_int
         lib.moments_strerror.argtypes = [ctypes.c_int]

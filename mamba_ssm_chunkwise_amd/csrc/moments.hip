@@ -16,6 +16,12 @@
 
 using namespace mom;
 
+// Device scratch of the allocation-free forward (moments_fwd_static): one copy
+// per GPU, alive until the process ends. Host code never passes this name to a
+// kernel or a copy; it uses the address hipGetSymbolAddress returns for the
+// current device (static_scratch below).
+__device__ __align__(256) unsigned char scratch[MOMENTS_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 std::atomic<int> g_last_hip{0};
@@ -477,6 +483,31 @@ int with_variant(const Plan& P, F&& f) {
   return MOMENTS_ENOTSUP;
 }
 
+// Address of this device's copy of `scratch`, looked up once per device with
+// that device current; nullptr (and the HIP error recorded) on failure.
+void* static_scratch() {
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    hip_fail(e);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> g(mu);
+  if ((int)ptrs.size() <= dev) ptrs.resize(dev + 1, nullptr);
+  if (ptrs[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      hip_fail(e);
+      return nullptr;
+    }
+    ptrs[dev] = p;
+  }
+  return ptrs[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -513,6 +544,18 @@ int moments_fwd(const moments_desc* desc, const void* xhat, const void* bhat, co
   });
 }
 
+int moments_fwd_static(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                       const void* rot, const void* h0, float* m2, float* m1, void* stream) {
+  Plan P;
+  MOM_TRY(make_plan(desc, &P));
+  if (P.ws_fwd > (size_t)MOMENTS_STATIC_SCRATCH_BYTES) return MOMENTS_ESCRATCH;
+  void* ws = static_scratch();
+  if (ws == nullptr) return MOMENTS_EHIP;
+  // every region the forward reads is written earlier in the same call (carries
+  // by the carry pass, partial moments by the main kernel), so nothing is cleared
+  return moments_fwd(desc, xhat, bhat, da, rot, h0, m2, m1, ws, MOMENTS_STATIC_SCRATCH_BYTES, stream);
+}
+
 int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
                 const void* rot, const void* h0, const float* d_m2, const float* d_m1, void* d_xhat,
                 void* d_bhat, void* d_da, void* d_rot, void* d_h0, void* workspace,
@@ -542,6 +585,7 @@ const char* moments_strerror(int code) {
     case MOMENTS_ENOTSUP: return "shape not covered by the compiled kernels";
     case MOMENTS_EWORKSPACE: return "workspace too small";
     case MOMENTS_EHIP: return "HIP runtime error (see moments_last_hip_error)";
+    case MOMENTS_ESCRATCH: return "problem needs more than the static scratch of moments_fwd_static";
   }
   return "unknown error";
 }
