@@ -13,6 +13,7 @@
 #include "kernels_bwdt.h"
 #include "kernels_fwdt.h"
 #include "kernels_cscan.h"
+#include "kernels_fwd4.h"
 
 using namespace mom;
 
@@ -93,6 +94,8 @@ struct Plan {
   bool bwdt;    // backward main kernel in the transposed layout (bf16, c <= 2)
   bool fwdt;    // forward main kernel in the transposed layout (bf16, c <= 2)
   bool fwdt_inc;  // ... carrying the state rows itself (one group per chain): no carry pass
+  bool fwd4;      // forward main kernel in the lane-pair layout (bf16, p <= 128)
+  bool fwd4_inc;  // ... carrying the state rows itself
   size_t carry, dec, m2p, m1p, db, dm1i, gdb;  // workspace offsets
   size_t ws_fwd, ws_bwd;
 };
@@ -112,6 +115,20 @@ size_t fwdt_lds(const Geo& g, int NT, int CK) {
   if (NT == 4 && CK == 2) return LdsF<4, 2>::total(RT, g.p);
   if (NT == 8 && CK == 1) return LdsF<8, 1>::total(RT, g.p);
   if (NT == 8 && CK == 2) return LdsF<8, 2>::total(RT, g.p);
+  return 0;
+}
+
+// LDS bytes of k_fwd4 for (NT, CK), or 0 when that kernel does not cover the shape.
+size_t fwd4_lds(const Geo& g, int NT, int CK, bool inc) {
+  if (g.p > 128) return 0;  // m1 accumulators: 32 rows per wave
+  const int RG = rot_groups(g), pp = 4 * ((g.p + 3) / 4), rk = g.rot_kind == 3 ? 3 : 1;
+  if (NT == 4 && RG * (rk == 3 ? 4 : 2) > 4) return 0;
+  if (NT == 4 && CK == 1) return LdsF4<4, 1>::total(pp, rk, RG, inc);
+  if (NT == 4 && CK == 2) return LdsF4<4, 2>::total(pp, rk, RG, inc);
+  if (NT == 4 && CK == 4) return LdsF4<4, 4>::total(pp, rk, RG, inc);
+  if (NT == 8 && CK == 1) return LdsF4<8, 1>::total(pp, rk, RG, inc);
+  if (NT == 8 && CK == 2) return LdsF4<8, 2>::total(pp, rk, RG, inc);
+  if (NT == 8 && CK == 4) return LdsF4<8, 4>::total(pp, rk, RG, inc);
   return 0;
 }
 
@@ -200,11 +217,19 @@ int make_plan(const moments_desc* d, Plan* P) {
   P->carry = o; o = align256(o + chains * (size_t)g.NK * pr * 4);
   P->dec = o; o = align256(o + chains * (size_t)g.NK * 4);
   const size_t base = o;
-  P->m2p = o; o = align256(o + chains * (size_t)g.NGR * P->R * P->R * 4);
+  P->m2p = o; o = align256(o + chains * (size_t)g.NGR * NW4 * P->R * P->R * 4);  // per wave for k_fwd4
   P->m1p = o; o = align256(o + chains * (size_t)g.NGR * g.p * P->R * 4);
   P->ws_fwd = o;
   P->db = base;
   o = align256(base + chains * (size_t)g.NK * pr * 4);
+  if (bf) {
+    const size_t l4 = fwd4_lds(g, P->NT, P->CK, false);
+    P->fwd4 = l4 > 0 && l4 <= kLdsLimit;
+    P->fwd4_inc = P->fwd4 && g.NGR == 1 && fwd4_lds(g, P->NT, P->CK, true) <= kLdsLimit;
+  } else {
+    P->fwd4 = false;
+    P->fwd4_inc = false;
+  }
   if (bf && P->CK <= 2) {
     const size_t lf = fwdt_lds(g, P->NT, P->CK);
     P->fwdt = lf > 0 && lf <= kLdsLimit;
@@ -301,10 +326,51 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   const T* B = (const T*)bhat;
   const T* D = (const T*)da;
   const T* Rt = (const T*)rot;
-  if (!P.fwdt_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
   float* m2p = (float*)(ws + P.m2p);
   float* m1p = (float*)(ws + P.m1p);
   const int chains = g.b * g.h;
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (P.fwd4) {
+      if (!P.fwd4_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
+      const int RG = rot_groups(g);
+      auto launch = [&](auto rot_c, auto rg_c) -> int {
+        constexpr int RO = decltype(rot_c)::value, RGc = decltype(rg_c)::value;
+        if constexpr (RGc * (RO == 3 ? 4 : 2) > NT) {
+          return MOMENTS_ENOTSUP;
+        } else {
+          const size_t lds = fwd4_lds(g, NT, CK, P.fwd4_inc);
+          if (g.NK >= 1) {
+            auto go = [&](auto m1t_c, auto inc_c) -> int {
+              constexpr int M1 = decltype(m1t_c)::value;
+              constexpr bool INC = decltype(inc_c)::value == 1;
+              MOM_TRY(set_lds(k_fwd4<NT, RO, CK, RGc, M1, INC>, lds));
+              ProfScope ps(KID_FWD, st);
+              hipLaunchKernelGGL((k_fwd4<NT, RO, CK, RGc, M1, INC>), dim3(chains * g.NGR), dim3(NT4), lds, st, g, X, B,
+                                 D, Rt, INC ? nullptr : (const float*)(ws + P.carry), (const T*)h0, m2p, m1p);
+              return check_launch();
+            };
+            if (P.fwd4_inc) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<1>{}) : go(IC<2>{}, IC<1>{}));
+            else MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<0>{}) : go(IC<2>{}, IC<0>{}));
+          }
+          const int nout = P.R * P.R + g.p * P.R;
+          ProfScope ps(KID_REDUCE, st);
+          hipLaunchKernelGGL(k_reduce4, dim3(chains, (nout + NTH - 1) / NTH), dim3(NTH), 0, st, g, P.R,
+                             RGc > 0 ? RO : 0, (const float*)m2p, (const float*)m1p, m2, m1);
+          return check_launch();
+        }
+      };
+      if constexpr (ROT == 0) {
+        return launch(IC<0>{}, IC<0>{});
+      } else {
+        if (RG == 0) return launch(IC<0>{}, IC<0>{});
+        if (RG == 1) return launch(IC<ROT>{}, IC<1>{});
+        if (RG == 2) return launch(IC<ROT>{}, IC<2>{});
+        if (RG == 4) return launch(IC<ROT>{}, IC<4>{});
+        return MOMENTS_ENOTSUP;
+      }
+    }
+  }
+  if (!P.fwdt_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
   bool done = false;
   if constexpr (std::is_same<T, bf16>::value && CK <= 2) {
     if (P.fwdt && g.NK >= 1) {
