@@ -15,6 +15,13 @@ Two independent CPU implementations live here:
   exists to pin the oracle: chunk-length invariance (including the oracle's
   checkpointed backward over several 256-token segments) and the d_da identity.
 
+* ``rotation_seq.py`` (numpy fp64): the rotation-sequence producer upstream of
+  the moments path (inclusive angle sums; left-to-right renormalised Hamilton
+  products of quaternion increments) and its reverse-mode VJP, pinned in
+  ``tests/test_rotation_seq.py`` (scipy rotation composition, matrix products,
+  a coaxial closed form, finite differences, scale invariance, and the moments
+  gradient with respect to the increments).
+
 Parity pins (see ``tests/test_oracle_pins.py``): finite differences, torch
 float64 autograd, chunk-length invariance, the rotation-orthogonality trace
 identity, closed forms, zero gradients past valid_len, d_m2 antisymmetric

@@ -15,8 +15,11 @@ angles ``[b,s,h,a]`` or cumulative unit quaternions ``[b,s,h,J,4]``, (w,x,y,z)):
   (Q_t = Q_{t-1} * q_t) by a doubling prefix product in float64 with
   renormalisation after every doubling step, then cast.
 
-The composition of quaternions here is input preparation (the step upstream of
-the path); the method itself never sees the increments.
+The composition here only prepares the cumulative input of the moments path
+(a doubling product in float64, an algorithm neither implementation uses). The
+rotation-sequence producer, which composes increments itself, is tested on the
+raw increments (``generate(..., increments=True)["rot_inc"]``), never on this
+composition.
 """
 from __future__ import annotations
 
@@ -110,11 +113,13 @@ def _quat_prefix(q: torch.Tensor, dim: int) -> torch.Tensor:
     return q.movedim(0, dim)
 
 
-def generate(w: Workload, device="cpu", with_cotangents=True):
+def generate(w: Workload, device="cpu", with_cotangents=True, increments=False):
     """Draw one workload. Returns a dict of tensors on ``device`` in the workload's
     dtype (d_m2, d_m1 are float32): xhat[b,s,c,h,p], bhat[b,s,c,h,r], da[b,s,h],
     rot ([b,s,h,a] | [b,s,h,J,4] | None), h0[b,h,p,r] | None, d_m2[b,h,r,r],
-    d_m1[b,h,p,r]."""
+    d_m1[b,h,p,r]. With ``increments`` it also returns the per-token rotation
+    increments the cumulative ``rot`` was composed from, cast to the workload's
+    dtype, as ``rot_inc`` (same shape as ``rot``; None without a rotation)."""
     g = torch.Generator(device=device)
     g.manual_seed(w.seed)
     f32 = dict(device=device, dtype=torch.float32, generator=g)
@@ -128,13 +133,19 @@ def generate(w: Workload, device="cpu", with_cotangents=True):
         a = w.rope_dim // 2
         inc = (torch.rand(w.b, w.s, w.h, a, **f32) * 2.0 - 1.0) * w.angle_step
         out["rot"] = torch.cumsum(inc.double(), dim=1).to(dt)
+        if increments:
+            out["rot_inc"] = inc.to(dt)
     elif w.rot_kind == ROT_QUAT:
         v = torch.randn(w.b, w.s, w.h, w.quat_blocks, 3, **f32).double() * w.quat_sd
         phi = v.norm(dim=-1, keepdim=True).clamp_min(1e-30)
         q = torch.cat([torch.cos(phi / 2), torch.sin(phi / 2) * v / phi], dim=-1)
         out["rot"] = _quat_prefix(q, dim=1).to(dt).contiguous()
+        if increments:
+            out["rot_inc"] = q.to(dt).contiguous()
     else:
         out["rot"] = None
+        if increments:
+            out["rot_inc"] = None
     if w.h0_sd is None:
         out["h0"] = None
     else:
