@@ -132,6 +132,42 @@ def cpu_baseline(w, t, seconds_hint=15.0):
                       f"tokens/s = chains*tokens/h/time"}
 
 
+def producer_leg(w, M, W, dev, reps=10):
+    """Times the rotation-sequence producer (moments_rot_fwd) and its VJP
+    (moments_rot_bwd) on the workload's increments, outside the timed step.
+    Both are HBM-bound streams: the algorithmic bytes are one read of each input
+    and one write of the output (2 and 3 tensors of rot's size); the kernels read
+    their inputs twice (segment totals, then the walk), which the per-kernel
+    figures show."""
+    import torch
+    if w.rot_kind == W.ROT_NONE:
+        return None
+    inc, d_rot = W.rotation_increments(w, dev)
+    d = M.rot_desc(inc, w.rot_kind)
+    rot = torch.empty_like(inc)
+    d_inc = torch.empty_like(inc)
+    size = inc.numel() * inc.element_size()
+    out = {"shape": list(inc.shape), "dtype": w.dtype}
+    for name, call, nbytes in (("fwd", lambda: M.moments_rot_fwd(d, inc, rot), 2 * size),
+                               ("bwd", lambda: M.moments_rot_bwd(d, inc, d_rot, d_inc), 3 * size)):
+        call()
+        torch.cuda.synchronize()
+        M.profile_reset()
+        M.profile_enable(True)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        M.profile_enable(False)
+        prof = {k: v for k, v in M.profile_read().items() if k.startswith("k_rot") and v[0] > 0}
+        ms = sum(tot for _, tot in prof.values()) / reps
+        gbs = nbytes / (ms / 1e3) / 1e9
+        out[name] = {"ms": round(ms, 4), "algorithmic_bytes": nbytes, "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "kernels_ms": {k: round(tot / max(n, 1), 4) for k, (n, tot) in sorted(prof.items())}}
+    M.profile_reset()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -244,6 +280,8 @@ def main():
         torch.cuda.synchronize()
         del src_t, dst_t
 
+    producer = producer_leg(w, M, W, dev)
+
     cpu = None
     if not args.no_cpu:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
@@ -268,6 +306,7 @@ def main():
         "roofline": roof,
         "step_roofline": step_roof,
         "cpu_baseline": cpu,
+        "producer": producer,
     }
     print(json.dumps(out), flush=True)
 

@@ -121,6 +121,43 @@ int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, co
                 void* d_xhat, void* d_bhat, void* d_da, void* d_rot, void* d_h0,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Rotation-sequence producer: builds the cumulative rotation that moments_fwd
+ * and moments_bwd take (rot) from per-token increments ("recalculated.rs"
+ * source page: RotPrim carries cumulative angles [b,s,h,a] or cumulative unit
+ * quaternions [b,s,h,J,4]; quat_mul_prim is the Hamilton product on the packed
+ * (w,x,y,z) axis). The pages do not print this step; it is read as
+ *   complex modes : rot[b,t,h,i] = sum_{t' <= t} inc[b,t',h,i]
+ *   quaternion    : rot[b,t,h,j] = N(rot[b,t-1,h,j] (x) inc[b,t,h,j]),
+ *                   rot[b,-1,h,j] = 1, N(v) = v / |v|
+ * (left-to-right composition, renormalised every step; for unit increments N
+ * changes nothing in exact arithmetic, for any nonzero increments the result is
+ * the normalised product inc[0] (x) ... (x) inc[t]). Every position t < s is
+ * produced (valid_len is not read). Quaternion increments must be nonzero.
+ *
+ * Reads desc->b, s, h, dtype, rot_kind (not MOMENTS_ROT_NONE), rope_dim (complex
+ * modes: a = rope_dim/2 angles per head) or quat_blocks; the other fields are
+ * ignored. inc and rot have rot's layout from moments_fwd ([b,s,h,a] or
+ * [b,s,h,J,4], row-major, desc->dtype, 16-byte aligned device memory) and must
+ * not overlap. Sums and products run in fp32. Returns MOMENTS_EINVAL for a bad
+ * descriptor, NULL or misaligned pointers, MOMENTS_ENOTSUP for b > 65535 or
+ * more than 2^24 chains per token (h * a or h * J) or 2^30 in all (times b),
+ * MOMENTS_EWORKSPACE below moments_rot_workspace_size(); empty shapes (b, s or h
+ * zero) launch nothing and accept NULL pointers. */
+int64_t moments_rot_workspace_size(const moments_desc* desc, int is_bwd);
+int moments_rot_fwd(const moments_desc* desc, const void* inc, void* rot, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* VJP of the producer: d_inc from d_rot (the cotangent of rot, e.g. the d_rot
+ * moments_bwd returns) and the same increments inc:
+ *   complex modes : d_inc[t] = sum_{t' >= t} d_rot[t']
+ *   quaternion    : the reverse-mode derivative of the renormalised product;
+ *                   d_inc[t] is orthogonal to inc[t] (rescaling an increment
+ *                   leaves rot unchanged).
+ * Same layouts, dtype, alignment and errors as moments_rot_fwd; inc, d_rot and
+ * d_inc must not overlap. */
+int moments_rot_bwd(const moments_desc* desc, const void* inc, const void* d_rot, void* d_inc,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 const char* moments_strerror(int code);
 int moments_last_hip_error(void);
 

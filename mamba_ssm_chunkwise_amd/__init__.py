@@ -15,7 +15,7 @@ from ._lib import (BF16, F32, ROT_HALF, ROT_NONE, ROT_PAIRWISE, ROT_QUAT, Desc, 
                    MomentsError)
 
 __all__ = ["make_desc", "moments_validate", "moments_workspace_size", "moments_fwd", "moments_fwd_static",
-           "moments_bwd",
+           "moments_bwd", "rot_desc", "moments_rot_workspace_size", "moments_rot_fwd", "moments_rot_bwd",
            "kernel_chunk_len",
            "Desc", "MomentsError", "ROT_NONE", "ROT_PAIRWISE", "ROT_HALF", "ROT_QUAT"]
 
@@ -178,6 +178,70 @@ def moments_bwd(desc: Desc, xhat, bhat, da, rot, h0, d_m2, d_m1, want=("xhat", "
                                  _ptr(out["d_h0"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
     _lib.check(rc)
     return out
+
+
+def rot_desc(inc, rot_kind, rope_dim=0, quat_blocks=0):
+    """Descriptor of the rotation-sequence producer for increments ``inc``
+    ([b,s,h,a] angles with rope_dim = 2a, or [b,s,h,J,4] quaternions). Only b,
+    s, h, dtype, rot_kind and rope_dim / quat_blocks are read by the library."""
+    if not isinstance(inc, torch.Tensor):
+        raise ValueError("inc must be a torch.Tensor")
+    b, s, h = (int(x) for x in inc.shape[:3])
+    if rot_kind == ROT_QUAT and quat_blocks == 0 and inc.dim() == 5:
+        quat_blocks = int(inc.shape[3])
+    if rot_kind in (ROT_PAIRWISE, ROT_HALF) and rope_dim == 0 and inc.dim() == 4:
+        rope_dim = 2 * int(inc.shape[3])
+    dtype = BF16 if inc.dtype == torch.bfloat16 else F32
+    return Desc(b, s, 1, h, 1, 1, 1, s, int(dtype), int(rot_kind), int(rope_dim), int(quat_blocks))
+
+
+def _rot_shape(desc: Desc):
+    if desc.rot_kind == ROT_QUAT:
+        return (desc.b, desc.s, desc.h, desc.quat_blocks, 4)
+    if desc.rot_kind in (ROT_PAIRWISE, ROT_HALF):
+        return (desc.b, desc.s, desc.h, desc.rope_dim // 2)
+    raise ValueError("the producer needs a rotation (rot_kind must not be ROT_NONE)")
+
+
+def moments_rot_workspace_size(desc: Desc, is_bwd: bool) -> int:
+    n = _lib.load().moments_rot_workspace_size(ctypes.byref(desc), int(bool(is_bwd)))
+    if n < 0:
+        _lib.check(int(n))
+    return int(n)
+
+
+def _rot_call(desc, is_bwd, inc, d_rot, out):
+    if not isinstance(inc, torch.Tensor):
+        raise ValueError("inc must be a torch.Tensor")
+    dev = inc.device
+    shape = _rot_shape(desc)
+    dt = torch.bfloat16 if desc.dtype == BF16 else torch.float32
+    _expect("inc", inc, shape, dt, dev)
+    if is_bwd:
+        _expect("d_rot", d_rot, shape, dt, dev)
+    _expect("out", out, shape, dt, dev, optional=True)
+    _require_gpu(dev)
+    if out is None:
+        out = torch.empty(shape, dtype=dt, device=dev)
+    n = moments_rot_workspace_size(desc, is_bwd)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    if is_bwd:
+        rc = lib.moments_rot_bwd(ctypes.byref(desc), _ptr(inc), _ptr(d_rot), _ptr(out), _ptr(ws), n, _stream(dev))
+    else:
+        rc = lib.moments_rot_fwd(ctypes.byref(desc), _ptr(inc), _ptr(out), _ptr(ws), n, _stream(dev))
+    _lib.check(rc)
+    return out
+
+
+def moments_rot_fwd(desc: Desc, inc, rot=None):
+    """Cumulative rotation (the moments path's ``rot``) from per-token increments."""
+    return _rot_call(desc, False, inc, None, rot)
+
+
+def moments_rot_bwd(desc: Desc, inc, d_rot, d_inc=None):
+    """Cotangent of the increments from the cotangent of the cumulative rotation."""
+    return _rot_call(desc, True, inc, d_rot, d_inc)
 
 
 def kernel_chunk_len() -> int:

@@ -19,7 +19,8 @@ ROT_NONE, ROT_PAIRWISE, ROT_HALF, ROT_QUAT = 0, 1, 2, 3
 
 EXPORTS = ("moments_validate", "moments_workspace_size", "moments_fwd", "moments_fwd_static", "moments_bwd",
            "moments_strerror", "moments_last_hip_error", "moments_kernel_chunk_len",
-           "moments_profile_enable", "moments_profile_read", "moments_profile_reset")
+           "moments_profile_enable", "moments_profile_read", "moments_profile_reset",
+           "moments_rot_workspace_size", "moments_rot_fwd", "moments_rot_bwd")
 
 
 class Desc(ctypes.Structure):
@@ -59,6 +60,12 @@ def load():
         lib.moments_fwd_static.restype = ctypes.c_int
         lib.moments_bwd.argtypes = [dp] + [vp] * 12 + [vp, ctypes.c_size_t, vp]
         lib.moments_bwd.restype = ctypes.c_int
+        lib.moments_rot_workspace_size.argtypes = [dp, ctypes.c_int]
+        lib.moments_rot_workspace_size.restype = ctypes.c_int64
+        lib.moments_rot_fwd.argtypes = [dp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.moments_rot_fwd.restype = ctypes.c_int
+        lib.moments_rot_bwd.argtypes = [dp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.moments_rot_bwd.restype = ctypes.c_int
         lib.moments_strerror.argtypes = [ctypes.c_int]
         lib.moments_strerror.restype = ctypes.c_char_p
         lib.moments_last_hip_error.argtypes = []

@@ -14,6 +14,7 @@
 #include "kernels_fwdt.h"
 #include "kernels_cscan.h"
 #include "kernels_fwd4.h"
+#include "kernels_rot.h"
 
 using namespace mom;
 
@@ -32,11 +33,11 @@ constexpr size_t kLdsLimit = 160 * 1024;
 // ---- optional per-kernel event timing (moments_profile_*) -------------------
 enum KernelId {
   KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_PREP, KID_GSCAN, KID_GFIX,
-  KID_CSCAN, KID_N
+  KID_CSCAN, KID_ROTSEG, KID_ROTCARRY, KID_ROTAPPLY, KID_N
 };
 const char* const kKernelNames[KID_N] = {"k_carry", "k_scan",      "k_fwd",      "k_reduce", "k_bwd",  "k_dscan",
                                          "k_fix",   "k_zero_tail", "k_prep_dm1", "k_gscan",  "k_gfix",
-                                         "k_cscan"};
+                                         "k_cscan", "k_rot_seg",   "k_rot_carry", "k_rot_apply"};
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -549,6 +550,123 @@ int with_variant(const Plan& P, F&& f) {
   return MOMENTS_ENOTSUP;
 }
 
+// ---- rotation-sequence producer ---------------------------------------------
+struct RotPlan {
+  RotGeo g;
+  bool bf, quat, empty;
+  int V;                // chains per thread of the streaming passes
+  size_t tot, aux, ws_fwd, ws_bwd;  // workspace offsets and bytes
+};
+
+// Reads b, s, h, dtype, rot_kind, rope_dim / quat_blocks of the descriptor.
+int make_rot_plan(const moments_desc* d, RotPlan* P) {
+  if (d == nullptr) return MOMENTS_EINVAL;
+  if (d->b < 0 || d->s < 0 || d->h < 0) return MOMENTS_EINVAL;
+  if (d->dtype != MOMENTS_F32 && d->dtype != MOMENTS_BF16) return MOMENTS_EINVAL;
+  int64_t per_h = 0;
+  if (d->rot_kind == MOMENTS_ROT_COMPLEX_PAIRWISE || d->rot_kind == MOMENTS_ROT_COMPLEX_HALF) {
+    if (d->rope_dim < 2 || d->rope_dim % 2 != 0) return MOMENTS_EINVAL;
+    per_h = d->rope_dim / 2;
+    P->quat = false;
+  } else if (d->rot_kind == MOMENTS_ROT_QUATERNION) {
+    if (d->quat_blocks < 1) return MOMENTS_EINVAL;
+    per_h = d->quat_blocks;
+    P->quat = true;
+  } else {
+    return MOMENTS_EINVAL;
+  }
+  const int64_t C = d->h * per_h;
+  if (C > (1 << 24) || d->s > (1ll << 30) || d->b > 65535 || d->b * C > (1ll << 30)) return MOMENTS_ENOTSUP;
+  P->bf = d->dtype == MOMENTS_BF16;
+  P->empty = d->b == 0 || d->s == 0 || C == 0;
+  RotGeo& g = P->g;
+  g.b = (int)d->b;
+  g.s = (int)d->s;
+  g.C = (int)C;
+  // chains per thread: up to 16 bytes of one token row per load, C divisible by it
+  const int width = (P->quat ? 4 : 1) * (P->bf ? 2 : 4);
+  P->V = 1;
+  while (P->V * 2 * width <= 16 && g.C % (P->V * 2) == 0) P->V *= 2;
+  // segments long enough that every walk amortises its entering value, short
+  // enough that (segments x chain groups) fills the chip with ~128K threads
+  int64_t seg = 16;
+  const int64_t work = (int64_t)g.b * g.s * (g.C / P->V);
+  while (seg < 1024 && work / (2 * seg) >= (1 << 17)) seg *= 2;
+  while (g.s > 0 && (g.s + seg - 1) / seg > 65535) seg *= 2;
+  g.seg = (int)seg;
+  g.nseg = g.s == 0 ? 0 : (int)((g.s + seg - 1) / seg);
+  const size_t n = (size_t)g.b * g.nseg * g.C * (P->quat ? 4 : 1) * sizeof(float);
+  P->tot = 0;
+  P->aux = (n + 255) / 256 * 256;
+  P->ws_fwd = n;
+  P->ws_bwd = P->quat ? P->aux + n : n;
+  return 0;
+}
+
+template <typename T, bool QUAT, bool BWD, int V>
+int run_rot(const RotPlan& P, const void* inc, const void* dout, void* out, unsigned char* ws, hipStream_t st) {
+  const RotGeo& g = P.g;
+  float* tot = (float*)(ws + P.tot);
+  float* aux = QUAT && BWD ? (float*)(ws + P.aux) : nullptr;
+  const int groups = g.C / V;
+  const dim3 grid((groups + ROT_TPB - 1) / ROT_TPB, g.nseg, g.b);
+  {
+    ProfScope ps(KID_ROTSEG, st);
+    hipLaunchKernelGGL((k_rot_seg<T, QUAT, BWD, V>), grid, dim3(ROT_TPB), 0, st, g, (const T*)inc,
+                       (const T*)dout, tot, aux);
+    MOM_TRY(check_launch());
+  }
+  {
+    ProfScope ps(KID_ROTCARRY, st);
+    const int n = g.b * g.C;
+    hipLaunchKernelGGL((k_rot_carry<QUAT, BWD>), dim3((n + ROT_TPB - 1) / ROT_TPB), dim3(ROT_TPB), 0, st, g,
+                       tot, aux);
+    MOM_TRY(check_launch());
+  }
+  ProfScope ps(KID_ROTAPPLY, st);
+  hipLaunchKernelGGL((k_rot_apply<T, QUAT, BWD, V>), grid, dim3(ROT_TPB), 0, st, g, (const T*)inc,
+                     (const T*)dout, tot, aux, (T*)out);
+  return check_launch();
+}
+
+int rot_entry(const moments_desc* desc, bool bwd, const void* inc, const void* dout, void* out, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  RotPlan P;
+  MOM_TRY(make_rot_plan(desc, &P));
+  if (P.empty) return 0;
+  if (!inc || !out || (bwd && !dout)) return MOMENTS_EINVAL;
+  const void* ptrs[] = {inc, dout, out, workspace};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return MOMENTS_EINVAL;
+  const size_t need = bwd ? P.ws_bwd : P.ws_fwd;
+  if (workspace_bytes < need || workspace == nullptr) return MOMENTS_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  // V = 1, 2, 4 or 8 chains per thread (8 only for bf16 angles)
+  auto go = [&](auto tt, auto vv) -> int {
+    using T = typename decltype(tt)::type;
+    constexpr int V = decltype(vv)::value;
+    if constexpr (V <= 2) {
+      if (P.quat) return bwd ? run_rot<T, true, true, V>(P, inc, dout, out, ws, st)
+                             : run_rot<T, true, false, V>(P, inc, dout, out, ws, st);
+    } else {
+      if (P.quat) return MOMENTS_ENOTSUP;  // the plan never gives quaternions more than 2
+    }
+    return bwd ? run_rot<T, false, true, V>(P, inc, dout, out, ws, st)
+               : run_rot<T, false, false, V>(P, inc, dout, out, ws, st);
+  };
+  auto by_v = [&](auto tt) -> int {
+    switch (P.V) {
+      case 1: return go(tt, IC<1>{});
+      case 2: return go(tt, IC<2>{});
+      case 4: return go(tt, IC<4>{});
+    }
+    if constexpr (std::is_same<typename decltype(tt)::type, bf16>::value) return go(tt, IC<8>{});
+    return MOMENTS_ENOTSUP;
+  };
+  return P.bf ? by_v(TT<bf16>{}) : by_v(TT<float>{});
+}
+
 // Address of this device's copy of `scratch`, looked up once per device with
 // that device current; nullptr (and the HIP error recorded) on failure.
 void* static_scratch() {
@@ -642,6 +760,23 @@ int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, co
     return run_bwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
         P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, st);
   });
+}
+
+int64_t moments_rot_workspace_size(const moments_desc* desc, int is_bwd) {
+  RotPlan P;
+  const int rc = make_rot_plan(desc, &P);
+  if (rc != 0) return rc;
+  return P.empty ? 0 : (int64_t)(is_bwd ? P.ws_bwd : P.ws_fwd);
+}
+
+int moments_rot_fwd(const moments_desc* desc, const void* inc, void* rot, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return rot_entry(desc, false, inc, nullptr, rot, workspace, workspace_bytes, stream);
+}
+
+int moments_rot_bwd(const moments_desc* desc, const void* inc, const void* d_rot, void* d_inc, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return rot_entry(desc, true, inc, d_rot, d_inc, workspace, workspace_bytes, stream);
 }
 
 const char* moments_strerror(int code) {

@@ -153,3 +153,64 @@ def test_binding_rejects_dtypes_devices_and_pooled_cotangent():
     t = _tensors(d)                                # everything right, but on the host
     with pytest.raises(ValueError, match="GPU"):
         _call("bwd", d, t)
+
+
+# ---------------------------------------------------------------- rotation-sequence producer
+@pytest.mark.parametrize("kw,code", [
+    (dict(rot_kind=M.ROT_PAIRWISE, rope_dim=8), 0),
+    (dict(rot_kind=M.ROT_HALF, rope_dim=8), 0),
+    (dict(rot_kind=M.ROT_QUAT, rope_dim=0, quat_blocks=3), 0),
+    (dict(rot_kind=M.ROT_NONE, rope_dim=0), -1),
+    (dict(rot_kind=M.ROT_PAIRWISE, rope_dim=7), -1),
+    (dict(rot_kind=M.ROT_PAIRWISE, rope_dim=0), -1),
+    (dict(rot_kind=M.ROT_QUAT, rope_dim=0, quat_blocks=0), -1),
+    (dict(dtype=5), -1),
+    (dict(s=-1), -1),
+    (dict(b=70000), -2),
+    (dict(r=4096, rope_dim=2000, p=0, c=99, chunk_len=0), 0),   # fields the producer does not read
+])
+def test_rot_workspace_and_validation(kw, code):
+    n = _lib.load().moments_rot_workspace_size(ctypes.byref(_desc(**kw)), 1)
+    if code == 0:
+        assert n > 0
+    else:
+        assert n == code
+
+
+def test_rot_workspace_sizes():
+    lib = _lib.load()
+    q = _desc(rot_kind=M.ROT_QUAT, rope_dim=0, quat_blocks=3)
+    fwd = lib.moments_rot_workspace_size(ctypes.byref(q), 0)
+    bwd = lib.moments_rot_workspace_size(ctypes.byref(q), 1)
+    assert 0 < fwd < bwd   # the quaternion VJP keeps a second per-segment array
+    a = _desc()
+    assert lib.moments_rot_workspace_size(ctypes.byref(a), 0) == lib.moments_rot_workspace_size(ctypes.byref(a), 1)
+    assert lib.moments_rot_workspace_size(ctypes.byref(_desc(s=0)), 1) == 0
+
+
+def test_rot_errors_without_gpu():
+    lib = _lib.load()
+    d = _desc()
+    null = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    assert lib.moments_rot_fwd(ctypes.byref(d), null, fake, fake, 1 << 40, null) == _lib.EINVAL
+    assert lib.moments_rot_bwd(ctypes.byref(d), fake, null, fake, fake, 1 << 40, null) == _lib.EINVAL
+    assert lib.moments_rot_fwd(ctypes.byref(d), fake, fake, fake, 16, null) == _lib.EWORKSPACE
+    misaligned = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.moments_rot_fwd(ctypes.byref(d), misaligned, fake, fake, 1 << 40, null) == _lib.EINVAL
+    # empty shapes launch nothing and accept NULL pointers
+    assert lib.moments_rot_fwd(ctypes.byref(_desc(s=0)), null, null, null, 0, null) == 0
+    assert lib.moments_rot_bwd(ctypes.byref(_desc(b=0)), null, null, null, null, 0, null) == 0
+
+
+def test_rot_binding_rejects_shapes():
+    import torch
+    inc = torch.zeros(2, 16, 3, 4)
+    d = M.rot_desc(inc, M.ROT_PAIRWISE)
+    assert (d.b, d.s, d.h, d.rope_dim) == (2, 16, 3, 8)
+    with pytest.raises(ValueError, match="inc has shape"):
+        M.moments_rot_fwd(d, torch.zeros(2, 16, 3, 5))
+    with pytest.raises(ValueError, match="d_rot has shape"):
+        M.moments_rot_bwd(d, inc, torch.zeros(2, 16, 3))
+    with pytest.raises(ValueError, match="GPU"):
+        M.moments_rot_fwd(d, inc)

@@ -156,6 +156,32 @@ def generate(w: Workload, device="cpu", with_cotangents=True, increments=False):
     return out
 
 
+def rotation_increments(w: Workload, device="cpu", scale=None):
+    """Per-token rotation increments alone, for the rotation-sequence producer:
+    the distribution ``generate`` composes (U(-angle_step, angle_step) angles, or
+    unit quaternions from N(0, quat_sd^2)^3 axis-angle vectors), drawn from a
+    stream of their own (seed + 7919), cast to the workload's dtype, and a
+    cotangent N(0, 1) of the same shape. ``scale`` = (lo, hi) multiplies each
+    quaternion by U(lo, hi) (non-unit increments). Returns (inc, d_rot)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed + 7919)
+    f32 = dict(device=device, dtype=torch.float32, generator=g)
+    dt = w.torch_dtype
+    if w.rot_kind in (ROT_PAIRWISE, ROT_HALF):
+        inc = (torch.rand(w.b, w.s, w.h, w.rope_dim // 2, **f32) * 2.0 - 1.0) * w.angle_step
+    elif w.rot_kind == ROT_QUAT:
+        v = torch.randn(w.b, w.s, w.h, w.quat_blocks, 3, **f32).double() * w.quat_sd
+        phi = v.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+        inc = torch.cat([torch.cos(phi / 2), torch.sin(phi / 2) * v / phi], dim=-1)
+        if scale is not None:
+            lo, hi = scale
+            inc = inc * (lo + (hi - lo) * torch.rand(inc.shape[:-1] + (1,), **f32).double())
+    else:
+        raise ValueError("the workload has no rotation")
+    d_rot = torch.randn(inc.shape, **f32)
+    return inc.to(dt).contiguous(), d_rot.to(dt).contiguous()
+
+
 def small(name, dtype="f32", b=1, s=48, c=2, h=2, p=24, r=40, chunk_len=16, valid_len=None,
           rot_kind=ROT_PAIRWISE, rope_dim=16, quat_blocks=0, seed=7, h0_sd=0.1, da_mu=-0.5,
           angle_step=0.3, quat_sd=0.3, da_shift=0.0):
