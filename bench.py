@@ -175,6 +175,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_pairwise_b8_s8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--saved-carry", action="store_true",
+                    help="time the saved-carry variant: moments_fwd_save keeps the chunk-boundary states, "
+                         "moments_bwd_saved reads them instead of running its carry pass")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run one plain device copy of 1 GiB (reads 1 GiB, writes "
                          "1 GiB) so a counter run can calibrate HBM byte counters")
@@ -203,10 +206,19 @@ def main():
     grads = M.moments_bwd(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], t["d_m2"], t["d_m1"],
                           workspace=ws)
 
+    saved = (torch.empty(max(M.moments_saved_size(d), 1), dtype=torch.uint8, device=dev)
+             if args.saved_carry else None)
+
     def step():
-        M.moments_fwd(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], m2=m2, m1=m1, workspace=ws)
-        M.moments_bwd(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], t["d_m2"], t["d_m1"],
-                      out=grads, workspace=ws)
+        if saved is None:
+            M.moments_fwd(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], m2=m2, m1=m1, workspace=ws)
+            M.moments_bwd(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], t["d_m2"], t["d_m1"],
+                          out=grads, workspace=ws)
+        else:
+            M.moments_fwd_save(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], m2=m2, m1=m1, saved=saved,
+                               workspace=ws)
+            M.moments_bwd_saved(d, t["xhat"], t["bhat"], t["da"], t["rot"], t["h0"], saved, t["d_m2"],
+                                t["d_m1"], out=grads, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -302,7 +314,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "b": w.b, "s": w.s, "valid_len": w.valid_len, "c": w.c, "h": w.h,
                    "p": w.p, "r": w.r, "chunk_len": w.chunk_len, "rot_kind": w.rot_kind,
-                   "rope_dim": w.rope_dim, "quat_blocks": w.quat_blocks, "parallelism": "none"},
+                   "rope_dim": w.rope_dim, "quat_blocks": w.quat_blocks, "parallelism": "none",
+                   "saved_carry": bool(args.saved_carry)},
         "roofline": roof,
         "step_roofline": step_roof,
         "cpu_baseline": cpu,

@@ -121,6 +121,38 @@ int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, co
                 void* d_xhat, void* d_bhat, void* d_da, void* d_rot, void* d_h0,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Saved-carry variant ("backward.rs" source page, module doc and
+ * boundary_carries: the backward needs the state entering every chunk, which
+ * the pages recompute with a cheap chunk-level pass; "recalculated.rs" module
+ * doc: the node itself keeps only its inputs). moments_fwd_save is moments_fwd
+ * that also leaves those boundary states in a caller buffer `saved`;
+ * moments_bwd_saved is moments_bwd that reads them from there instead of
+ * recomputing them (it skips the carry pass). The results equal the plain
+ * calls up to rounding (the states reach the buffer through the forward's own
+ * arithmetic).
+ *
+ * `saved` holds, at kernel-chunk granularity (moments_kernel_chunk_len()
+ * tokens; NK = ceil(min(valid_len, s) / that) chunks per chain):
+ *   float32 states [b*h][NK][p][r] entering each chunk (entry 0 is h0, or
+ *   zeros), columns in the library's internal order (the caller's order, except
+ *   that half-split pairs (i, r/2+i) sit at (2i, 2i+1)), then, at the next
+ *   256-byte boundary, float32 chunk decays [b*h][NK] (exp of the sum of da over
+ *   the chunk; the last chunk's entry is not used).
+ * Treat it as opaque: fill it with moments_fwd_save and pass it, unchanged and
+ * with the same descriptor and inputs, to moments_bwd_saved. Its size is
+ * moments_saved_size(desc) bytes (about 4 * b*h*NK*p*r), device memory, 16-byte
+ * aligned, owned by the caller. A saved buffer below that size returns
+ * MOMENTS_EWORKSPACE, a NULL one MOMENTS_EINVAL. Workspaces are those of
+ * moments_fwd and moments_bwd. */
+int64_t moments_saved_size(const moments_desc* desc);
+int moments_fwd_save(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                     const void* rot, const void* h0, float* m2, float* m1, void* saved,
+                     size_t saved_bytes, void* workspace, size_t workspace_bytes, void* stream);
+int moments_bwd_saved(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                      const void* rot, const void* h0, const void* saved, size_t saved_bytes,
+                      const float* d_m2, const float* d_m1, void* d_xhat, void* d_bhat, void* d_da,
+                      void* d_rot, void* d_h0, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Rotation-sequence producer: builds the cumulative rotation that moments_fwd
  * and moments_bwd take (rot) from per-token increments ("recalculated.rs"
  * source page: RotPrim carries cumulative angles [b,s,h,a] or cumulative unit

@@ -15,7 +15,7 @@ from ._lib import (BF16, F32, ROT_HALF, ROT_NONE, ROT_PAIRWISE, ROT_QUAT, Desc, 
                    MomentsError)
 
 __all__ = ["make_desc", "moments_validate", "moments_workspace_size", "moments_fwd", "moments_fwd_static",
-           "moments_bwd", "rot_desc", "moments_rot_workspace_size", "moments_rot_fwd", "moments_rot_bwd",
+           "moments_bwd", "moments_saved_size", "moments_fwd_save", "moments_bwd_saved", "rot_desc", "moments_rot_workspace_size", "moments_rot_fwd", "moments_rot_bwd",
            "kernel_chunk_len",
            "Desc", "MomentsError", "ROT_NONE", "ROT_PAIRWISE", "ROT_HALF", "ROT_QUAT"]
 
@@ -152,8 +152,56 @@ def moments_fwd_static(desc: Desc, xhat, bhat, da, rot, h0, m2, m1):
     return m2, m1
 
 
+def moments_saved_size(desc: Desc) -> int:
+    """Bytes of the saved-carry buffer of moments_fwd_save / moments_bwd_saved."""
+    n = _lib.load().moments_saved_size(ctypes.byref(desc))
+    if n < 0:
+        _lib.check(int(n))
+    return int(n)
+
+
+def _saved_buffer(desc, device, saved):
+    n = moments_saved_size(desc)
+    if saved is None:
+        return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    if not isinstance(saved, torch.Tensor) or saved.device != device or not saved.is_contiguous():
+        raise ValueError(f"saved must be a contiguous tensor on {device}")
+    if saved.numel() * saved.element_size() < n:
+        raise ValueError(f"saved holds {saved.numel() * saved.element_size()} bytes, the descriptor needs {n}")
+    return saved
+
+
+def moments_fwd_save(desc: Desc, xhat, bhat, da, rot, h0, m2=None, m1=None, saved=None, workspace=None):
+    """moments_fwd that also keeps the chunk-boundary states for the backward.
+    Returns (m2, m1, saved); saved is an opaque uint8 device tensor to pass to
+    moments_bwd_saved with the same descriptor and inputs."""
+    dev, _, _ = _check_inputs(desc, xhat, bhat, da, rot, h0)
+    _expect("m2", m2, (desc.b, desc.h, desc.r, desc.r), torch.float32, dev, optional=True)
+    _expect("m1", m1, (desc.b, desc.h, desc.p, desc.r), torch.float32, dev, optional=True)
+    _require_gpu(dev)
+    if m2 is None:
+        m2 = torch.empty(desc.b, desc.h, desc.r, desc.r, dtype=torch.float32, device=dev)
+    if m1 is None:
+        m1 = torch.empty(desc.b, desc.h, desc.p, desc.r, dtype=torch.float32, device=dev)
+    sv = _saved_buffer(desc, dev, saved)
+    ws = _workspace(desc, False, dev, workspace)
+    rc = _lib.load().moments_fwd_save(ctypes.byref(desc), _ptr(xhat), _ptr(bhat), _ptr(da), _ptr(rot),
+                                      _ptr(h0), _ptr(m2), _ptr(m1), _ptr(sv), sv.numel(), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(dev))
+    _lib.check(rc)
+    return m2, m1, sv
+
+
+def moments_bwd_saved(desc: Desc, xhat, bhat, da, rot, h0, saved, d_m2, d_m1,
+                      want=("xhat", "bhat", "da", "rot", "h0"), out=None, workspace=None):
+    """moments_bwd reading the chunk-boundary states moments_fwd_save kept
+    (no carry pass). Same returns as moments_bwd."""
+    return moments_bwd(desc, xhat, bhat, da, rot, h0, d_m2, d_m1, want=want, out=out, workspace=workspace,
+                       _saved=saved)
+
+
 def moments_bwd(desc: Desc, xhat, bhat, da, rot, h0, d_m2, d_m1, want=("xhat", "bhat", "da", "rot", "h0"),
-                out=None, workspace=None):
+                out=None, workspace=None, _saved=None):
     """Returns dict d_xhat, d_bhat, d_da, d_rot, d_h0 (input dtype; None when
     not wanted or not defined)."""
     dev, specs, dt = _check_inputs(desc, xhat, bhat, da, rot, h0)
@@ -172,10 +220,15 @@ def moments_bwd(desc: Desc, xhat, bhat, da, rot, h0, d_m2, d_m1, want=("xhat", "
         if k in want and specs[k] is not None and out.get(key) is None:
             out[key] = torch.empty(specs[k], dtype=dt, device=dev)
     ws = _workspace(desc, True, dev, workspace)
-    rc = _lib.load().moments_bwd(ctypes.byref(desc), _ptr(xhat), _ptr(bhat), _ptr(da), _ptr(rot),
-                                 _ptr(h0), _ptr(d_m2), _ptr(d_m1), _ptr(out["d_xhat"]),
-                                 _ptr(out["d_bhat"]), _ptr(out["d_da"]), _ptr(out["d_rot"]),
-                                 _ptr(out["d_h0"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    grads = (_ptr(d_m2), _ptr(d_m1), _ptr(out["d_xhat"]), _ptr(out["d_bhat"]), _ptr(out["d_da"]),
+             _ptr(out["d_rot"]), _ptr(out["d_h0"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(dev))
+    if _saved is None:
+        rc = _lib.load().moments_bwd(ctypes.byref(desc), _ptr(xhat), _ptr(bhat), _ptr(da), _ptr(rot),
+                                     _ptr(h0), *grads)
+    else:
+        sv = _saved_buffer(desc, dev, _saved)
+        rc = _lib.load().moments_bwd_saved(ctypes.byref(desc), _ptr(xhat), _ptr(bhat), _ptr(da), _ptr(rot),
+                                           _ptr(h0), _ptr(sv), sv.numel() * sv.element_size(), *grads)
     _lib.check(rc)
     return out
 

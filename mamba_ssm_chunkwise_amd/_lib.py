@@ -20,7 +20,8 @@ ROT_NONE, ROT_PAIRWISE, ROT_HALF, ROT_QUAT = 0, 1, 2, 3
 EXPORTS = ("moments_validate", "moments_workspace_size", "moments_fwd", "moments_fwd_static", "moments_bwd",
            "moments_strerror", "moments_last_hip_error", "moments_kernel_chunk_len",
            "moments_profile_enable", "moments_profile_read", "moments_profile_reset",
-           "moments_rot_workspace_size", "moments_rot_fwd", "moments_rot_bwd")
+           "moments_rot_workspace_size", "moments_rot_fwd", "moments_rot_bwd",
+           "moments_saved_size", "moments_fwd_save", "moments_bwd_saved")
 
 
 class Desc(ctypes.Structure):
@@ -60,6 +61,12 @@ def load():
         lib.moments_fwd_static.restype = ctypes.c_int
         lib.moments_bwd.argtypes = [dp] + [vp] * 12 + [vp, ctypes.c_size_t, vp]
         lib.moments_bwd.restype = ctypes.c_int
+        lib.moments_saved_size.argtypes = [dp]
+        lib.moments_saved_size.restype = ctypes.c_int64
+        lib.moments_fwd_save.argtypes = [dp] + [vp] * 7 + [vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp]
+        lib.moments_fwd_save.restype = ctypes.c_int
+        lib.moments_bwd_saved.argtypes = [dp] + [vp] * 5 + [vp, ctypes.c_size_t] + [vp] * 7 + [vp, ctypes.c_size_t, vp]
+        lib.moments_bwd_saved.restype = ctypes.c_int
         lib.moments_rot_workspace_size.argtypes = [dp, ctypes.c_int]
         lib.moments_rot_workspace_size.restype = ctypes.c_int64
         lib.moments_rot_fwd.argtypes = [dp, vp, vp, vp, ctypes.c_size_t, vp]

@@ -234,11 +234,12 @@ __host__ __device__ constexpr int tri(int a, int b) {
   return a * NT - a * (a - 1) / 2 + (b - a);
 }
 
-template <int NT, int ROT, int CK, int RG, int M1T, bool INC>
+template <int NT, int ROT, int CK, int RG, int M1T, int INC>
 __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__ xhat,
                                                   const bf16* __restrict__ bhat, const bf16* __restrict__ da,
                                                   const bf16* __restrict__ rot, const float* __restrict__ carry,
-                                                  const bf16* __restrict__ h0, float* m2part, float* m1part) {
+                                                  const bf16* __restrict__ h0, float* m2part, float* m1part,
+                                                  float* __restrict__ save, float* __restrict__ save_dec) {
   constexpr int R = 16 * NT, K = ELL * CK, KP = cf_pitch(K);
   constexpr int NKS0 = CK >= 2 ? CK / 2 : 1;   // K-steps seen by tokens 0..15 (j <= 15)
   constexpr int NTRI = NT * (NT + 1) / 2;
@@ -264,7 +265,9 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
   const int lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int nrow = (g.p - w + 3) / 4;  // rows of this wave: p = w + 4k
 
-  constexpr bool inc = INC;  // the state rows are carried in LDS (carry == nullptr)
+  // INC 0: entering states from the carry pass; 1: carried in LDS (carry ==
+  // nullptr); 2: carried, and also written to `save` / `save_dec`
+  constexpr bool inc = INC != 0;
   // index of this lane's columns in the carry-pass rows (their column order
   // interleaves half-split pairs), -1 for padding
   int cidx[NT];
@@ -273,11 +276,19 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
     const int cc = lp_col(g, ORD, 16 * ct + n);
     cidx[ct] = cc >= 0 ? inv_perm_rc(g, cc) : -1;
   }
+  // saving the carries: lane-pair column of carry-pass column 64u + lane (-1 past r)
+  int sic[(R + 63) / 64];
+#pragma unroll
+  for (int u = 0; u < (R + 63) / 64; u++) {
+    const int col = 64 * u + lane;
+    sic[u] = INC == 2 && col < g.r ? lp_ic(g, ORD, perm_rc(g, col)) : -1;
+  }
   if (inc) {
     for (int idx = tid; idx < g.p * R; idx += NT4) {
       const int pp = idx / R, ic = idx % R;
       const int cc = lp_col(g, ORD, ic);
-      carryL[idx] = (h0 != nullptr && cc >= 0) ? (float)h0[((size_t)bh * g.p + pp) * g.r + cc] : 0.0f;
+      const float v = (h0 != nullptr && cc >= 0) ? (float)h0[((size_t)bh * g.p + pp) * g.r + cc] : 0.0f;
+      carryL[idx] = v;
     }
   }
 
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
   // The row work of one chunk (see the software pipeline at its call). Tokens
   // past valid_len have zero W factors and decays, so their states, and c,
   // come out as exact zeros.
-  float* dummyL = (float*)(smem + L::dummy(PP, ROT, RG, INC)) + (size_t)w * NT * 64;
+  float* dummyL = (float*)(smem + L::dummy(PP, ROT, RG, inc)) + (size_t)w * NT * 64;
   auto rows = [&](const float (&dtok)[2][4], const float (&lw)[2][CK][8 / CK]) {
     if (nrow == 0) return;
     using RV = typename std::conditional<ROT == 3, f4, fl2>::type;
@@ -325,7 +336,7 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
       }
     };
     auto load_hv = [&](int pr, float (&hv)[NT]) {
-      if constexpr (INC) {
+      if constexpr (inc) {
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) hv[ct] = carryL[pr * R + 16 * ct + n];
       } else {
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
         for (int tt = 0; tt < 2; tt++)
 #pragma unroll
           for (int i = 0; i < 4; i++) h[tt][ct][i] += dtok[tt][i] * hv[ct];
-      if constexpr (INC) {
+      if constexpr (inc) {
         // the state at the chunk's last token (lanes q = 3) enters the next chunk;
         // the other lanes, and repeated rows, store to a scratch row instead
         float* dst = (q == 3 && real) ? carryL + pr * R + n : dummyL + lane;
@@ -456,7 +467,7 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
         for (int tt = 0; tt < 2; tt++)
 #pragma unroll
           for (int i = 0; i < 4; i++) h[tt][gr * GS + u][i] += dtok[tt][i] * hv[gr * GS + u];
-      if constexpr (INC) {
+      if constexpr (inc) {
         float* dst = (q == 3 && real) ? carryL + pr * R + n : dummyL + lane;
         const int stp = (q == 3 && real) ? 16 : 64;
 #pragma unroll
@@ -658,6 +669,19 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
     // row kk+1 (carry, rotation, packing) and the W fragments of row kk+2, so the
     // single wave of the SIMD keeps its MFMA pipe fed while it does the lane work.
     // Steps past the last row work on the last row again and discard the result.
+    if constexpr (INC == 2) {
+      // With INC == 2 (one group per chain) the state entering the chunk, and the
+      // chunk's decay, are also written out in the carry pass's layout (fp32,
+      // [p][r] in its column order), so that a later backward can skip its
+      // carry pass. The rows are the wave's own, as in LDS; one store per 64
+      // consecutive columns.
+      float* dst = save + ((size_t)bh * g.NK + nc) * g.p * g.r;
+      for (int pr = w; pr < g.p; pr += 4)
+#pragma unroll
+        for (int u = 0; u < (R + 63) / 64; u++)
+          if (sic[u] >= 0) dst[(size_t)pr * g.r + 64 * u + lane] = carryL[pr * R + sic[u]];
+      if (tid == 0 && nc + 1 < g.NK) save_dec[(size_t)bh * g.NK + nc] = s_d[ELL - 1];
+    }
     rows(dtok, lw);
   }
   // ---- this wave's partials: m2 tiles (upper triangle mirrored) and m1 rows ----

@@ -99,6 +99,7 @@ struct Plan {
   bool fwd4_inc;  // ... carrying the state rows itself
   size_t carry, dec, m2p, m1p, db, dm1i, gdb;  // workspace offsets
   size_t ws_fwd, ws_bwd;
+  size_t saved;  // bytes of the saved carries: states [chains][NK][p][r], then decays [chains][NK]
 };
 
 int round_nt(int r, bool /*bf*/) {
@@ -217,6 +218,7 @@ int make_plan(const moments_desc* d, Plan* P) {
   size_t o = 0;
   P->carry = o; o = align256(o + chains * (size_t)g.NK * pr * 4);
   P->dec = o; o = align256(o + chains * (size_t)g.NK * 4);
+  P->saved = o;  // the same two regions, at the same offsets, in the caller's buffer
   const size_t base = o;
   P->m2p = o; o = align256(o + chains * (size_t)g.NGR * NW4 * P->R * P->R * 4);  // per wave for k_fwd4
   P->m1p = o; o = align256(o + chains * (size_t)g.NGR * g.p * P->R * 4);
@@ -278,12 +280,12 @@ int check_launch() {
     if (_rc != 0) return _rc; \
   } while (0)
 
+// The carry pass: states entering every kernel chunk (carry) and chunk decays
+// (dec), into the workspace or the caller's saved-carry buffer.
 template <typename T, int NT, int CK>
 int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, const T* h0,
-                      unsigned char* ws, hipStream_t st) {
+                      float* carry, float* dec, hipStream_t st) {
   const Geo& g = P.g;
-  float* carry = (float*)(ws + P.carry);
-  float* dec = (float*)(ws + P.dec);
   const int chains = g.b * g.h;
   if constexpr (std::is_same<T, bf16>::value) {
     // one sequential walk per chain when there are enough chains to fill the
@@ -319,10 +321,15 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   return 0;
 }
 
+// saved != nullptr: also leave the carries and chunk decays in the caller's
+// buffer (the carrying kernels write them; otherwise the carry pass writes there).
 template <typename T, int NT, int ROT, int CK>
 int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, const void* rot,
-            const void* h0, float* m2, float* m1, unsigned char* ws, hipStream_t st) {
+            const void* h0, float* m2, float* m1, unsigned char* ws, unsigned char* saved, hipStream_t st) {
   const Geo& g = P.g;
+  unsigned char* cbase = saved != nullptr ? saved : ws;
+  float* carry = (float*)(cbase + P.carry);
+  float* dec = (float*)(cbase + P.dec);
   const T* X = (const T*)xhat;
   const T* B = (const T*)bhat;
   const T* D = (const T*)da;
@@ -332,7 +339,7 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   const int chains = g.b * g.h;
   if constexpr (std::is_same<T, bf16>::value) {
     if (P.fwd4) {
-      if (!P.fwd4_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
+      if (!P.fwd4_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, carry, dec, st)));
       const int RG = rot_groups(g);
       auto launch = [&](auto rot_c, auto rg_c) -> int {
         constexpr int RO = decltype(rot_c)::value, RGc = decltype(rg_c)::value;
@@ -343,14 +350,16 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
           if (g.NK >= 1) {
             auto go = [&](auto m1t_c, auto inc_c) -> int {
               constexpr int M1 = decltype(m1t_c)::value;
-              constexpr bool INC = decltype(inc_c)::value == 1;
+              constexpr int INC = decltype(inc_c)::value;
               MOM_TRY(set_lds(k_fwd4<NT, RO, CK, RGc, M1, INC>, lds));
               ProfScope ps(KID_FWD, st);
               hipLaunchKernelGGL((k_fwd4<NT, RO, CK, RGc, M1, INC>), dim3(chains * g.NGR), dim3(NT4), lds, st, g, X, B,
-                                 D, Rt, INC ? nullptr : (const float*)(ws + P.carry), (const T*)h0, m2p, m1p);
+                                 D, Rt, INC ? nullptr : (const float*)carry, (const T*)h0, m2p, m1p,
+                                 INC == 2 ? carry : nullptr, INC == 2 ? dec : nullptr);
               return check_launch();
             };
-            if (P.fwd4_inc) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<1>{}) : go(IC<2>{}, IC<1>{}));
+            if (P.fwd4_inc && saved != nullptr) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<2>{}) : go(IC<2>{}, IC<2>{}));
+            else if (P.fwd4_inc) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<1>{}) : go(IC<2>{}, IC<1>{}));
             else MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<0>{}) : go(IC<2>{}, IC<0>{}));
           }
           const int nout = P.R * P.R + g.p * P.R;
@@ -371,18 +380,20 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
       }
     }
   }
-  if (!P.fwdt_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
+  // the transposed carrying forward keeps no carries: with `saved` the carry pass runs
+  const bool fwdt_inc = P.fwdt_inc && saved == nullptr;
+  if (!fwdt_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, carry, dec, st)));
   bool done = false;
   if constexpr (std::is_same<T, bf16>::value && CK <= 2) {
     if (P.fwdt && g.NK >= 1) {
       const int RT = rot_tiles(g);
       auto launch = [&](auto rot_c, auto rt_c) -> int {
         constexpr int RO = decltype(rot_c)::value, RTc = decltype(rt_c)::value;
-        const size_t lds = P.fwdt_inc ? LdsF<NT, CK>::total_inc(RTc, g.p) : LdsF<NT, CK>::total(RTc, g.p);
+        const size_t lds = fwdt_inc ? LdsF<NT, CK>::total_inc(RTc, g.p) : LdsF<NT, CK>::total(RTc, g.p);
         MOM_TRY(set_lds(k_fwdt<NT, RO, CK, RTc>, lds));
         ProfScope ps(KID_FWD, st);
         hipLaunchKernelGGL((k_fwdt<NT, RO, CK, RTc>), dim3(chains * g.NGR), dim3(NTT), lds, st, g, X, B, D, Rt,
-                           P.fwdt_inc ? nullptr : (const float*)(ws + P.carry), (const T*)h0, m2p, m1p);
+                           fwdt_inc ? nullptr : (const float*)carry, (const T*)h0, m2p, m1p);
         return check_launch();
       };
       int rc = MOMENTS_ENOTSUP;
@@ -406,7 +417,7 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
     MOM_TRY(set_lds(k_fwd<T, NT, ROT, CK>, lds));
     ProfScope ps(KID_FWD, st);
     hipLaunchKernelGGL((k_fwd<T, NT, ROT, CK>), dim3(chains * g.NGR), dim3(NTH), lds, st, g, X, B, D, Rt,
-                       (const float*)(ws + P.carry), m2p, m1p);
+                       (const float*)carry, m2p, m1p);
     MOM_TRY(check_launch());
   }
   {
@@ -421,15 +432,16 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
 template <typename T, int NT, int ROT, int CK>
 int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, const void* rot,
             const void* h0, const float* dm2, const float* dm1, void* dx, void* db, void* dda,
-            void* drot, void* dh0, unsigned char* ws, hipStream_t st) {
+            void* drot, void* dh0, unsigned char* ws, const unsigned char* saved, hipStream_t st) {
   const Geo& g = P.g;
   const T* X = (const T*)xhat;
   const T* B = (const T*)bhat;
   const T* D = (const T*)da;
   const T* Rt = (const T*)rot;
-  MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, ws, st)));
-  float* carry = (float*)(ws + P.carry);
-  float* dec = (float*)(ws + P.dec);
+  // the carries come from the caller's saved buffer, or from the carry pass
+  float* carry = saved != nullptr ? (float*)(saved + P.carry) : (float*)(ws + P.carry);
+  float* dec = saved != nullptr ? (float*)(saved + P.dec) : (float*)(ws + P.dec);
+  if (saved == nullptr) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, carry, dec, st)));
   float* Db = (float*)(ws + P.db);
   const int chains = g.b * g.h;
   bool done = false;
@@ -694,6 +706,56 @@ void* static_scratch() {
 
 }  // namespace
 
+// Shared bodies of the forward and backward entry points; `saved` (optional)
+// is the caller's saved-carry buffer of `saved_bytes`.
+static int fwd_impl(const moments_desc* desc, const void* xhat, const void* bhat, const void* da, const void* rot,
+                    const void* h0, float* m2, float* m1, void* saved, size_t saved_bytes, bool want_saved,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  MOM_TRY(make_plan(desc, &P));
+  if (!xhat || !bhat || !da || !m2 || !m1) return MOMENTS_EINVAL;
+  if (desc->rot_kind != MOMENTS_ROT_NONE && rot == nullptr) return MOMENTS_EINVAL;
+  if (want_saved && P.saved > 0 && saved == nullptr) return MOMENTS_EINVAL;
+  if (want_saved && saved_bytes < P.saved) return MOMENTS_EWORKSPACE;
+  const void* ptrs[] = {xhat, bhat, da, rot, h0, m2, m1, workspace, saved};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return MOMENTS_EINVAL;
+  if (workspace_bytes < P.ws_fwd || (P.ws_fwd > 0 && workspace == nullptr)) return MOMENTS_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  unsigned char* sv = want_saved && P.saved > 0 ? (unsigned char*)saved : nullptr;
+  return with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
+    using T = typename decltype(tt)::type;
+    return run_fwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
+        P, xhat, bhat, da, rot, h0, m2, m1, ws, sv, st);
+  });
+}
+
+static int bwd_impl(const moments_desc* desc, const void* xhat, const void* bhat, const void* da, const void* rot,
+                    const void* h0, const void* saved, size_t saved_bytes, bool use_saved, const float* d_m2,
+                    const float* d_m1, void* d_xhat, void* d_bhat, void* d_da, void* d_rot, void* d_h0,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  MOM_TRY(make_plan(desc, &P));
+  if (!xhat || !bhat || !da || !d_m2 || !d_m1) return MOMENTS_EINVAL;
+  if (desc->rot_kind != MOMENTS_ROT_NONE && rot == nullptr) return MOMENTS_EINVAL;
+  if (desc->rot_kind == MOMENTS_ROT_NONE && d_rot != nullptr) return MOMENTS_EINVAL;
+  if (use_saved && P.saved > 0 && saved == nullptr) return MOMENTS_EINVAL;
+  if (use_saved && saved_bytes < P.saved) return MOMENTS_EWORKSPACE;
+  const void* ptrs[] = {xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, workspace, saved};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return MOMENTS_EINVAL;
+  if (workspace_bytes < P.ws_bwd || (P.ws_bwd > 0 && workspace == nullptr)) return MOMENTS_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned char* ws = (unsigned char*)workspace;
+  const unsigned char* sv = use_saved && P.saved > 0 ? (const unsigned char*)saved : nullptr;
+  return with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
+    using T = typename decltype(tt)::type;
+    return run_bwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
+        P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, sv, st);
+  });
+}
+
 extern "C" {
 
 int moments_validate(const moments_desc* desc) {
@@ -711,21 +773,21 @@ int64_t moments_workspace_size(const moments_desc* desc, int is_bwd) {
 int moments_fwd(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
                 const void* rot, const void* h0, float* m2, float* m1, void* workspace,
                 size_t workspace_bytes, void* stream) {
+  return fwd_impl(desc, xhat, bhat, da, rot, h0, m2, m1, nullptr, 0, false, workspace, workspace_bytes, stream);
+}
+
+int64_t moments_saved_size(const moments_desc* desc) {
   Plan P;
-  MOM_TRY(make_plan(desc, &P));
-  if (!xhat || !bhat || !da || !m2 || !m1) return MOMENTS_EINVAL;
-  if (desc->rot_kind != MOMENTS_ROT_NONE && rot == nullptr) return MOMENTS_EINVAL;
-  const void* ptrs[] = {xhat, bhat, da, rot, h0, m2, m1, workspace};
-  for (const void* p : ptrs)
-    if (p != nullptr && !aligned16(p)) return MOMENTS_EINVAL;
-  if (workspace_bytes < P.ws_fwd || (P.ws_fwd > 0 && workspace == nullptr)) return MOMENTS_EWORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
-  unsigned char* ws = (unsigned char*)workspace;
-  return with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
-    using T = typename decltype(tt)::type;
-    return run_fwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
-        P, xhat, bhat, da, rot, h0, m2, m1, ws, st);
-  });
+  const int rc = make_plan(desc, &P);
+  if (rc != 0) return rc;
+  return (int64_t)P.saved;
+}
+
+int moments_fwd_save(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                     const void* rot, const void* h0, float* m2, float* m1, void* saved, size_t saved_bytes,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return fwd_impl(desc, xhat, bhat, da, rot, h0, m2, m1, saved, saved_bytes, true, workspace, workspace_bytes,
+                  stream);
 }
 
 int moments_fwd_static(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
@@ -744,22 +806,16 @@ int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, co
                 const void* rot, const void* h0, const float* d_m2, const float* d_m1, void* d_xhat,
                 void* d_bhat, void* d_da, void* d_rot, void* d_h0, void* workspace,
                 size_t workspace_bytes, void* stream) {
-  Plan P;
-  MOM_TRY(make_plan(desc, &P));
-  if (!xhat || !bhat || !da || !d_m2 || !d_m1) return MOMENTS_EINVAL;
-  if (desc->rot_kind != MOMENTS_ROT_NONE && rot == nullptr) return MOMENTS_EINVAL;
-  if (desc->rot_kind == MOMENTS_ROT_NONE && d_rot != nullptr) return MOMENTS_EINVAL;
-  const void* ptrs[] = {xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, workspace};
-  for (const void* p : ptrs)
-    if (p != nullptr && !aligned16(p)) return MOMENTS_EINVAL;
-  if (workspace_bytes < P.ws_bwd || (P.ws_bwd > 0 && workspace == nullptr)) return MOMENTS_EWORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
-  unsigned char* ws = (unsigned char*)workspace;
-  return with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
-    using T = typename decltype(tt)::type;
-    return run_bwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
-        P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, st);
-  });
+  return bwd_impl(desc, xhat, bhat, da, rot, h0, nullptr, 0, false, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0,
+                  workspace, workspace_bytes, stream);
+}
+
+int moments_bwd_saved(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                      const void* rot, const void* h0, const void* saved, size_t saved_bytes, const float* d_m2,
+                      const float* d_m1, void* d_xhat, void* d_bhat, void* d_da, void* d_rot, void* d_h0,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(desc, xhat, bhat, da, rot, h0, saved, saved_bytes, true, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot,
+                  d_h0, workspace, workspace_bytes, stream);
 }
 
 int64_t moments_rot_workspace_size(const moments_desc* desc, int is_bwd) {

@@ -214,3 +214,31 @@ def test_rot_binding_rejects_shapes():
         M.moments_rot_bwd(d, inc, torch.zeros(2, 16, 3))
     with pytest.raises(ValueError, match="GPU"):
         M.moments_rot_fwd(d, inc)
+
+
+# ---------------------------------------------------------------- saved-carry variant
+def test_saved_size_and_errors_without_gpu():
+    lib = _lib.load()
+    d = _desc()
+    n = M.moments_saved_size(d)
+    # fp32 states entering each 32-token kernel chunk, then the chunk decays
+    ell = M.kernel_chunk_len()
+    nk = -(-min(d.valid_len, d.s) // ell)
+    states = d.b * d.h * nk * d.p * d.r * 4
+    assert n == (states + 255) // 256 * 256 + (d.b * d.h * nk * 4 + 255) // 256 * 256
+    assert M.moments_saved_size(_desc(valid_len=0)) == 0
+    with pytest.raises(M.MomentsError):
+        M.moments_saved_size(_desc(p=0))
+    null = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    big = 1 << 40
+    rc = lib.moments_fwd_save(ctypes.byref(d), fake, fake, fake, fake, null, fake, fake, null, big, fake, big, null)
+    assert rc == _lib.EINVAL           # NULL saved buffer
+    rc = lib.moments_fwd_save(ctypes.byref(d), fake, fake, fake, fake, null, fake, fake, fake, 16, fake, big, null)
+    assert rc == _lib.EWORKSPACE       # saved buffer too small
+    args = [fake] * 5 + [null, big] + [fake] * 7 + [fake, big, null]
+    rc = lib.moments_bwd_saved(ctypes.byref(d), *args)
+    assert rc == _lib.EINVAL
+    args = [fake] * 5 + [fake, 16] + [fake] * 7 + [fake, big, null]
+    rc = lib.moments_bwd_saved(ctypes.byref(d), *args)
+    assert rc == _lib.EWORKSPACE
