@@ -16,7 +16,7 @@
  *     quaternion       : 4-blocks 4j..4j+3, j < quat_blocks, left Hamilton
  *                        product by Q = rot[b,t,h,j,:] = (w,x,y,z)
  *     coordinates outside the rotated width pass through unchanged;
- *   and the masked moments over t < V:
+ *   and the masked moments over t < V (V per sequence with desc->valid_lens):
  *     m2[b,h]     = sum_t c_t^T c_t                       ([r, r])
  *     m1[b,h,p,:] = sum_t c_t[p, :]                       ([p, r], per state row)
  *   The pages' pooled first moment m1[b,h,r] is m1.sum over p; its cotangent is
@@ -80,6 +80,15 @@ typedef struct {
   int32_t rot_kind;         /* moments_rot_kind */
   int64_t rope_dim;         /* complex modes: rotated coordinates, even, <= r */
   int64_t quat_blocks;      /* quaternion mode: J, 4*J <= r */
+  /* Per-sequence valid lengths (ragged batch), or NULL: a device array of b
+   * int32; sequence bi uses V_bi = min(max(valid_lens[bi], 0), valid_len, s)
+   * in place of the batch-wide min(valid_len, s), which still bounds every
+   * sequence and sizes the workspaces ("recalculated.rs" page, chunk_mask and
+   * the trait's valid_len: one scalar there; here the masks, and so the
+   * gradients that are exactly zero, follow each sequence's own length).
+   * The array is read by the kernels (device memory, alive until the queued
+   * work has finished); the host never reads it. */
+  const int32_t* valid_lens;
 } moments_desc;
 
 /* Host-only check of a descriptor (no GPU needed). Returns 0, MOMENTS_EINVAL or

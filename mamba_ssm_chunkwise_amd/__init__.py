@@ -14,19 +14,42 @@ from . import _lib
 from ._lib import (BF16, F32, ROT_HALF, ROT_NONE, ROT_PAIRWISE, ROT_QUAT, Desc,  # noqa: F401
                    MomentsError)
 
-__all__ = ["make_desc", "moments_validate", "moments_workspace_size", "moments_fwd", "moments_fwd_static",
+__all__ = ["make_desc", "set_valid_lens", "moments_validate", "moments_workspace_size", "moments_fwd", "moments_fwd_static",
            "moments_bwd", "moments_saved_size", "moments_fwd_save", "moments_bwd_saved", "rot_desc", "moments_rot_workspace_size", "moments_rot_fwd", "moments_rot_bwd",
            "kernel_chunk_len",
            "Desc", "MomentsError", "ROT_NONE", "ROT_PAIRWISE", "ROT_HALF", "ROT_QUAT"]
 
 
-def make_desc(xhat, bhat, chunk_len, valid_len, rot_kind, rope_dim=0, quat_blocks=0, dtype=None):
+def make_desc(xhat, bhat, chunk_len, valid_len, rot_kind, rope_dim=0, quat_blocks=0, dtype=None,
+              valid_lens=None):
     b, s, c, h, p = xhat.shape
     r = bhat.shape[-1]
     if dtype is None:
         dtype = BF16 if xhat.dtype == torch.bfloat16 else F32
-    return Desc(b, s, c, h, p, r, int(chunk_len), int(valid_len), int(dtype), int(rot_kind),
-                int(rope_dim), int(quat_blocks))
+    d = Desc(b, s, c, h, p, r, int(chunk_len), int(valid_len), int(dtype), int(rot_kind),
+             int(rope_dim), int(quat_blocks))
+    return set_valid_lens(d, valid_lens)
+
+
+def set_valid_lens(desc: Desc, valid_lens):
+    """Per-sequence valid lengths: ``valid_lens`` is an int32 GPU tensor of shape
+    [b] (or None for one length, desc.valid_len, for the whole batch). Sequence
+    bi then uses min(max(valid_lens[bi], 0), desc.valid_len, s). The descriptor
+    keeps a reference to the tensor, whose contents the kernels read."""
+    if valid_lens is None:
+        desc.valid_lens = None
+        desc._valid_lens_ref = None
+        return desc
+    if not isinstance(valid_lens, torch.Tensor):
+        raise ValueError("valid_lens must be a torch.Tensor")
+    if tuple(valid_lens.shape) != (int(desc.b),) or valid_lens.dtype != torch.int32:
+        raise ValueError(f"valid_lens must be int32 of shape ({desc.b},), got {valid_lens.dtype} "
+                         f"{tuple(valid_lens.shape)}")
+    if valid_lens.device.type != "cuda" or not valid_lens.is_contiguous():
+        raise ValueError("valid_lens must be a contiguous GPU tensor")
+    desc.valid_lens = valid_lens.data_ptr()
+    desc._valid_lens_ref = valid_lens
+    return desc
 
 
 def moments_validate(desc: Desc) -> int:
@@ -85,6 +108,12 @@ def _check_inputs(desc: Desc, xhat, bhat, da, rot, h0):
     if not isinstance(xhat, torch.Tensor):
         raise ValueError("xhat must be a torch.Tensor")
     dev = xhat.device
+    if desc.valid_lens:
+        ref = getattr(desc, "_valid_lens_ref", None)
+        if ref is None or ref.data_ptr() != desc.valid_lens:
+            raise ValueError("set per-sequence lengths with set_valid_lens (the descriptor keeps the tensor)")
+        if ref.device != dev:
+            raise ValueError(f"valid_lens is on {ref.device}, the inputs on {dev}")
     specs, dt = _input_specs(desc)
     _expect("xhat", xhat, specs["xhat"], dt, dev)
     _expect("bhat", bhat, specs["bhat"], dt, dev)

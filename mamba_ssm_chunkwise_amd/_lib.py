@@ -29,7 +29,8 @@ class Desc(ctypes.Structure):
                 ("h", ctypes.c_int64), ("p", ctypes.c_int64), ("r", ctypes.c_int64),
                 ("chunk_len", ctypes.c_int64), ("valid_len", ctypes.c_int64),
                 ("dtype", ctypes.c_int32), ("rot_kind", ctypes.c_int32),
-                ("rope_dim", ctypes.c_int64), ("quat_blocks", ctypes.c_int64)]
+                ("rope_dim", ctypes.c_int64), ("quat_blocks", ctypes.c_int64),
+                ("valid_lens", ctypes.c_void_p)]
 
 
 class MomentsError(RuntimeError):

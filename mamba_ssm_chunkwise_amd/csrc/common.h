@@ -154,7 +154,18 @@ struct Geo {
   int NGR;       // workgroups per (b,h) chain: ceil(NK / G)
   int half;      // half-split: internal state column order interleaves the halves
   int cinv;      // ceil(65536 / c): j = (k * cinv) >> 16 for the folded index k < 65536 / c
+  const int* lens;  // per-sequence valid lengths [b] (device), or nullptr: every sequence has V
 };
+
+// Valid length of sequence bi: lens[bi] clamped to [0, V] (V bounds every
+// sequence and sets the chunk count NK that sizes the grids and workspaces).
+// Kernels that mask by position replace g.V with it once bi is known; chunks
+// past a sequence's length then hold no valid token and contribute exact zeros.
+__device__ __forceinline__ int chain_len(const Geo& g, int bi) {
+  if (g.lens == nullptr) return g.V;
+  const int v = g.lens[bi];
+  return v < 0 ? 0 : (v < g.V ? v : g.V);
+}
 
 // Internal state-column order. Half-split pairs (i, r/2+i) are stored next to
 // each other (internal 2i, 2i+1) so every complex mode rotates adjacent columns.

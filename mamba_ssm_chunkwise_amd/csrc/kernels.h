@@ -206,6 +206,7 @@ __global__ __launch_bounds__(NTH, 1) void k_carry(Geo g, int PK, const T* __rest
   const int per = g.NK - 1;
   const int bh = blockIdx.x / per, n = blockIdx.x % per;
   const int bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
 
   stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(NTH, 1) void k_fwd(Geo g, const T* __restrict__ xha
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
   const int wi = w >> 1, wj = w & 1;  // this wave's m2 tiles: rows half wi, cols half wj
   const int nrounds = (g.p + 3) / 4;

@@ -52,6 +52,7 @@ __global__ __launch_bounds__(NTHB, 1) void k_bwd(
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
   const int u = w & 3, v = w >> 2;
   const int col0 = 16 * NH * v;
@@ -434,6 +435,7 @@ __global__ __launch_bounds__(NTH, 1) void k_fix(Geo g, int PK, const T* __restri
   const int per = g.NK - 1;
   const int bh = blockIdx.x / per, n = blockIdx.x % per;
   const int bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
   const int pr = g.p * g.r;
   const float* Dp = Db + ((size_t)bh * g.NK + n) * pr;
@@ -616,6 +618,7 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
   const int ng = g.NGR - 1;
   const int bh = blockIdx.x / ng, grp = blockIdx.x % ng;
   const int bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
   const int pr = g.p * g.r;
   const float* Dp = DB + ((size_t)bh * g.NGR + grp) * pr;

@@ -339,6 +339,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   // tid is refreshed through an empty asm at every chunk: the per-thread
   // addresses of the chunk-boundary work are then recomputed per chunk instead
   // of being hoisted out of the chunk loop and held (spilled) across the rounds
@@ -576,7 +577,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     __syncthreads();
 
     // ---- per-lane chunk constants (LDS tables, filled by wave 0's lanes) ----
-    const int tv = g.V - nc * ELL;  // valid tokens of this chunk (>= 1)
+    const int tv = g.V - nc * ELL;  // valid tokens of this chunk (<= 0: none)
     if (w == 0) {
       // W factors: L[16h+n][j of the slots 32ks+8q..], flattened (h*CK+ks)*(8/CK)+v
 #pragma unroll

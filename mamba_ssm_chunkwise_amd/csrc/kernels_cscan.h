@@ -64,6 +64,7 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
   float* wv = (float*)(smem + L::wv(PK));  // per buffer: exp(a_last - a_j), j < ELL; then dec
 
   const int bh = blockIdx.x, bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, q = lane >> 4;
   const int MT = PK / 16;
   const int xpr = PK / 8;  // xhat pieces per (j,c)

@@ -260,6 +260,7 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, n = lane & 15, q = lane >> 4;
@@ -639,7 +640,7 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
     __syncthreads();
 
     // ---- per-lane chunk constants -------------------------------------------
-    const int tv = g.V - nc * ELL;  // valid tokens of this chunk (>= 1)
+    const int tv = g.V - nc * ELL;  // valid tokens of this chunk (<= 0: none)
     float dtok[2][4];               // d_t at the lane's tokens 16tt + 4q + i (0 past valid_len)
 #pragma unroll
     for (int tt = 0; tt < 2; tt++) {

@@ -59,6 +59,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
 
   const int bh = blockIdx.x / g.NGR, gi = blockIdx.x % g.NGR;
   const int bi = bh / g.h, hi = bh % g.h;
+  g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   // tid is refreshed through an empty asm at every chunk, so the per-thread
   // addresses of the chunk staging are recomputed per chunk rather than held
   // (spilled) across the rounds
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(NTT, 1) void k_fwdt(Geo g, const bf16* __restrict__
     }
     store_round(fetch_round(nc, 0), 0);
     __syncthreads();
-    const int tv = g.V - nc * ELL;  // valid tokens of this chunk (>= 1)
+    const int tv = g.V - nc * ELL;  // valid tokens of this chunk (<= 0: none)
     if (w < LWE) {
       // W factor entry w: L[t][j] = exp(a_t - a_j) for j <= t (else 0) at the
       // four flattened f = (h*CK+ks)*(8/CK)+v, t = 16h + n, j of slot 32ks+8q+v

@@ -199,6 +199,7 @@ int make_plan(const moments_desc* d, Plan* P) {
   g.A = A; g.J = J; g.RW = RW;
   g.half = d->rot_kind == MOMENTS_ROT_COMPLEX_HALF;
   g.cinv = (65536 + g.c - 1) / g.c;
+  g.lens = (const int*)d->valid_lens;
   const int64_t chains = (int64_t)g.b * g.h;
   const int64_t total = chains * g.NK;
   // chunks per workgroup of the main kernels: about 512 workgroups (two per
