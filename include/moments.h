@@ -43,6 +43,14 @@
  * Errors: functions return 0 on success or a negative MOMENTS_E* code; nothing
  * is launched when a call fails validation. moments_strerror() names a code;
  * moments_last_hip_error() returns the hipError_t behind MOMENTS_EHIP.
+ *
+ * Debug check: with the environment variable MOMENTS_CHECK_FINITE set (to
+ * anything but "" or "0", read at every call), moments_fwd* and moments_bwd*
+ * scan their outputs after the work (m2 and m1; every gradient they wrote),
+ * wait for the stream, and return MOMENTS_ENONFINITE if one holds a NaN or an
+ * infinity (the pages sanitise m2 and m1 at the end of moments_phys_fwd,
+ * "recalculated.rs" source page; the sanitiser's body is not on the pages and
+ * is read as this check). The flag lives in the last 256 bytes of the workspace.
  */
 #ifndef MOMENTS_H
 #define MOMENTS_H
@@ -60,7 +68,8 @@ enum {
   MOMENTS_ENOTSUP = -2,    /* shape outside what the compiled kernels cover */
   MOMENTS_EWORKSPACE = -3, /* workspace_bytes below moments_workspace_size() */
   MOMENTS_EHIP = -4,       /* a HIP launch or runtime call failed */
-  MOMENTS_ESCRATCH = -5    /* moments_fwd_static: the problem needs more scratch than it has */
+  MOMENTS_ESCRATCH = -5,   /* moments_fwd_static: the problem needs more scratch than it has */
+  MOMENTS_ENONFINITE = -6  /* debug check (MOMENTS_CHECK_FINITE set): an output is not finite */
 };
 
 typedef enum { MOMENTS_F32 = 0, MOMENTS_BF16 = 1 } moments_dtype;

@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_build", "libmoments.so")
 
-OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5
+OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP, ESCRATCH, ENONFINITE = 0, -1, -2, -3, -4, -5, -6
 STATIC_SCRATCH_BYTES = 64 << 20
 F32, BF16 = 0, 1
 ROT_NONE, ROT_PAIRWISE, ROT_HALF, ROT_QUAT = 0, 1, 2, 3

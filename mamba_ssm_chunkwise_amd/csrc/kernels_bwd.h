@@ -756,4 +756,17 @@ __global__ __launch_bounds__(NTH) void k_zero_tail(Geo g, int z0, T* d_xhat, T* 
   fill(d_rot, (size_t)g.h * g.RW);
 }
 
+// Debug finiteness check of an output (enabled by MOMENTS_CHECK_FINITE): any
+// non-finite element sets flag[0] to 1 (every writer writes the same value).
+__global__ __launch_bounds__(NTH) void k_flag_clear(int* flag) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) flag[0] = 0;
+}
+template <typename T>
+__global__ __launch_bounds__(NTH) void k_check_finite(const T* __restrict__ x, size_t n, int* flag) {
+  const size_t stride = (size_t)gridDim.x * NTH;
+  bool bad = false;
+  for (size_t i = (size_t)blockIdx.x * NTH + threadIdx.x; i < n; i += stride) bad |= !__builtin_isfinite(to_f(x[i]));
+  if (bad) flag[0] = 1;
+}
+
 }  // namespace mom

@@ -4,7 +4,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cstdlib>
 #include <type_traits>
 #include <mutex>
 #include <vector>
@@ -100,6 +102,7 @@ struct Plan {
   size_t carry, dec, m2p, m1p, db, dm1i, gdb;  // workspace offsets
   size_t ws_fwd, ws_bwd;
   size_t saved;  // bytes of the saved carries: states [chains][NK][p][r], then decays [chains][NK]
+  size_t flag_fwd, flag_bwd;  // the finiteness check's flag (last 256 bytes of each workspace)
 };
 
 int round_nt(int r, bool /*bf*/) {
@@ -223,6 +226,8 @@ int make_plan(const moments_desc* d, Plan* P) {
   const size_t base = o;
   P->m2p = o; o = align256(o + chains * (size_t)g.NGR * NW4 * P->R * P->R * 4);  // per wave for k_fwd4
   P->m1p = o; o = align256(o + chains * (size_t)g.NGR * g.p * P->R * 4);
+  P->flag_fwd = o;
+  o += 256;
   P->ws_fwd = o;
   P->db = base;
   o = align256(base + chains * (size_t)g.NK * pr * 4);
@@ -252,6 +257,8 @@ int make_plan(const moments_desc* d, Plan* P) {
   if (P->bwdt) o = align256(o + chains * (size_t)g.p * P->R * 4);
   P->gdb = o;  // per-group boundary cotangents of the transposed backward
   if (P->bwdt) o = align256(o + chains * (size_t)g.NGR * pr * 4);
+  P->flag_bwd = o;
+  o += 256;
   P->ws_bwd = o;
   return MOMENTS_OK;
 }
@@ -534,6 +541,43 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
   return 0;
 }
 
+// Debug finiteness check (the pages' san() on the outputs), on when the
+// environment variable MOMENTS_CHECK_FINITE is set to anything but "" or "0".
+// It waits for the stream and returns MOMENTS_ENONFINITE if any listed output
+// holds a NaN or an infinity.
+bool check_finite_on() {
+  const char* e = getenv("MOMENTS_CHECK_FINITE");
+  return e != nullptr && e[0] != 0 && !(e[0] == '0' && e[1] == 0);
+}
+
+struct OutSpan {
+  const void* p;
+  size_t n;
+  bool f32;
+};
+
+int check_finite(const OutSpan* outs, int nout, unsigned char* flag_mem, hipStream_t st) {
+  int* flag = (int*)flag_mem;
+  hipLaunchKernelGGL(k_flag_clear, dim3(1), dim3(NTH), 0, st, flag);
+  MOM_TRY(check_launch());
+  for (int i = 0; i < nout; i++) {
+    if (outs[i].p == nullptr || outs[i].n == 0) continue;
+    const unsigned blocks = (unsigned)std::min<size_t>((outs[i].n + NTH - 1) / NTH, 2048);
+    if (outs[i].f32)
+      hipLaunchKernelGGL(k_check_finite<float>, dim3(blocks), dim3(NTH), 0, st, (const float*)outs[i].p, outs[i].n,
+                         flag);
+    else
+      hipLaunchKernelGGL(k_check_finite<bf16>, dim3(blocks), dim3(NTH), 0, st, (const bf16*)outs[i].p, outs[i].n,
+                         flag);
+    MOM_TRY(check_launch());
+  }
+  int host = 0;
+  hipError_t e = hipMemcpyAsync(&host, flag, sizeof(int), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  return host ? MOMENTS_ENONFINITE : 0;
+}
+
 // Calls f(TT<T>, IC<NT>, IC<ROT>, IC<CK>) for the compiled variant matching the plan.
 template <class F>
 int with_variant(const Plan& P, F&& f) {
@@ -725,11 +769,17 @@ static int fwd_impl(const moments_desc* desc, const void* xhat, const void* bhat
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
   unsigned char* sv = want_saved && P.saved > 0 ? (unsigned char*)saved : nullptr;
-  return with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
+  MOM_TRY(with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
     using T = typename decltype(tt)::type;
     return run_fwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
         P, xhat, bhat, da, rot, h0, m2, m1, ws, sv, st);
-  });
+  }));
+  if (check_finite_on()) {
+    const size_t bh = (size_t)P.g.b * P.g.h;
+    const OutSpan outs[] = {{m2, bh * P.g.r * P.g.r, true}, {m1, bh * P.g.p * P.g.r, true}};
+    return check_finite(outs, 2, ws + P.flag_fwd, st);
+  }
+  return 0;
 }
 
 static int bwd_impl(const moments_desc* desc, const void* xhat, const void* bhat, const void* da, const void* rot,
@@ -750,11 +800,20 @@ static int bwd_impl(const moments_desc* desc, const void* xhat, const void* bhat
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
   const unsigned char* sv = use_saved && P.saved > 0 ? (const unsigned char*)saved : nullptr;
-  return with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
+  MOM_TRY(with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
     using T = typename decltype(tt)::type;
     return run_bwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
         P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, sv, st);
-  });
+  }));
+  if (check_finite_on()) {
+    const Geo& g = P.g;
+    const size_t tok = (size_t)g.b * g.s;
+    const OutSpan outs[] = {{d_xhat, tok * g.c * g.h * g.p, !P.bf}, {d_bhat, tok * g.c * g.h * g.r, !P.bf},
+                            {d_da, tok * g.h, !P.bf}, {d_rot, tok * g.h * g.RW, !P.bf},
+                            {d_h0, (size_t)g.b * g.h * g.p * g.r, !P.bf}};
+    return check_finite(outs, 5, ws + P.flag_bwd, st);
+  }
+  return 0;
 }
 
 extern "C" {
@@ -844,6 +903,7 @@ const char* moments_strerror(int code) {
     case MOMENTS_EWORKSPACE: return "workspace too small";
     case MOMENTS_EHIP: return "HIP runtime error (see moments_last_hip_error)";
     case MOMENTS_ESCRATCH: return "problem needs more than the static scratch of moments_fwd_static";
+    case MOMENTS_ENONFINITE: return "an output holds a NaN or an infinity (MOMENTS_CHECK_FINITE is set)";
   }
   return "unknown error";
 }

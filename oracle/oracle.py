@@ -13,6 +13,7 @@ ROT_NONE, ROT_PAIRWISE, ROT_HALF, ROT_QUAT = 0, 1, 2, 3
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moments_oracle.c")
 _LIB = os.path.join(_HERE, "_build", "liboracle.so")
+_LIB_SAN = os.path.join(_HERE, "_build", "liboracle_san.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -26,24 +27,29 @@ def library_path() -> str:
     return _LIB
 
 
-def build() -> str:
-    """Compile the oracle with gcc (always recompiles)."""
-    os.makedirs(os.path.dirname(_LIB), exist_ok=True)
-    tmp = _LIB + ".tmp"
-    subprocess.run(["gcc", "-O3", "-march=x86-64-v3", "-fPIC", "-shared", "-std=c11", "-pthread", _SRC,
-                    "-o", tmp, "-lm"],
-                   check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+def build(sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (always recompiles). With ``sanitize``, a
+    separate AddressSanitizer + UndefinedBehaviorSanitizer build
+    (liboracle_san.so), which a process loads through MOMENTS_ORACLE_LIB with
+    gcc's libasan preloaded."""
+    out = _LIB_SAN if sanitize else _LIB
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp"
+    opt = (["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+            "-fno-sanitize-recover=undefined"] if sanitize else ["-O3", "-march=x86-64-v3"])
+    subprocess.run(["gcc", *opt, "-fPIC", "-shared", "-std=c11", "-pthread", _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
 
 
 def _load():
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            path = os.environ.get("MOMENTS_ORACLE_LIB") or _LIB
+            if path == _LIB and (not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
                 build()
-            lib = ctypes.CDLL(_LIB)
+            lib = ctypes.CDLL(path)
             dp = ctypes.POINTER(ctypes.c_double)
             ip = ctypes.POINTER(ctypes.c_int64)
             lib.oracle_fwd.argtypes = [ctypes.POINTER(_Desc)] + [dp] * 7 + [ip, ctypes.c_int64, ctypes.c_int64,
