@@ -161,7 +161,9 @@ int moments_bwd(const moments_desc* desc, const void* xhat, const void* bhat, co
  * moments_saved_size(desc) bytes (about 4 * b*h*NK*p*r), device memory, 16-byte
  * aligned, owned by the caller. A saved buffer below that size returns
  * MOMENTS_EWORKSPACE, a NULL one MOMENTS_EINVAL. Workspaces are those of
- * moments_fwd and moments_bwd. */
+ * moments_fwd and moments_bwd. For bf16 with c = 4 the backward walks token
+ * pairs, with chunk boundaries of its own, and runs its own carry pass: there
+ * moments_bwd_saved validates the buffer but does not read it. */
 int64_t moments_saved_size(const moments_desc* desc);
 int moments_fwd_save(const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
                      const void* rot, const void* h0, float* m2, float* m1, void* saved,

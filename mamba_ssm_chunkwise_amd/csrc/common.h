@@ -27,6 +27,7 @@ constexpr int NTHB = 1024; // threads per workgroup of the backward main kernel 
 constexpr int NCW = 4;     // backward: waves sharing one state row (column quarters)
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+template <int V> struct IC4 { static constexpr int value = V; };  // compile-time index tag
 typedef __bf16 bf16;
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 
@@ -155,6 +156,7 @@ struct Geo {
   int half;      // half-split: internal state column order interleaves the halves
   int cinv;      // ceil(65536 / c): j = (k * cinv) >> 16 for the folded index k < 65536 / c
   const int* lens;  // per-sequence valid lengths [b] (device), or nullptr: every sequence has V
+  int pair;         // backward over token pairs: only odd tokens carry moments (see moments.hip)
 };
 
 // Valid length of sequence bi: lens[bi] clamped to [0, V] (V bounds every

@@ -756,6 +756,65 @@ __global__ __launch_bounds__(NTH) void k_zero_tail(Geo g, int z0, T* d_xhat, T* 
   fill(d_rot, (size_t)g.h * g.RW);
 }
 
+// ---- backward over token pairs (bf16, four channels) -------------------------
+// A chain of s tokens with four channels is walked as 2s tokens of two channels
+// each: token t becomes pair tokens 2t (channels 0, 1) and 2t+1 (channels 2, 3).
+// With da 0 at 2t+1 and da_t at 2t, the state after 2t+1 is the state after t
+// (h~[t] = exp(da_t) h~[t-1] + sum over the four channels), and the xhat, bhat,
+// d_xhat and d_bhat tensors already have the pair layout ([b,s,4,h,.] is
+// [b,2s,2,h,.] in memory). Only odd pair tokens carry moments, so the backward
+// masks d_c at even ones (Geo::pair). These kernels build the pair-token da and
+// rot (and doubled per-sequence lengths) and take d_da (at 2t) and d_rot (at
+// 2t+1) back.
+// Rows of `unit`-sized pieces: U is uint4 when a token row of rot is a multiple
+// of 16 bytes, else the element type.
+template <typename T, typename U>
+__global__ __launch_bounds__(NTH) void k_pair_prep(Geo g, const T* __restrict__ da, const U* __restrict__ rot,
+                                                   int rot_units, T* __restrict__ da2, U* __restrict__ rot2,
+                                                   int* __restrict__ lens2) {
+  const size_t stride = (size_t)gridDim.x * NTH;
+  const size_t start = (size_t)blockIdx.x * NTH + threadIdx.x;
+  const size_t nda = (size_t)g.b * g.s * g.h;
+  for (size_t i = start; i < nda; i += stride) {
+    const size_t bt = i / g.h, hi = i % g.h;  // bt = bi * s + t
+    const size_t bi = bt / g.s, t = bt % g.s;
+    const size_t o = ((bi * 2 * g.s + 2 * t) * g.h + hi);
+    da2[o] = da[i];
+    da2[o + g.h] = to_t<T>(0.0f);
+  }
+  if (rot != nullptr) {
+    const size_t nrot = (size_t)g.b * g.s * rot_units;
+    for (size_t i = start; i < nrot; i += stride) {
+      const size_t bt = i / rot_units, k = i % rot_units;
+      const U v = rot[i];
+      rot2[(2 * bt) * rot_units + k] = v;
+      rot2[(2 * bt + 1) * rot_units + k] = v;
+    }
+  }
+  if (lens2 != nullptr && start < (size_t)g.b) lens2[start] = 2 * chain_len(g, (int)start);
+}
+
+template <typename T, typename U>
+__global__ __launch_bounds__(NTH) void k_pair_post(Geo g, const T* __restrict__ dda2, const U* __restrict__ drot2,
+                                                   int rot_units, T* __restrict__ d_da, U* __restrict__ d_rot) {
+  const size_t stride = (size_t)gridDim.x * NTH;
+  const size_t start = (size_t)blockIdx.x * NTH + threadIdx.x;
+  if (d_da != nullptr) {
+    const size_t nda = (size_t)g.b * g.s * g.h;
+    for (size_t i = start; i < nda; i += stride) {
+      const size_t bt = i / g.h, hi = i % g.h;
+      d_da[i] = dda2[(2 * bt) * g.h + hi];
+    }
+  }
+  if (d_rot != nullptr) {
+    const size_t nrot = (size_t)g.b * g.s * rot_units;
+    for (size_t i = start; i < nrot; i += stride) {
+      const size_t bt = i / rot_units, k = i % rot_units;
+      d_rot[i] = drot2[(2 * bt + 1) * rot_units + k];
+    }
+  }
+}
+
 // Debug finiteness check of an output (enabled by MOMENTS_CHECK_FINITE): any
 // non-finite element sets flag[0] to 1 (every writer writes the same value).
 __global__ __launch_bounds__(NTH) void k_flag_clear(int* flag) {

@@ -141,12 +141,17 @@ struct LdsT {
   static constexpr size_t Gs = red + nred * 4;
   static constexpr size_t rot = Gs + gsb;
   static_assert(Gs % 16 == 0 && rot % 16 == 0 && lw % 16 == 0 && cst % 16 == 0, "aligned regions");
-  // rotation table (RT rotated tiles): 16*RT + 4 floats per token
-  __host__ __device__ static size_t total(int RT) { return rot + (size_t)ELL * rt_pitch(16 * RT) * 4; }
-  // the rotation-gradient reduction [wave][16 tokens][8RT or 16RT] must fit the G space
+  // rotation table (RT rotated tiles), rt_pitch(16*RT) entries per token: fp32
+  // cos/sin pairs for complex modes, the bf16 input quaternions as they are
+  __host__ __device__ static size_t total(int RT, int rot_kind) {
+    return rot + (size_t)ELL * rt_pitch(16 * RT) * (rot_kind == 3 ? 2 : 4);
+  }
+  // the rotation-gradient reduction [wave][16 tokens][8RT or 16RT] runs in at
+  // most four passes over the G space
   __host__ __device__ static bool fits(int rot_kind, int RT) {
     const size_t rw = rot_kind == 3 ? (size_t)16 * RT : (size_t)8 * RT;
-    return (size_t)NWT * 16 * rw * 4 <= gsb;
+    const size_t full = (size_t)NWT * 16 * rw * 4;
+    return full <= gsb || (RT >= 2 && full <= 2 * gsb) || (RT >= 4 && full <= 4 * gsb);
   }
 };
 
@@ -228,7 +233,7 @@ struct WideStage {
       }
     }
   }
-  __device__ void store(const Geo& g, bf16* bsT, bf16* bsY, bf16* xs, float* rt, int tid) const {
+  __device__ void store(const Geo& g, bf16* bsT, bf16* bsY, bf16* xs, void* rtv, int tid) const {
 #pragma unroll
     for (int i = 0; i < NBL; i++) {
       const int idx = tid + i * NTT;
@@ -267,12 +272,10 @@ struct WideStage {
         float s0, c0, s1, c1;
         sincosf(bf16_lo(r1[i]), &s0, &c0);
         sincosf(bf16_hi(r1[i]), &s1, &c1);
-        *reinterpret_cast<f4*>(rt + tk * RTP + 4 * a2) = f4{c0, s0, c1, s1};
+        *reinterpret_cast<f4*>((float*)rtv + tk * RTP + 4 * a2) = f4{c0, s0, c1, s1};
       } else if constexpr (ROT == 3) {
         const int tk = idx / (2 * RT), e8 = idx % (2 * RT);
-        float* d = rt + tk * RTP + 8 * e8;
-        *reinterpret_cast<f4*>(d) = f4{bf16_lo(r3[i][0]), bf16_hi(r3[i][0]), bf16_lo(r3[i][1]), bf16_hi(r3[i][1])};
-        *reinterpret_cast<f4*>(d + 4) = f4{bf16_lo(r3[i][2]), bf16_hi(r3[i][2]), bf16_lo(r3[i][3]), bf16_hi(r3[i][3])};
+        *reinterpret_cast<u4*>((bf16*)rtv + tk * RTP + 8 * e8) = r3[i];  // two blocks, bf16 as loaded
       }
     }
   }
@@ -328,7 +331,17 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   float* LT = (float*)(smem + L::LT);
   float* s_a = (float*)(smem + L::a);
   float* s_d = (float*)(smem + L::d);
-  float* rt = (float*)(smem + L::rot);
+  using RTE = typename std::conditional<ROT == 3, bf16, float>::type;  // rotation table entries
+  RTE* rt = (RTE*)(smem + L::rot);
+  // four consecutive table entries as floats (a cos/sin pair of two angles, or a quaternion)
+  auto rt4 = [&](int idx) -> f4 {
+    if constexpr (ROT == 3) {
+      const uint2 v = *reinterpret_cast<const uint2*>(rt + idx);
+      return f4{bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+    } else {
+      return *reinterpret_cast<const f4*>(rt + idx);
+    }
+  };
   bf16* Gs = (bf16*)(smem + L::Gs);
   bf16* dXs = (bf16*)(smem + L::dXs);
   float* red = (float*)(smem + L::red);
@@ -562,7 +575,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           const int pos = nc * ELL + tk;
           float v = (e & 3) == 0 ? 1.0f : 0.0f;
           if ((e >> 2) < g.J && pos < g.V) v = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e];
-          rt[tk * RTP + e] = v;
+          rt[tk * RTP + e] = (RTE)v;
         }
       }
       stage_x(nc, 0);
@@ -634,7 +647,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       // One state row, all columns, this wave's 16 tokens, in two parts: the
       // states and the packed c^T, then (after a barrier that retires the
       // previous round's reads of the G blocks) everything that writes them.
-      // MASK zeroes d_c at tokens >= tv (only the chunk holding valid_len needs it).
+      // MASK zeroes d_c at tokens >= tv (only the chunk holding valid_len needs
+      // it), and at even tokens when the chain is walked in token pairs.
       const int pl = p - pblk;
       u4 cP[KSR];
       u4 hP[ROT == 3 ? KSR : 1];
@@ -680,7 +694,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           if (ks < nks) bn[ks] = ld_frag(bsT + n * KP + 32 * ks + 8 * q);
         // carry and rotation rows pipelined one column tile ahead as well
         f4 hvn = *reinterpret_cast<const f4*>(hrow + 4 * q);
-        f4 rtn = RT > 0 ? *reinterpret_cast<const f4*>(rt + t * RTP + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+        f4 rtn = RT > 0 ? rt4(t * RTP + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
           __builtin_amdgcn_sched_barrier(0);
@@ -693,7 +707,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             for (int ks = 0; ks < CK; ks++)
               if (ks < nks) bn[ks] = ld_frag(bsT + (16 * (ct + 1) + n) * KP + 32 * ks + 8 * q);
             hvn = *reinterpret_cast<const f4*>(hrow + 16 * (ct + 1) + 4 * q);
-            if (ct + 1 < RT) rtn = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * (ct + 1) + 4 * q);
+            if (ct + 1 < RT) rtn = rt4(t * RTP + 16 * (ct + 1) + 4 * q);
           }
           __builtin_amdgcn_sched_barrier(0);
           f4 hT = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -762,7 +776,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
             for (int ks = 0; ks < KSR; ks++) d = MM<bf16>::mma(sa[ks], as_bf8(cP[ks]), d);
             if constexpr (MASK) {
-              if (t >= tv) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
+              if (t >= tv || (g.pair && !(t & 1))) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
             }
             f4 hc;  // c (complex, none) or h~ (quaternion), from the packed fragments
             {
@@ -776,7 +790,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             f4 G = d;
             if constexpr (ROT == 3) {
               if (ct < RT) {
-                const f4 Q = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+                const f4 Q = rt4(t * RTP + 16 * ct + 4 * q);
                 G[0] = Q[0] * d[0] + Q[1] * d[1] + Q[2] * d[2] + Q[3] * d[3];
                 G[1] = Q[0] * d[1] - Q[1] * d[0] - Q[2] * d[3] + Q[3] * d[2];
                 G[2] = Q[0] * d[2] + Q[1] * d[3] - Q[2] * d[0] - Q[3] * d[1];
@@ -790,7 +804,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             } else {
               if constexpr (ROT == 1) {
                 if (ct < RT) {
-                  const f4 r4 = *reinterpret_cast<const f4*>(rt + t * RTP + 16 * ct + 4 * q);
+                  const f4 r4 = rt4(t * RTP + 16 * ct + 4 * q);
                   float* ra = racc[ct < RT ? ct : 0];
                   ra[0] += d[0] * hc[1] - d[1] * hc[0];
                   ra[1] += d[2] * hc[3] - d[3] * hc[2];
@@ -847,7 +861,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       if (p < g.p) row1();
       __syncthreads();  // the previous round's d_bhat reads of the G blocks are done
       if (p < g.p) {
-        if (tv >= ELL) row2(std::false_type{});
+        if (tv >= ELL && !g.pair) row2(std::false_type{});
         else row2(std::true_type{});
       }
       store_carry(pf, (round + 1) & 1);  // its buffer was last read two rounds back
@@ -971,8 +985,13 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     // through LDS behind one barrier: d_bhat in the G space, the rotation-gradient
     // partials in the (now dead) bhat tiles when they fit there
     constexpr int rw = ROT == 3 ? 16 * RTA : 8 * RTA;
-    constexpr bool RB_IN_B = (size_t)NWT * 16 * rw * 4 <= L::xs - L::bsT;
-    float* RB = RB_IN_B ? (float*)(smem + L::bsT) : (float*)Gs;  // [w][16 tokens][rw]
+    constexpr size_t RB_FULL = (size_t)NWT * 16 * rw * 4;
+    constexpr bool RB_IN_B = RB_FULL <= L::xs - L::bsT;
+    // passes over groups of rotated tiles when the partials exceed the G space
+    constexpr int NPASS = RB_IN_B || RB_FULL <= L::gsb ? 1 : RB_FULL <= 2 * L::gsb ? 2 : 4;
+    static_assert(ROT == 0 || RTA % NPASS == 0, "whole rotated tiles per pass");
+    constexpr int rwq = rw / NPASS, CTP = RTA / NPASS;  // columns and rotated tiles per pass
+    float* RB = RB_IN_B ? (float*)(smem + L::bsT) : (float*)Gs;  // [w][16 tokens][rwq]
     bf16* DBs = Gs;  // [K][SP]
     if (d_bhat != nullptr) {
 #pragma unroll
@@ -983,21 +1002,36 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           for (int i = 0; i < 4; i++)
             DBs[(16 * (kq * KH + kb) + 4 * q + i) * SP + 16 * (cq * CH + cb) + n] = (bf16)dbacc[kb][cb][i];
     }
-    auto rb_write = [&]() {
+    auto rb_write = [&](auto pass_c) {
+      constexpr int PS = decltype(pass_c)::value;
 #pragma unroll
-      for (int ct = 0; ct < RTA; ct++) {
-        float* dst = RB + (w * 16 + n) * rw;
+      for (int c = 0; c < CTP; c++) {
+        const int ct = PS * CTP + c;
+        float* dst = RB + (w * 16 + n) * rwq;
         if constexpr (ROT == 1) {
-          dst[8 * ct + 2 * q] = racc[ct][0];
-          dst[8 * ct + 2 * q + 1] = racc[ct][1];
+          dst[8 * c + 2 * q] = racc[ct][0];
+          dst[8 * c + 2 * q + 1] = racc[ct][1];
         } else {
 #pragma unroll
-          for (int v = 0; v < 4; v++) dst[4 * (4 * ct + q) + v] = racc[ct][v];
+          for (int v = 0; v < 4; v++) dst[4 * (4 * c + q) + v] = racc[ct][v];
         }
       }
     };
+    // one pass of the fixed-order sum over the waves of a token half
+    auto rb_reduce = [&](int pass) {
+      for (int idx = tid; idx < ELL * rwq; idx += NTT) {
+        const int tk = idx / rwq, el = idx % rwq, e = pass * rwq + el;
+        if (e >= g.RW) continue;
+        const int half = tk >> 4;
+        float s = 0.0f;
+#pragma unroll
+        for (int uu = 0; uu < 4; uu++) s += RB[((4 * half + uu) * 16 + (tk & 15)) * rwq + el];
+        const int pos = nc * ELL + tk;
+        if (pos < g.s) d_rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e] = (bf16)s;
+      }
+    };
     if constexpr (ROT != 0 && RB_IN_B) {
-      if (d_rot != nullptr) rb_write();
+      if (d_rot != nullptr) rb_write(IC4<0>{});
     }
     rg[(w * 4 + q) * 16 + n] = gcar;
 #pragma unroll
@@ -1034,19 +1068,21 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     // ---- rotation gradient: fixed-order sum over the waves of a token half -----
     if constexpr (ROT != 0) {
       if (d_rot != nullptr) {
-        if constexpr (!RB_IN_B) {
-          __syncthreads();  // the d_bhat reads of the shared space are done
-          rb_write();
-          __syncthreads();
-        }
-        for (int idx = tid; idx < ELL * g.RW; idx += NTT) {
-          const int tk = idx / g.RW, e = idx % g.RW;
-          const int half = tk >> 4;
-          float s = 0.0f;
-#pragma unroll
-          for (int uu = 0; uu < 4; uu++) s += RB[((4 * half + uu) * 16 + (tk & 15)) * rw + e];
-          const int pos = nc * ELL + tk;
-          if (pos < g.s) d_rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e] = (bf16)s;
+        if constexpr (RB_IN_B) {
+          rb_reduce(0);
+        } else {
+          auto one_pass = [&](auto pass_c) {
+            __syncthreads();  // the d_bhat reads (or the previous pass) of the shared space are done
+            rb_write(pass_c);
+            __syncthreads();
+            rb_reduce(decltype(pass_c)::value);
+          };
+          one_pass(IC4<0>{});
+          if constexpr (NPASS > 1) one_pass(IC4<1>{});
+          if constexpr (NPASS > 2) {
+            one_pass(IC4<2>{});
+            one_pass(IC4<3>{});
+          }
         }
       }
     }

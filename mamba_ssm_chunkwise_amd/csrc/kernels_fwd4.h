@@ -226,8 +226,6 @@ struct Stage4 {
   }
 };
 
-template <int V> struct IC4 { static constexpr int value = V; };
-
 // Index of the upper-triangle tile (a <= b) in a flat array.
 template <int NT>
 __host__ __device__ constexpr int tri(int a, int b) {

@@ -35,11 +35,12 @@ constexpr size_t kLdsLimit = 160 * 1024;
 // ---- optional per-kernel event timing (moments_profile_*) -------------------
 enum KernelId {
   KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_PREP, KID_GSCAN, KID_GFIX,
-  KID_CSCAN, KID_ROTSEG, KID_ROTCARRY, KID_ROTAPPLY, KID_N
+  KID_CSCAN, KID_ROTSEG, KID_ROTCARRY, KID_ROTAPPLY, KID_PAIR, KID_N
 };
 const char* const kKernelNames[KID_N] = {"k_carry", "k_scan",      "k_fwd",      "k_reduce", "k_bwd",  "k_dscan",
                                          "k_fix",   "k_zero_tail", "k_prep_dm1", "k_gscan",  "k_gfix",
-                                         "k_cscan", "k_rot_seg",   "k_rot_carry", "k_rot_apply"};
+                                         "k_cscan", "k_rot_seg",   "k_rot_carry", "k_rot_apply",
+                                         "k_pair"};
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -103,6 +104,10 @@ struct Plan {
   size_t ws_fwd, ws_bwd;
   size_t saved;  // bytes of the saved carries: states [chains][NK][p][r], then decays [chains][NK]
   size_t flag_fwd, flag_bwd;  // the finiteness check's flag (last 256 bytes of each workspace)
+  // backward over token pairs (bf16, c == 4): workspace regions after the pair
+  // plan's own workspace (pair-token da, rot, their gradients, lengths)
+  bool pair;
+  size_t pr_da2, pr_rot2, pr_dda2, pr_drot2, pr_lens2;
 };
 
 int round_nt(int r, bool /*bf*/) {
@@ -142,13 +147,31 @@ size_t bwdt_lds(const Geo& g, int NT, int CK) {
   const int RT = rot_tiles(g);
   auto one = [&](auto lt) -> size_t {
     using LT = typename decltype(lt)::type;
-    return LT::fits(g.rot_kind, RT) ? LT::total(RT) : 0;
+    return LT::fits(g.rot_kind, RT) ? LT::total(RT, g.rot_kind) : 0;
   };
   if (NT == 4 && CK == 1) return one(TT<LdsT<4, 1>>{});
   if (NT == 4 && CK == 2) return one(TT<LdsT<4, 2>>{});
   if (NT == 8 && CK == 1) return one(TT<LdsT<8, 1>>{});
   if (NT == 8 && CK == 2) return one(TT<LdsT<8, 2>>{});
   return 0;
+}
+
+int make_plan(const moments_desc* d, Plan* P);
+
+// Plan of the token-pair backward: 2s tokens of two channels each, twice the
+// valid length; per-sequence lengths are doubled on the device (lens2).
+int make_pair_plan(const moments_desc* d, Plan* Pv) {
+  moments_desc v = *d;
+  const int64_t V = d->valid_len < d->s ? d->valid_len : d->s;
+  v.s = 2 * d->s;
+  v.c = 2;
+  v.chunk_len = 2 * d->chunk_len;
+  v.valid_len = 2 * V;
+  v.valid_lens = nullptr;
+  const int rc = make_plan(&v, Pv);
+  if (rc != MOMENTS_OK) return rc;
+  Pv->g.pair = 1;
+  return MOMENTS_OK;
 }
 
 int make_plan(const moments_desc* d, Plan* P) {
@@ -260,6 +283,24 @@ int make_plan(const moments_desc* d, Plan* P) {
   P->flag_bwd = o;
   o += 256;
   P->ws_bwd = o;
+  P->pair = false;
+  if (bf && d->c == 4) {
+    // four channels: the backward walks token pairs of two channels each with the
+    // transposed kernel (the general kernel's registers do not hold four channels)
+    Plan Pv;
+    if (make_pair_plan(d, &Pv) == MOMENTS_OK && Pv.bwdt) {
+      const size_t tok = (size_t)g.b * g.s;
+      size_t q = align256(Pv.ws_bwd);
+      P->pr_da2 = q; q = align256(q + 2 * tok * g.h * 2);
+      P->pr_rot2 = q; q = align256(q + 2 * tok * g.h * g.RW * 2);
+      P->pr_dda2 = q; q = align256(q + 2 * tok * g.h * 2);
+      P->pr_drot2 = q; q = align256(q + 2 * tok * g.h * g.RW * 2);
+      P->pr_lens2 = q; q = align256(q + (size_t)g.b * 4);
+      P->flag_bwd = q;
+      P->ws_bwd = q + 256;
+      P->pair = true;
+    }
+  }
   return MOMENTS_OK;
 }
 
@@ -466,7 +507,7 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
       const int RT = rot_tiles(g);
       auto launch = [&](auto rot_c, auto rt_c) -> int {
         constexpr int RO = decltype(rot_c)::value, RTc = decltype(rt_c)::value;
-        const size_t lds = LdsT<NT, CK>::total(RTc);
+        const size_t lds = LdsT<NT, CK>::total(RTc, RO);
         MOM_TRY(set_lds(k_bwdt<NT, RO, CK, RTc>, lds));
         ProfScope ps(KID_BWD, st);
         hipLaunchKernelGGL((k_bwdt<NT, RO, CK, RTc>), dim3(chains * g.NGR), dim3(NTT), lds, st, g, X, B, D, Rt,
@@ -751,6 +792,61 @@ void* static_scratch() {
 
 }  // namespace
 
+// Backward over token pairs (see k_pair_prep): pair-token da and rot are built
+// in the workspace, the transposed backward runs on the pair plan (d_xhat and
+// d_bhat land in place: the layouts coincide), and d_da, d_rot are taken back.
+static int run_pair_bwd(const Plan& P, const moments_desc* desc, const void* xhat, const void* bhat, const void* da,
+                        const void* rot, const void* h0, const float* d_m2, const float* d_m1, void* d_xhat,
+                        void* d_bhat, void* d_da, void* d_rot, void* d_h0, unsigned char* ws, hipStream_t st) {
+  Plan Pv;
+  MOM_TRY(make_pair_plan(desc, &Pv));
+  const Geo& g = P.g;
+  bf16* da2 = (bf16*)(ws + P.pr_da2);
+  bf16* rot2 = (bf16*)(ws + P.pr_rot2);
+  bf16* dda2 = (bf16*)(ws + P.pr_dda2);
+  bf16* drot2 = (bf16*)(ws + P.pr_drot2);
+  int* lens2 = g.lens != nullptr ? (int*)(ws + P.pr_lens2) : nullptr;
+  Pv.g.lens = lens2;
+  const size_t row_bytes = (size_t)g.h * g.RW * sizeof(bf16);
+  const bool wide = row_bytes % 16 == 0;
+  const int units = (int)(wide ? row_bytes / 16 : (size_t)g.h * g.RW);
+  const size_t work = (size_t)g.b * g.s * (size_t)(units > g.h ? units : g.h);
+  const unsigned blocks = (unsigned)std::min<size_t>((work + NTH - 1) / NTH, 8192);
+  {
+    ProfScope ps(KID_PAIR, st);
+    if (wide)
+      hipLaunchKernelGGL((k_pair_prep<bf16, uint4>), dim3(blocks), dim3(NTH), 0, st, g, (const bf16*)da,
+                         (const uint4*)rot, units, da2, (uint4*)rot2, lens2);
+    else
+      hipLaunchKernelGGL((k_pair_prep<bf16, bf16>), dim3(blocks), dim3(NTH), 0, st, g, (const bf16*)da,
+                         (const bf16*)rot, units, da2, rot2, lens2);
+    MOM_TRY(check_launch());
+  }
+  unsigned char* wsv = ws;  // the pair plan's workspace is the first Pv.ws_bwd bytes
+  MOM_TRY(with_variant(Pv, [&](auto tt, auto nt, auto rk, auto ck) {
+    using T = typename decltype(tt)::type;
+    constexpr int CK = decltype(ck)::value;
+    if constexpr (!std::is_same<T, bf16>::value || CK != 2) {
+      return MOMENTS_ENOTSUP;
+    } else {
+      return run_bwd<T, decltype(nt)::value, decltype(rk)::value, CK>(
+          Pv, xhat, bhat, da2, rot != nullptr ? rot2 : nullptr, h0, d_m2, d_m1, d_xhat, d_bhat,
+          d_da != nullptr ? dda2 : nullptr, d_rot != nullptr ? drot2 : nullptr, d_h0, wsv, nullptr, st);
+    }
+  }));
+  if (d_da != nullptr || d_rot != nullptr) {
+    ProfScope ps(KID_PAIR, st);
+    if (wide)
+      hipLaunchKernelGGL((k_pair_post<bf16, uint4>), dim3(blocks), dim3(NTH), 0, st, g, (const bf16*)dda2,
+                         (const uint4*)drot2, units, (bf16*)d_da, (uint4*)d_rot);
+    else
+      hipLaunchKernelGGL((k_pair_post<bf16, bf16>), dim3(blocks), dim3(NTH), 0, st, g, (const bf16*)dda2,
+                         (const bf16*)drot2, units, (bf16*)d_da, (bf16*)d_rot);
+    MOM_TRY(check_launch());
+  }
+  return 0;
+}
+
 // Shared bodies of the forward and backward entry points; `saved` (optional)
 // is the caller's saved-carry buffer of `saved_bytes`.
 static int fwd_impl(const moments_desc* desc, const void* xhat, const void* bhat, const void* da, const void* rot,
@@ -800,11 +896,17 @@ static int bwd_impl(const moments_desc* desc, const void* xhat, const void* bhat
   hipStream_t st = (hipStream_t)stream;
   unsigned char* ws = (unsigned char*)workspace;
   const unsigned char* sv = use_saved && P.saved > 0 ? (const unsigned char*)saved : nullptr;
-  MOM_TRY(with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
-    using T = typename decltype(tt)::type;
-    return run_bwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
-        P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, sv, st);
-  }));
+  if (P.pair) {
+    // the token-pair walk computes its own carries (at its chunk boundaries), so
+    // a saved buffer is not read here
+    MOM_TRY(run_pair_bwd(P, desc, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, st));
+  } else {
+    MOM_TRY(with_variant(P, [&](auto tt, auto nt, auto rk, auto ck) {
+      using T = typename decltype(tt)::type;
+      return run_bwd<T, decltype(nt)::value, decltype(rk)::value, decltype(ck)::value>(
+          P, xhat, bhat, da, rot, h0, d_m2, d_m1, d_xhat, d_bhat, d_da, d_rot, d_h0, ws, sv, st);
+    }));
+  }
   if (check_finite_on()) {
     const Geo& g = P.g;
     const size_t tok = (size_t)g.b * g.s;

@@ -69,6 +69,11 @@ SMALL = [
     (W.ROT_PAIRWISE, "f32", dict(da_mu=-4.0, da_shift=0.06)),
     (W.ROT_HALF, "bf16", dict(c=2, p=64, r=128, rope_dim=64, valid_len=96, da_mu=-4.0, da_shift=0.06)),
     (W.ROT_QUAT, "bf16", dict(c=4, p=33, r=128, quat_blocks=32, valid_len=100, da_mu=-4.0, da_shift=0.04)),
+    # four channels (backward over token pairs): rotation rows that are not a
+    # multiple of 16 bytes, no rotation, no initial state, a partial last chunk
+    (W.ROT_PAIRWISE, "bf16", dict(c=4, p=16, r=32, rope_dim=6, valid_len=90)),
+    (W.ROT_NONE, "bf16", dict(c=4, p=37, r=64, valid_len=95)),
+    (W.ROT_QUAT, "bf16", dict(c=4, p=128, r=128, quat_blocks=32, valid_len=77, h0_sd=None)),
 ]
 
 
