@@ -175,6 +175,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_pairwise_b8_s8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--ragged", action="store_true",
+                    help="per-sequence valid lengths (seeded, uniform in [V/4, V]); tokens = their sum")
     ap.add_argument("--saved-carry", action="store_true",
                     help="time the saved-carry variant: moments_fwd_save keeps the chunk-boundary states, "
                          "moments_bwd_saved reads them instead of running its carry pass")
@@ -199,6 +201,12 @@ def main():
     t = W.generate(w, device=dev)
     d = M.Desc(w.b, w.s, w.c, w.h, w.p, w.r, w.chunk_len, w.valid_len,
                M.BF16 if w.dtype == "bf16" else M.F32, w.rot_kind, w.rope_dim, w.quat_blocks)
+    lens = None
+    if args.ragged:
+        gl = torch.Generator().manual_seed(w.seed + 31)
+        V = min(w.valid_len, w.s)
+        lens = torch.randint(max(V // 4, 1), V + 1, (w.b,), generator=gl, dtype=torch.int32)
+        M.set_valid_lens(d, lens.to(dev))
     ws = torch.empty(max(M.moments_workspace_size(d, False), M.moments_workspace_size(d, True)),
                      dtype=torch.uint8, device=dev)
     m2 = torch.empty(w.b, w.h, w.r, w.r, dtype=torch.float32, device=dev)
@@ -238,7 +246,7 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps
     prof = M.profile_read()
     V = min(w.valid_len, w.s)
-    tokens = w.b * V
+    tokens = w.b * V if lens is None else int(lens.clamp(0, V).sum())
     value = tokens / (ms / 1e3)
 
     ell = M.kernel_chunk_len()
@@ -315,7 +323,8 @@ def main():
         "config": {"workload": w.name, "b": w.b, "s": w.s, "valid_len": w.valid_len, "c": w.c, "h": w.h,
                    "p": w.p, "r": w.r, "chunk_len": w.chunk_len, "rot_kind": w.rot_kind,
                    "rope_dim": w.rope_dim, "quat_blocks": w.quat_blocks, "parallelism": "none",
-                   "saved_carry": bool(args.saved_carry)},
+                   "saved_carry": bool(args.saved_carry),
+                   "valid_lens": None if lens is None else [int(x) for x in lens]},
         "roofline": roof,
         "step_roofline": step_roof,
         "cpu_baseline": cpu,

@@ -157,7 +157,13 @@ struct Geo {
   int cinv;      // ceil(65536 / c): j = (k * cinv) >> 16 for the folded index k < 65536 / c
   const int* lens;  // per-sequence valid lengths [b] (device), or nullptr: every sequence has V
   int pair;         // backward over token pairs: only odd tokens carry moments (see moments.hip)
+  int skip;         // with per-sequence lengths: chunks past a sequence's length are not walked
+                    // (set only when every kernel of the call skips them the same way)
 };
+
+// Kernel chunks a sequence walks: all NK, or with `skip` only those holding a
+// valid token of the sequence (g.V already holds its length).
+__device__ __forceinline__ int chain_nk(const Geo& g) { return g.skip ? (g.V + ELL - 1) / ELL : g.NK; }
 
 // Valid length of sequence bi: lens[bi] clamped to [0, V] (V bounds every
 // sequence and sets the chunk count NK that sizes the grids and workspaces).

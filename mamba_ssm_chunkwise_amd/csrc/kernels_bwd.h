@@ -565,23 +565,30 @@ __global__ __launch_bounds__(NTH) void k_gscan(Geo g, const float* __restrict__ 
   const int e = blockIdx.y * NTH + threadIdx.x;
   const int pr = g.p * g.r;
   if (e >= pr) return;
+  g.V = chain_len(g, bh / g.h);
+  // groups holding walked chunks (the others enter nothing: their D_B is zero)
+  const int nkc = chain_nk(g), ngc = (nkc + g.G - 1) / g.G;
   const float* Dc = dec + (size_t)bh * g.NK;
-  auto qprod = [&](int gr) {  // Q over the whole group gr (its chunks are all < NK-1 here)
-    const int a = gr * g.G, b = (a + g.G < g.NK) ? a + g.G : g.NK;
+  auto qprod = [&](int gr) {  // Q over the whole group gr (its chunks are all < nkc-1 here)
+    const int a = gr * g.G, b = (a + g.G < nkc) ? a + g.G : nkc;
     float qv = 1.0f;
     for (int k = a; k < b; k++) qv *= Dc[k];
     return qv;
   };
   float D = 0.0f;  // D_B(g + 1) while walking down
   for (int gr = g.NGR - 2; gr >= 0; gr--) {
+    if (gr + 1 >= ngc) {
+      DB[((size_t)bh * g.NGR + gr) * pr + e] = 0.0f;
+      continue;
+    }
     const int n0n = (gr + 1) * g.G;
     const float din = Db[((size_t)bh * g.NK + n0n) * pr + e];
-    D = (gr + 1 < g.NGR - 1) ? din + qprod(gr + 1) * D : din;
+    D = (gr + 1 < ngc - 1) ? din + qprod(gr + 1) * D : din;
     DB[((size_t)bh * g.NGR + gr) * pr + e] = D;
   }
   if (d_h0 != nullptr) {
-    float d0 = g.NK > 0 ? Db[(size_t)bh * g.NK * pr + e] : 0.0f;
-    if (g.NGR > 1) d0 += qprod(0) * D;
+    float d0 = nkc > 0 ? Db[(size_t)bh * g.NK * pr + e] : 0.0f;
+    if (ngc > 1) d0 += qprod(0) * D;
     const int p0 = e / g.r, rc = e % g.r;
     d_h0[((size_t)bh * g.p + p0) * g.r + perm_rc(g, rc)] = to_t<T>(d0);
   }
@@ -619,6 +626,8 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
   const int bh = blockIdx.x / ng, grp = blockIdx.x % ng;
   const int bi = bh / g.h, hi = bh % g.h;
   g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
+  // nothing enters a group whose successor holds no walked chunk
+  if (grp + 1 >= (chain_nk(g) + g.G - 1) / g.G) return;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
   const int pr = g.p * g.r;
   const float* Dp = DB + ((size_t)bh * g.NGR + grp) * pr;
@@ -734,26 +743,37 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
   }
 }
 
-// Zeros for every gradient at positions [z0, s) (chunks never processed).
+// Zeros for every gradient at positions [z0, s) (chunks never processed); with
+// `skip`, from each sequence's first unwalked chunk (grid y = sequence).
 template <typename T>
 __global__ __launch_bounds__(NTH) void k_zero_tail(Geo g, int z0, T* d_xhat, T* d_bhat, T* d_da,
                                                    T* d_rot) {
-  const size_t npos = (size_t)(g.s - z0);
   const size_t stride = (size_t)gridDim.x * NTH;
   const size_t start = (size_t)blockIdx.x * NTH + threadIdx.x;
   const T zero = to_t<T>(0.0f);
-  auto fill = [&](T* ptr, size_t per_pos) {
-    if (ptr == nullptr) return;
-    const size_t total = (size_t)g.b * npos * per_pos;
-    for (size_t i = start; i < total; i += stride) {
-      const size_t bi = i / (npos * per_pos), rest = i % (npos * per_pos);
-      ptr[((size_t)bi * g.s + z0) * per_pos + rest] = zero;
+  const int V0 = g.V;
+  // without skip one pass covers every sequence from z0; with it, sequence by sequence
+  for (int bfirst = g.skip ? (int)blockIdx.y : 0; bfirst < g.b; bfirst += g.skip ? (int)gridDim.y : g.b) {
+    const int bend = g.skip ? bfirst + 1 : g.b;
+    if (g.skip) {
+      g.V = V0;
+      g.V = chain_len(g, bfirst);
+      z0 = chain_nk(g) * ELL;
     }
-  };
-  fill(d_xhat, (size_t)g.c * g.h * g.p);
-  fill(d_bhat, (size_t)g.c * g.h * g.r);
-  fill(d_da, (size_t)g.h);
-  fill(d_rot, (size_t)g.h * g.RW);
+    const size_t npos = (size_t)(g.s > z0 ? g.s - z0 : 0);
+    auto fill = [&](T* ptr, size_t per_pos) {
+      if (ptr == nullptr) return;
+      const size_t total = (size_t)(bend - bfirst) * npos * per_pos;
+      for (size_t i = start; i < total; i += stride) {
+        const size_t bi = bfirst + i / (npos * per_pos), rest = i % (npos * per_pos);
+        ptr[((size_t)bi * g.s + z0) * per_pos + rest] = zero;
+      }
+    };
+    fill(d_xhat, (size_t)g.c * g.h * g.p);
+    fill(d_bhat, (size_t)g.c * g.h * g.r);
+    fill(d_da, (size_t)g.h);
+    fill(d_rot, (size_t)g.h * g.RW);
+  }
 }
 
 // ---- backward over token pairs (bf16, four channels) -------------------------

@@ -461,7 +461,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     if (wide) wst.load(g, xhat, bhat, rot, ncl, bi, hi, tid);
   };
   const int n0 = gi * g.G;
-  const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
+  const int nkc = chain_nk(g);  // chunks walked
+  const int n1 = (n0 + g.G < nkc) ? n0 + g.G : nkc;
   const int nrounds = (g.p + 3) / 4;
   // ---- d_da of chunk ncs: sum_{t>=s} d_t <G[t], h_-> + sum_{s'<s} (C[s'] - Rw[s']),
   // from the per-wave partials the chunk left in LDS (and its s_d, which the

@@ -163,10 +163,11 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
 #pragma unroll
   for (int nt = 0; nt < NT; nt++) icol[nt] = 16 * nt + m < g.r ? inv_perm_rc(g, 16 * nt + m) : 0;
 
-  if (g.NK > 1) store(fetch(0), 0);
+  const int nkc = chain_nk(g);  // chunks walked (carries past them are not written)
+  if (nkc > 1) store(fetch(0), 0);
   __syncthreads();
-  for (int nc = 0; nc < g.NK; nc++) {
-    const bool more = nc + 2 < g.NK;  // chunk nc+1 contributes U only if it is not the last
+  for (int nc = 0; nc < nkc; nc++) {
+    const bool more = nc + 2 < nkc;  // chunk nc+1 contributes U only if it is not the last
     Pf pf;
     if (more) pf = fetch(nc + 1);
     float* out = carry + ((size_t)bh * g.NK + nc) * pr;
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
         }
       }
     }
-    if (nc + 1 < g.NK) {
+    if (nc + 1 < nkc) {
       const int b = nc & 1;
       const float* wb = wv + b * (ELL + 4);
       const float dn = wb[ELL];

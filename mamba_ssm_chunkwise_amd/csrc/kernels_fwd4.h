@@ -579,7 +579,8 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
   };
 
   const int n0 = gi * g.G;
-  const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
+  const int nkc = chain_nk(g);  // chunks walked
+  const int n1 = (n0 + g.G < nkc) ? n0 + g.G : nkc;
   using ST = Stage4<NT, CK, ROT, RG>;
   const bool wide = ST::usable(g);
   ST st;

@@ -373,8 +373,13 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
 // saved != nullptr: also leave the carries and chunk decays in the caller's
 // buffer (the carrying kernels write them; otherwise the carry pass writes there).
 template <typename T, int NT, int ROT, int CK>
-int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, const void* rot,
+int run_fwd(const Plan& P0, const void* xhat, const void* bhat, const void* da, const void* rot,
             const void* h0, float* m2, float* m1, unsigned char* ws, unsigned char* saved, hipStream_t st) {
+  // with per-sequence lengths the lane-pair forward and its carry pass skip the
+  // chunks past each sequence (a saved buffer then holds only the walked chunks,
+  // which only the transposed backward reads alike)
+  Plan P = P0;
+  P.g.skip = P.g.lens != nullptr && std::is_same<T, bf16>::value && P.fwd4 && (saved == nullptr || P.bwdt);
   const Geo& g = P.g;
   unsigned char* cbase = saved != nullptr ? saved : ws;
   float* carry = (float*)(cbase + P.carry);
@@ -479,9 +484,13 @@ int run_fwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
 }
 
 template <typename T, int NT, int ROT, int CK>
-int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, const void* rot,
+int run_bwd(const Plan& P0, const void* xhat, const void* bhat, const void* da, const void* rot,
             const void* h0, const float* dm2, const float* dm1, void* dx, void* db, void* dda,
             void* drot, void* dh0, unsigned char* ws, const unsigned char* saved, hipStream_t st) {
+  // with per-sequence lengths the transposed path (carry pass, walk, group
+  // fix-ups, zero fill) skips the chunks past each sequence
+  Plan P = P0;
+  P.g.skip = P.g.lens != nullptr && std::is_same<T, bf16>::value && CK <= 2 && P.bwdt && P.g.NK >= 1;
   const Geo& g = P.g;
   const T* X = (const T*)xhat;
   const T* B = (const T*)bhat;
@@ -573,10 +582,11 @@ int run_bwd(const Plan& P, const void* xhat, const void* bhat, const void* da, c
     MOM_TRY(check_launch());
   }
   const int z0 = g.NK * ELL;
-  if (z0 < g.s) {
+  if (z0 < g.s || g.skip) {
     ProfScope ps(KID_ZERO, st);
-    hipLaunchKernelGGL((k_zero_tail<T>), dim3(1024), dim3(NTH), 0, st, g, z0, (T*)dx, (T*)db, (T*)dda,
-                       (T*)drot);
+    hipLaunchKernelGGL((k_zero_tail<T>), dim3(g.skip ? 256 : 1024, g.skip ? std::min(g.b, 65535) : 1), dim3(NTH), 0,
+                       st, g, z0,
+                       (T*)dx, (T*)db, (T*)dda, (T*)drot);
     MOM_TRY(check_launch());
   }
   return 0;
