@@ -210,16 +210,56 @@ __global__ __launch_bounds__(NTH, 1) void k_carry(Geo g, int PK, const T* __rest
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, m = lane & 15, q = lane >> 4;
 
   stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
-  stage_bhat<T, R, CK>(g, bhat, bi, hi, n, bs);
-  __syncthreads();
+  // bf16 rows of 16-byte pieces (p and r multiples of 8): one wide load per 8
+  // values, work items over (j,c) fastest so the LDS writes of a wave are
+  // consecutive; otherwise element by element
+  constexpr bool BF = sizeof(T) == 2;
+  const bool wide = BF && g.p % 8 == 0 && g.r % 8 == 0;
   const float* wl = s_L + (ELL - 1) * (ELL + 1);  // L[l-1][j] = exp(a_last - a_j)
-  for (int idx = threadIdx.x; idx < K * PK; idx += NTH) {
-    const int k = idx / PK, pp = idx % PK;
-    const int j = k / CK, ci = k % CK;
-    const int pos = n * ELL + j;
-    float v = 0.0f;
-    if (pp < g.p && ci < g.c) v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp]) * wl[j];
-    as[pp * KP + k] = to_t<T>(v);
+  if constexpr (BF) {
+    if (wide) {
+      for (int idx = threadIdx.x; idx < K * (R / 8); idx += NTH) {
+        const int k = idx % K, c8 = idx / K;
+        const int j = k / CK, ci = k % CK, pos = n * ELL + j;
+        u4 v = u4{0u, 0u, 0u, 0u};
+        if (8 * c8 < g.r && pos < g.V && ci < g.c)
+          v = *reinterpret_cast<const u4*>(bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8);
+        const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+          const int cc = 8 * c8 + u;  // caller column; internal columns interleave half-split pairs
+          bs[(cc < g.r ? inv_perm_rc(g, cc) : cc) * KP + k] = e[u];
+        }
+      }
+    }
+  }
+  if (!wide) stage_bhat<T, R, CK>(g, bhat, bi, hi, n, bs);
+  __syncthreads();  // the decays (wl) are staged
+  if constexpr (BF) {
+    if (wide) {
+      for (int idx = threadIdx.x; idx < K * (PK / 8); idx += NTH) {
+        const int k = idx % K, p8 = idx / K;
+        const int j = k / CK, ci = k % CK, pos = n * ELL + j;
+        u4 v = u4{0u, 0u, 0u, 0u};
+        if (8 * p8 < g.p && pos < g.V && ci < g.c)
+          v = *reinterpret_cast<const u4*>(xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + 8 * p8);
+        const T* e = reinterpret_cast<const T*>(&v);
+        const float f = wl[j];
+#pragma unroll
+        for (int u = 0; u < 8; u++) as[(8 * p8 + u) * KP + k] = to_t<T>(to_f(e[u]) * f);
+      }
+    }
+  }
+  if (!wide) {
+    for (int idx = threadIdx.x; idx < K * PK; idx += NTH) {
+      const int k = idx / PK, pp = idx % PK;
+      const int j = k / CK, ci = k % CK;
+      const int pos = n * ELL + j;
+      float v = 0.0f;
+      if (pp < g.p && ci < g.c && pos < g.V)
+        v = to_f(xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp]) * wl[j];
+      as[pp * KP + k] = to_t<T>(v);
+    }
   }
   __syncthreads();
   const int MT = PK / 16;
