@@ -258,7 +258,9 @@ def main():
     dom = max(per_kernel, key=lambda k: per_kernel[k][0] * per_kernel[k][1])
     avg_ms = per_kernel[dom][1]
     a = alg.get(dom, {"flops": 0, "bytes": 0})
-    kname = {"k_bwd": "k_bwdt", "k_fwd": "k_fwdt"}.get(dom, dom) if w.dtype == "bf16" and w.c <= 2 else dom
+    # the profiled kernel behind the library's name: the bf16 forward is the
+    # lane-pair kernel, the bf16 backward the transposed one (c = 4 walks token pairs)
+    kname = {"k_bwd": "k_bwdt", "k_fwd": "k_fwd4"}.get(dom, dom) if w.dtype == "bf16" and w.c != 3 else dom
     traffic = stored_traffic(kname, w.name)
     if a["flops"] > 0:
         peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
