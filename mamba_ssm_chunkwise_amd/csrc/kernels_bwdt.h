@@ -48,6 +48,14 @@ constexpr int NTT = 64 * NWT;   // threads of k_bwdt
 constexpr int LTP = 36;         // row pitch of LT[j][t] (floats)
 constexpr int XPB = 32;         // state rows per staged xhat block
 
+// Token slots of a chunk. A chain walked in token pairs (four channels: pair
+// token 2t holds channels 0, 1 of token t, pair token 2t+1 channels 2, 3) puts
+// its even pair tokens in slots 0..15 and its odd ones in slots 16..31, so the
+// first token half of the backward holds exactly the pair tokens whose d_c
+// vanish; slot s holds pair token 2 (s mod 16) + s / 16. Otherwise slot = token.
+__host__ __device__ __forceinline__ int slot_tok(const Geo& g, int s) { return g.pair ? 2 * (s & 15) + (s >> 4) : s; }
+__host__ __device__ __forceinline__ int tok_slot(const Geo& g, int t) { return g.pair ? 16 * (t & 1) + (t >> 1) : t; }
+
 // Column-contracting fragments built from accumulator registers: K-slot
 // 32ks + 8q + e holds state column 32ks + 16(e/4) + 4q + e%4, i.e. register
 // e%4 of column tile 2ks + e/4 in lane group q.
@@ -187,7 +195,7 @@ struct WideStage {
     for (int i = 0; i < NXL; i++) {
       const int idx = tid + i * NTT;
       const int k = idx % K, c8 = idx / K;
-      const int j = k / CK, ci = k % CK, pos = nc * ELL + j;
+      const int j = k / CK, ci = k % CK, pos = nc * ELL + slot_tok(g, j);
       xv[i] = u4{0u, 0u, 0u, 0u};
       if (idx < NXU && pblk + 8 * c8 < g.p && ci < g.c && pos < g.V)
         xv[i] = *reinterpret_cast<const u4*>(xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + 8 * c8);
@@ -210,7 +218,7 @@ struct WideStage {
     for (int i = 0; i < NBL; i++) {
       const int idx = tid + i * NTT;
       const int k = idx % K, c8 = idx / K;
-      const int j = k / CK, ci = k % CK, pos = nc * ELL + j;
+      const int j = k / CK, ci = k % CK, pos = nc * ELL + slot_tok(g, j);
       bv[i] = u4{0u, 0u, 0u, 0u};
       if (idx < NBU && 8 * c8 < g.r && ci < g.c && pos < g.V)
         bv[i] = *reinterpret_cast<const u4*>(bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8);
@@ -220,12 +228,12 @@ struct WideStage {
     for (int i = 0; i < NRL; i++) {
       const int idx = tid + i * NTT;
       if constexpr (ROT == 1) {
-        const int tk = idx / (4 * RT), a2 = idx % (4 * RT), pos = nc * ELL + tk;
+        const int tk = idx / (4 * RT), a2 = idx % (4 * RT), pos = nc * ELL + slot_tok(g, tk);
         r1[i] = 0u;
         if (idx < NRU && 2 * a2 < g.A && pos < g.V)
           r1[i] = *reinterpret_cast<const unsigned*>(rot + (((size_t)bi * g.s + pos) * g.h + hi) * g.RW + 2 * a2);
       } else if constexpr (ROT == 3) {
-        const int tk = idx / (2 * RT), e8 = idx % (2 * RT), pos = nc * ELL + tk;
+        const int tk = idx / (2 * RT), e8 = idx % (2 * RT), pos = nc * ELL + slot_tok(g, tk);
         const unsigned one = 0x3f80u;  // bf16 1.0: identity quaternions (1, 0, 0, 0)
         r3[i] = u4{one, 0u, one, 0u};
         if (idx < NRU && 2 * e8 < g.J && pos < g.V)
@@ -360,7 +368,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform in the wave
   const int lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int u = w & 3, tt = w >> 2;       // row slot of the round, token half
-  const int t = 16 * tt + n;              // this lane's token in the transposed tiles
+  const int t = 16 * tt + n;              // this lane's token slot in the transposed tiles
+  const int ptk = slot_tok(g, t);         // and its token
   const int kq = w / CW, cq = w % CW;     // d_bhat block of this wave
 
   // S = d_m2 + d_m2^T: rows internal columns, K-slots in col_of_slot order.
@@ -385,7 +394,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     for (int idx = tid; idx < K * XPB; idx += NTT) {
       const int k = idx / XPB, pl = idx % XPB;
       const int j = k / CK, ci = k % CK;
-      const int pos = nc * ELL + j;
+      const int pos = nc * ELL + slot_tok(g, j);
       float v = 0.0f;
       if (pblk + pl < g.p && ci < g.c && pos < g.V)
         v = (float)xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + pl];
@@ -401,7 +410,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       for (int idx = tid; idx < NXU; idx += NTT) {
         const int k = idx % K, c8 = idx / K;
         const int j = k / CK, ci = k % CK;
-        const int pos = nc * ELL + j;
+        const int pos = nc * ELL + slot_tok(g, j);
         if (ci < g.c && pos < g.s && pblk + 8 * c8 < g.p) {
           u4 v;
 #pragma unroll
@@ -417,7 +426,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     for (int idx = tid; idx < K * rows; idx += NTT) {
       const int k = idx / rows, pl = idx % rows;
       const int j = k / CK, ci = k % CK;
-      const int pos = nc * ELL + j;
+      const int pos = nc * ELL + slot_tok(g, j);
       if (ci < g.c && pos < g.s)
         d_xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + pl] = dXs[pl * KP + k];
     }
@@ -475,22 +484,22 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     // lane t < 32: x = d_t <G[t], h_->, y = C[t] - Rw[t]; then a suffix scan of x
     // and an exclusive prefix scan of y across the lanes (fixed order)
     const int tvs = g.V - ncs * ELL;
-    const int tk = tid & 31, half = tk >> 4;
+    const int tk = tid & 31, sl = tok_slot(g, tk), half = sl >> 4;
     float x = 0.0f, y = 0.0f;
     if (tid < ELL) {
       float gt = 0.0f, rw = 0.0f, cj = 0.0f;
 #pragma unroll
       for (int uu = 0; uu < 4; uu++) {
 #pragma unroll
-        for (int qq = 0; qq < 4; qq++) gt += rg[((4 * half + uu) * 4 + qq) * 16 + (tk & 15)];
-        rw += rwp[(4 * half + uu) * 16 + (tk & 15)];
+        for (int qq = 0; qq < 4; qq++) gt += rg[((4 * half + uu) * 4 + qq) * 16 + (sl & 15)];
+        rw += rwp[(4 * half + uu) * 16 + (sl & 15)];
       }
       // channels ci >= c hold exact zeros (their xhat is staged as zero)
 #pragma unroll
       for (int rr = 0; rr < 4; rr++)
 #pragma unroll
-        for (int ci = 0; ci < CK; ci++) cj += csum[rr * K + tk * CK + ci];
-      x = s_d[tk] * gt;
+        for (int ci = 0; ci < CK; ci++) cj += csum[rr * K + sl * CK + ci];
+      x = s_d[sl] * gt;
       y = cj - rw;
     }
 #pragma unroll
@@ -542,8 +551,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         if (tk >= off) v += up;
       }
       if (tid < 32) {
-        s_a[tk] = v;
-        s_d[tk] = expf(v);
+        const int sl = tok_slot(g, tk);  // lane tk is token tk of the chunk
+        s_a[sl] = v;
+        s_d[sl] = expf(v);
       }
     }
     if (wide) {
@@ -552,7 +562,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       for (int idx = tid; idx < K * R; idx += NTT) {
         const int k = idx / R, col = idx % R;
         const int j = k / CK, ci = k % CK;
-        const int pos = nc * ELL + j;
+        const int pos = nc * ELL + slot_tok(g, j);
         bf16 v = (bf16)0.0f;
         if (col < g.r && pos < g.V && ci < g.c)
           v = bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, col)];
@@ -562,7 +572,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       if constexpr (ROT == 1) {
         for (int idx = tid; idx < ELL * 8 * RT; idx += NTT) {
           const int tk = idx / (8 * RT), a = idx % (8 * RT);
-          const int pos = nc * ELL + tk;
+          const int pos = nc * ELL + slot_tok(g, tk);
           float th = 0.0f;
           if (a < g.A && pos < g.V) th = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + a];
           float sv, cv;
@@ -573,7 +583,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       } else if constexpr (ROT == 3) {
         for (int idx = tid; idx < ELL * 16 * RT; idx += NTT) {
           const int tk = idx / (16 * RT), e = idx % (16 * RT);
-          const int pos = nc * ELL + tk;
+          const int pos = nc * ELL + slot_tok(g, tk);
           float v = (e & 3) == 0 ? 1.0f : 0.0f;
           if ((e >> 2) < g.J && pos < g.V) v = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e];
           rt[tk * RTP + e] = (RTE)v;
@@ -586,7 +596,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, tk = idx % ELL;
-      LT[j * LTP + tk] = (j <= tk) ? expf(s_a[tk] - s_a[j]) : 0.0f;
+      LT[j * LTP + tk] = (slot_tok(g, j) <= slot_tok(g, tk)) ? expf(s_a[tk] - s_a[j]) : 0.0f;
     }
     __syncthreads();
 
@@ -777,7 +787,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
             for (int ks = 0; ks < KSR; ks++) d = MM<bf16>::mma(sa[ks], as_bf8(cP[ks]), d);
             if constexpr (MASK) {
-              if (t >= tv || (g.pair && !(t & 1))) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
+              if (ptk >= tv || (g.pair && !(ptk & 1))) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
             }
             f4 hc;  // c (complex, none) or h~ (quaternion), from the packed fragments
             {
@@ -859,11 +869,26 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
         part[16 * (q % NKT) + n] = vq;
       };
-      if (p < g.p) row1();
+      // Walked in token pairs, the first token half holds the even pair tokens:
+      // their d_c vanish, so their states are never needed and their G rows and
+      // d_xhat partials are zero.
+      const bool live = !(g.pair && tt == 0);  // wave-uniform
+      if (p < g.p && live) row1();
       __syncthreads();  // the previous round's d_bhat reads of the G blocks are done
       if (p < g.p) {
-        if (tv >= ELL && !g.pair) row2(std::false_type{});
-        else row2(std::true_type{});
+        if (!live) {
+          bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);
+#pragma unroll
+          for (int ky = 0; ky < KSR; ky++) {
+            *reinterpret_cast<unsigned long long*>(Gw + 32 * ky) = 0ull;
+            *reinterpret_cast<unsigned long long*>(Gw + 32 * ky + 16) = 0ull;
+          }
+          dxp[(tt * 4 + u) * K + 16 * (q % NKT) + n] = 0.0f;
+        } else if (tv >= ELL && !g.pair) {
+          row2(std::false_type{});
+        } else {
+          row2(std::true_type{});
+        }
       }
       store_carry(pf, (round + 1) & 1);  // its buffer was last read two rounds back
       __syncthreads();  // the round's G blocks and d_xhat partials are complete; next carry rows staged
@@ -1027,7 +1052,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         float s = 0.0f;
 #pragma unroll
         for (int uu = 0; uu < 4; uu++) s += RB[((4 * half + uu) * 16 + (tk & 15)) * rwq + el];
-        const int pos = nc * ELL + tk;
+        const int pos = nc * ELL + slot_tok(g, tk);
         if (pos < g.s) d_rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e] = (bf16)s;
       }
     };
@@ -1051,7 +1076,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         for (int idx = tid; idx < K * (R / 8); idx += NTT) {
           const int k = idx / (R / 8), c8 = idx % (R / 8);
           const int j = k / CK, ci = k % CK;
-          const int pos = nc * ELL + j;
+          const int pos = nc * ELL + slot_tok(g, j);
           if (pos < g.s && ci < g.c && 8 * c8 < g.r)
             *reinterpret_cast<u4*>(d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8) =
                 *reinterpret_cast<const u4*>(DBs + k * SP + 8 * c8);
@@ -1060,7 +1085,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         for (int idx = tid; idx < K * g.r; idx += NTT) {
           const int k = idx / g.r, ra = idx - k * g.r;
           const int j = k / CK, ci = k % CK;
-          const int pos = nc * ELL + j;
+          const int pos = nc * ELL + slot_tok(g, j);
           if (pos < g.s && ci < g.c)
             d_bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + ra] = DBs[k * SP + inv_perm_rc(g, ra)];
         }
