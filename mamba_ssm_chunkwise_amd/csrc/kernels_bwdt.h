@@ -49,12 +49,13 @@ constexpr int LTP = 36;         // row pitch of LT[j][t] (floats)
 constexpr int XPB = 32;         // state rows per staged xhat block
 
 // Token slots of a chunk. A chain walked in token pairs (four channels: pair
-// token 2t holds channels 0, 1 of token t, pair token 2t+1 channels 2, 3) puts
-// its even pair tokens in slots 0..15 and its odd ones in slots 16..31, so the
-// first token half of the backward holds exactly the pair tokens whose d_c
-// vanish; slot s holds pair token 2 (s mod 16) + s / 16. Otherwise slot = token.
-__host__ __device__ __forceinline__ int slot_tok(const Geo& g, int s) { return g.pair ? 2 * (s & 15) + (s >> 4) : s; }
-__host__ __device__ __forceinline__ int tok_slot(const Geo& g, int t) { return g.pair ? 16 * (t & 1) + (t >> 1) : t; }
+// token 2t holds channels 0, 1 of token t, pair token 2t+1 channels 2, 3; the
+// PO kernels) puts its even pair tokens in slots 0..15 and its odd ones in slots
+// 16..31: slot s holds pair token 2 (s mod 16) + s / 16. Otherwise slot = token.
+template <bool PO>
+__host__ __device__ __forceinline__ int slot_tok(int s) { return PO ? 2 * (s & 15) + (s >> 4) : s; }
+template <bool PO>
+__host__ __device__ __forceinline__ int tok_slot(int t) { return PO ? 16 * (t & 1) + (t >> 1) : t; }
 
 // Column-contracting fragments built from accumulator registers: K-slot
 // 32ks + 8q + e holds state column 32ks + 16(e/4) + 4q + e%4, i.e. register
@@ -123,10 +124,17 @@ __host__ __device__ __forceinline__ int rot_tiles(const Geo& g) {
 // Per-lane chunk constants are float4 rows interleaved by lane ([entry][lane]
 // of 16 bytes, conflict-free): LWE entries of W factors, 2*NKT of d_xhat
 // factors.
+// PO (pair mode, odd pair tokens): eight state rows per round, every wave on the
+// sixteen odd token slots; the tables of the first token half are not needed and
+// the rotation table holds the odd slots only.
 constexpr int LWE = 4;
-template <int NT, int CK>
+template <int NT, int CK, bool PO = false>
 struct LdsT {
   static constexpr int R = 16 * NT, K = ELL * CK, SP = cf_pitch(R), KP = cf_pitch(K), GTP = R + 16;
+  static constexpr int RR = PO ? 8 : 4;                  // state rows of a round
+  static constexpr int LWN = PO ? LWE / 2 : LWE;         // W-factor entries per lane
+  static constexpr int LYN = (PO ? 1 : 2) * (K / 16);    // d_xhat factor entries per lane
+  static constexpr int RTK = PO ? ELL / 2 : ELL;         // token slots of the rotation table
   static constexpr size_t Ss = 0;                                     // S rows, K-slot order
   static constexpr size_t bsT = Ss + (size_t)R * SP * 2;              // bhat^T [col][(j,c)]
   static constexpr size_t bsY = bsT + (size_t)R * KP * 2;             // bhat [(j,c)][col slot]
@@ -136,11 +144,11 @@ struct LdsT {
   static constexpr size_t a = LT + (size_t)ELL * LTP * 4;
   static constexpr size_t d = a + ELL * 4;
   static constexpr size_t lw = d + ELL * 4;
-  // rows of a round: carry [2 buffers][4][R], then d_m1 [4][R] and D+ [4][R]
-  static constexpr size_t cst = lw + (size_t)(LWE + 2 * (K / 16)) * 64 * 16;
-  static constexpr size_t dxp = cst + (size_t)4 * 4 * R * 4;                   // d_xhat partials [2][4][K]
+  // rows of a round: carry [2 buffers][RR][R], then d_m1 [RR][R] and D+ [RR][R]
+  static constexpr size_t cst = lw + (size_t)(LWN + LYN) * 64 * 16;
+  static constexpr size_t dxp = cst + (size_t)4 * RR * R * 4;                  // d_xhat partials [8 wave slots][K]
   static constexpr size_t red = dxp + (size_t)2 * 4 * K * 4;
-  static constexpr size_t nred = (size_t)NWT * 4 * 16 + NWT * 16 + 4 * K + ELL;  // floats of red
+  static constexpr size_t nred = (size_t)NWT * 4 * 16 + NWT * 16 + RR * K + ELL;  // floats of red
   // G of the round's rows, [row][token][column] (pitch GTP); at chunk end the
   // d_bhat tile and the rotation-gradient reduction reuse the space
   static constexpr size_t gs0 = (size_t)4 * ELL * GTP * 2;                     // G blocks
@@ -152,7 +160,7 @@ struct LdsT {
   // rotation table (RT rotated tiles), rt_pitch(16*RT) entries per token: fp32
   // cos/sin pairs for complex modes, the bf16 input quaternions as they are
   __host__ __device__ static size_t total(int RT, int rot_kind) {
-    return rot + (size_t)ELL * rt_pitch(16 * RT) * (rot_kind == 3 ? 2 : 4);
+    return rot + (size_t)RTK * rt_pitch(16 * RT) * (rot_kind == 3 ? 2 : 4);
   }
   // the rotation-gradient reduction [wave][16 tokens][8RT or 16RT] runs in at
   // most four passes over the G space
@@ -170,13 +178,14 @@ struct LdsT {
 // of once per element. BY also fills the bhat tile in (j,c)-row order used by
 // the backward. Rows past r, tokens past valid_len and channels past c are
 // written as zeros (identity rotations), like the element-wise staging.
-template <int NT, int CK, int ROT, int RT, bool BY>
+template <int NT, int CK, int ROT, int RT, bool BY, bool PO = false>
 struct WideStage {
+  static constexpr int TK = PO ? ELL / 2 : ELL, T0 = PO ? ELL / 2 : 0;  // rotation-table slots: T0.. (TK of them)
   static constexpr int R = 16 * NT, K = ELL * CK, KP = cf_pitch(K), SP = cf_pitch(R), RTP = rt_pitch(16 * RT);
   static constexpr int NBU = K * R / 8, NBL = (NBU + NTT - 1) / NTT;   // bhat: 8 columns per load
   static constexpr int NXU = K * XPB / 8, NXL = (NXU + NTT - 1) / NTT; // xhat block: 8 rows per load
   // rotation: complex 2 angles per load (4RT pairs per token), quaternion 2 blocks per load
-  static constexpr int NRU = ROT == 1 ? ELL * 4 * RT : ROT == 3 ? ELL * 2 * RT : 0;
+  static constexpr int NRU = ROT == 1 ? TK * 4 * RT : ROT == 3 ? TK * 2 * RT : 0;
   static constexpr int NRL = NRU > 0 ? (NRU + NTT - 1) / NTT : 1;
   u4 bv[NBL];
   u4 xv[NXL];
@@ -195,7 +204,7 @@ struct WideStage {
     for (int i = 0; i < NXL; i++) {
       const int idx = tid + i * NTT;
       const int k = idx % K, c8 = idx / K;
-      const int j = k / CK, ci = k % CK, pos = nc * ELL + slot_tok(g, j);
+      const int j = k / CK, ci = k % CK, pos = nc * ELL + slot_tok<PO>(j);
       xv[i] = u4{0u, 0u, 0u, 0u};
       if (idx < NXU && pblk + 8 * c8 < g.p && ci < g.c && pos < g.V)
         xv[i] = *reinterpret_cast<const u4*>(xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + 8 * c8);
@@ -218,7 +227,7 @@ struct WideStage {
     for (int i = 0; i < NBL; i++) {
       const int idx = tid + i * NTT;
       const int k = idx % K, c8 = idx / K;
-      const int j = k / CK, ci = k % CK, pos = nc * ELL + slot_tok(g, j);
+      const int j = k / CK, ci = k % CK, pos = nc * ELL + slot_tok<PO>(j);
       bv[i] = u4{0u, 0u, 0u, 0u};
       if (idx < NBU && 8 * c8 < g.r && ci < g.c && pos < g.V)
         bv[i] = *reinterpret_cast<const u4*>(bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8);
@@ -228,12 +237,12 @@ struct WideStage {
     for (int i = 0; i < NRL; i++) {
       const int idx = tid + i * NTT;
       if constexpr (ROT == 1) {
-        const int tk = idx / (4 * RT), a2 = idx % (4 * RT), pos = nc * ELL + slot_tok(g, tk);
+        const int tk = idx / (4 * RT), a2 = idx % (4 * RT), pos = nc * ELL + slot_tok<PO>(T0 + tk);
         r1[i] = 0u;
         if (idx < NRU && 2 * a2 < g.A && pos < g.V)
           r1[i] = *reinterpret_cast<const unsigned*>(rot + (((size_t)bi * g.s + pos) * g.h + hi) * g.RW + 2 * a2);
       } else if constexpr (ROT == 3) {
-        const int tk = idx / (2 * RT), e8 = idx % (2 * RT), pos = nc * ELL + slot_tok(g, tk);
+        const int tk = idx / (2 * RT), e8 = idx % (2 * RT), pos = nc * ELL + slot_tok<PO>(T0 + tk);
         const unsigned one = 0x3f80u;  // bf16 1.0: identity quaternions (1, 0, 0, 0)
         r3[i] = u4{one, 0u, one, 0u};
         if (idx < NRU && 2 * e8 < g.J && pos < g.V)
@@ -314,7 +323,7 @@ __device__ __forceinline__ f4 load_cols4(const float* row, int r, int col, int R
 
 // RT: column tiles carrying a rotation (compile time; the tables are padded
 // with the identity up to 8*RT complex pairs or 4*RT quaternion blocks).
-template <int NT, int ROT, int CK, int RT>
+template <int NT, int ROT, int CK, int RT, bool PO = false>
 __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     Geo g, const bf16* __restrict__ xhat, const bf16* __restrict__ bhat, const bf16* __restrict__ da,
     const bf16* __restrict__ rot, const float* __restrict__ carry, const float* __restrict__ dm2,
@@ -330,7 +339,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   constexpr int RTA = RT > 0 ? RT : 1;
   constexpr int RTP = rt_pitch(16 * RT);  // rotation table floats per token (padded)
   static_assert((ROT == 0) == (RT == 0) && RT <= NT && CH >= 1 && KH >= 1, "tiling");
-  using L = LdsT<NT, CK>;
+  using L = LdsT<NT, CK, PO>;
+  constexpr int RR = L::RR;  // state rows of a round
+  static_assert(!PO || CK == 2, "odd pair tokens: two channels per pair token");
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* Ss = (bf16*)(smem + L::Ss);
   bf16* bsT = (bf16*)(smem + L::bsT);
@@ -353,8 +364,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   bf16* Gs = (bf16*)(smem + L::Gs);
   bf16* dXs = (bf16*)(smem + L::dXs);
   float* red = (float*)(smem + L::red);
-  f4* LWt = (f4*)(smem + L::lw);          // [LWE][64]
-  f4* LYt = LWt + LWE * 64;               // [2*NKT][64]
+  f4* LWt = (f4*)(smem + L::lw);          // [LWN][64]
+  f4* LYt = LWt + L::LWN * 64;            // [LYN][64]
   float* cst = (float*)(smem + L::cst);   // [carry x2 | d_m1 | D+][row of the round][R]
   float* dxp = (float*)(smem + L::dxp);   // [token half][row of the round][K]
 
@@ -368,8 +379,12 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform in the wave
   const int lane = tid & 63, n = lane & 15, q = lane >> 4;
   const int u = w & 3, tt = w >> 2;       // row slot of the round, token half
-  const int t = 16 * tt + n;              // this lane's token slot in the transposed tiles
-  const int ptk = slot_tok(g, t);         // and its token
+  // PO: every wave works on the odd token slots; the first half takes rows 4..7
+  const int t = PO ? 16 + n : 16 * tt + n;  // this lane's token slot in the transposed tiles
+  const int rs = PO && tt == 0 ? 4 + u : u;  // this wave's row of the round
+  const int tr = PO ? n : t;                 // its row of the rotation table
+  const int gsl = PO && tt == 0 ? n : t;     // its slot row in the G block
+  const int ptk = slot_tok<PO>(t);         // and its token
   const int kq = w / CW, cq = w % CW;     // d_bhat block of this wave
 
   // S = d_m2 + d_m2^T: rows internal columns, K-slots in col_of_slot order.
@@ -387,14 +402,14 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
   }
 
-  using WS = WideStage<NT, CK, ROT, RT, true>;
+  using WS = WideStage<NT, CK, ROT, RT, true, PO>;
   const bool wide = WS::usable(g);
   WS wst;
   auto stage_x = [&](int nc, int pblk) {
     for (int idx = tid; idx < K * XPB; idx += NTT) {
       const int k = idx / XPB, pl = idx % XPB;
       const int j = k / CK, ci = k % CK;
-      const int pos = nc * ELL + slot_tok(g, j);
+      const int pos = nc * ELL + slot_tok<PO>(j);
       float v = 0.0f;
       if (pblk + pl < g.p && ci < g.c && pos < g.V)
         v = (float)xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + pl];
@@ -410,7 +425,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       for (int idx = tid; idx < NXU; idx += NTT) {
         const int k = idx % K, c8 = idx / K;
         const int j = k / CK, ci = k % CK;
-        const int pos = nc * ELL + slot_tok(g, j);
+        const int pos = nc * ELL + slot_tok<PO>(j);
         if (ci < g.c && pos < g.s && pblk + 8 * c8 < g.p) {
           u4 v;
 #pragma unroll
@@ -426,40 +441,68 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     for (int idx = tid; idx < K * rows; idx += NTT) {
       const int k = idx / rows, pl = idx % rows;
       const int j = k / CK, ci = k % CK;
-      const int pos = nc * ELL + slot_tok(g, j);
+      const int pos = nc * ELL + slot_tok<PO>(j);
       if (ci < g.c && pos < g.s)
         d_xhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pblk + pl] = dXs[pl * KP + k];
     }
   };
   // The carry rows h_-(n)[p][:], the d_m1 rows and the D(n+1) rows of a round
-  // (4 state rows) travel through LDS: every thread fetches one float4 of them
-  // a round ahead and stores it after the round's d_bhat work, off the rows'
-  // critical path. D(n+1) was written by this workgroup one chunk earlier.
-  constexpr int CQ = 3 * 4 * R / 4;  // float4 pieces per round
-  static_assert(CQ <= NTT, "one piece per thread");
-  static_assert(CQ % 64 == 0 && R % 64 == 0, "whole waves per array");
-  // This thread's piece of the round rows is fixed: array farr (uniform in the
-  // wave), row frr of the round, columns fcol..; per chunk only the row
-  // pointer of round 0 changes, and each round steps it by four rows.
-  const int farr = (w * 64) / R, frest = tid - farr * R;
-  const int frr = frest / (R / 4), fcol = 4 * (frest % (R / 4));
-  const bool fthr = w < CQ / 64;
-  const float* frow0 = nullptr;  // set per chunk
-  size_t fstep = 0;
-  int flim = R;
-  bool fon = false;
-  auto fetch_round = [&](int pr0) -> f4 {
-    f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (fon && pr0 + frr < g.p) v = load_cols4(frow0 + (size_t)(pr0 >> 2) * fstep, flim, fcol, R);
-    return v;
+  // (RR state rows) travel through LDS: every thread fetches its float4 pieces
+  // of them a round ahead and stores them after the round's d_bhat work, off the
+  // rows' critical path. D(n+1) was written by this workgroup one chunk earlier.
+  constexpr int CQA = RR * R / 4;          // float4 pieces of one array per round
+  constexpr int CQ = 3 * CQA;              // pieces per round
+  constexpr int NPC = (CQ + NTT - 1) / NTT;  // pieces per thread
+  static_assert(CQA % 64 == 0, "whole waves per array");
+  // This thread's pieces of the round rows are fixed: array farr (uniform in the
+  // wave), row frr of the round, columns fcol..; per chunk only the row pointer
+  // of round 0 changes, and each round steps it by RR rows.
+  struct RowPiece {
+    int farr, fidx, frr, fcol;
+    bool fthr, fon;
+    const float* frow0;
+    size_t fstep;
+    int flim;
+  };
+  RowPiece pc[NPC];
+#pragma unroll
+  for (int k = 0; k < NPC; k++) {
+    const int pi = tid + k * NTT;
+    pc[k].farr = __builtin_amdgcn_readfirstlane((w * 64 + k * NTT) / CQA);
+    pc[k].fidx = pi - pc[k].farr * CQA;
+    pc[k].frr = pc[k].fidx / (R / 4);
+    pc[k].fcol = 4 * (pc[k].fidx % (R / 4));
+    pc[k].fthr = w * 64 + k * NTT < CQ;
+    pc[k].frow0 = nullptr;  // set per chunk
+    pc[k].fstep = 0;
+    pc[k].flim = R;
+    pc[k].fon = false;
+  }
+  struct Pieces {
+    f4 v[NPC];
+  };
+  auto fetch_round = [&](int round) -> Pieces {
+    Pieces r;
+#pragma unroll
+    for (int k = 0; k < NPC; k++) {
+      r.v[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (pc[k].fon && RR * round + pc[k].frr < g.p)
+        r.v[k] = load_cols4(pc[k].frow0 + (size_t)round * pc[k].fstep, pc[k].flim, pc[k].fcol, R);
+    }
+    return r;
   };
   // The carry rows go to the buffer of the round's parity (they are read before
   // the round's first barrier); d_m1 and D+ rows to their single buffers.
-  auto store_carry = [&](f4 v, int buf) {
-    if (fthr && farr == 0) reinterpret_cast<f4*>(cst + (size_t)buf * 4 * R)[frest] = v;
+  auto store_carry = [&](const Pieces& v, int buf) {
+#pragma unroll
+    for (int k = 0; k < NPC; k++)
+      if (pc[k].fthr && pc[k].farr == 0) reinterpret_cast<f4*>(cst + (size_t)buf * RR * R)[pc[k].fidx] = v.v[k];
   };
-  auto store_dmdp = [&](f4 v) {
-    if (fthr && farr > 0) reinterpret_cast<f4*>(cst + (size_t)(4 + 4 * farr) * R)[frest] = v;
+  auto store_dmdp = [&](const Pieces& v) {
+#pragma unroll
+    for (int k = 0; k < NPC; k++)
+      if (pc[k].fthr && pc[k].farr > 0)
+        reinterpret_cast<f4*>(cst + (size_t)(1 + pc[k].farr) * RR * R)[pc[k].fidx] = v.v[k];
   };
 
   float dav = 0.0f;
@@ -472,7 +515,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int n0 = gi * g.G;
   const int nkc = chain_nk(g);  // chunks walked
   const int n1 = (n0 + g.G < nkc) ? n0 + g.G : nkc;
-  const int nrounds = (g.p + 3) / 4;
+  const int nrounds = (g.p + RR - 1) / RR;
   // ---- d_da of chunk ncs: sum_{t>=s} d_t <G[t], h_-> + sum_{s'<s} (C[s'] - Rw[s']),
   // from the per-wave partials the chunk left in LDS (and its s_d, which the
   // first wave alone rewrites, after this scan)
@@ -484,19 +527,31 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     // lane t < 32: x = d_t <G[t], h_->, y = C[t] - Rw[t]; then a suffix scan of x
     // and an exclusive prefix scan of y across the lanes (fixed order)
     const int tvs = g.V - ncs * ELL;
-    const int tk = tid & 31, sl = tok_slot(g, tk), half = sl >> 4;
+    const int tk = tid & 31, sl = tok_slot<PO>(tk), half = sl >> 4;
     float x = 0.0f, y = 0.0f;
     if (tid < ELL) {
       float gt = 0.0f, rw = 0.0f, cj = 0.0f;
+      if constexpr (PO) {
+        // every wave's partials are at the odd token slots 16..31; the even ones are zero
+        if (half == 1) {
 #pragma unroll
-      for (int uu = 0; uu < 4; uu++) {
+          for (int w8 = 0; w8 < NWT; w8++) {
 #pragma unroll
-        for (int qq = 0; qq < 4; qq++) gt += rg[((4 * half + uu) * 4 + qq) * 16 + (sl & 15)];
-        rw += rwp[(4 * half + uu) * 16 + (sl & 15)];
+            for (int qq = 0; qq < 4; qq++) gt += rg[(w8 * 4 + qq) * 16 + (sl & 15)];
+            rw += rwp[w8 * 16 + (sl & 15)];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int uu = 0; uu < 4; uu++) {
+#pragma unroll
+          for (int qq = 0; qq < 4; qq++) gt += rg[((4 * half + uu) * 4 + qq) * 16 + (sl & 15)];
+          rw += rwp[(4 * half + uu) * 16 + (sl & 15)];
+        }
       }
       // channels ci >= c hold exact zeros (their xhat is staged as zero)
 #pragma unroll
-      for (int rr = 0; rr < 4; rr++)
+      for (int rr = 0; rr < RR; rr++)
 #pragma unroll
         for (int ci = 0; ci < CK; ci++) cj += csum[rr * K + sl * CK + ci];
       x = s_d[sl] * gt;
@@ -520,27 +575,31 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   for (int nc = n1 - 1; nc >= n0; nc--) {
     asm volatile("" : "+v"(tid));
     const bool has_next = nc + 1 < n1;  // D(n+1) comes from this walk; zero at the group's end
-    if (farr == 0) {
-      frow0 = carry + (((size_t)bh * g.NK + nc) * g.p + frr) * g.r;
-      fstep = (size_t)4 * g.r;
-      flim = g.r;
-      fon = fthr;
-    } else if (farr == 1) {
-      frow0 = dm1i + ((size_t)bh * g.p + frr) * R;
-      fstep = (size_t)4 * R;
-      flim = R;
-      fon = fthr;
-    } else {
-      frow0 = Db + (((size_t)bh * g.NK + nc + 1) * g.p + frr) * g.r;
-      fstep = (size_t)4 * g.r;
-      flim = g.r;
-      fon = fthr && has_next;
+#pragma unroll
+    for (int k = 0; k < NPC; k++) {
+      RowPiece& f = pc[k];
+      if (f.farr == 0) {
+        f.frow0 = carry + (((size_t)bh * g.NK + nc) * g.p + f.frr) * g.r;
+        f.fstep = (size_t)RR * g.r;
+        f.flim = g.r;
+        f.fon = f.fthr;
+      } else if (f.farr == 1) {
+        f.frow0 = dm1i + ((size_t)bh * g.p + f.frr) * R;
+        f.fstep = (size_t)RR * R;
+        f.flim = R;
+        f.fon = f.fthr;
+      } else {
+        f.frow0 = Db + (((size_t)bh * g.NK + nc + 1) * g.p + f.frr) * g.r;
+        f.fstep = (size_t)RR * g.r;
+        f.flim = g.r;
+        f.fon = f.fthr && has_next;
+      }
     }
     float* dbase = Db + ((size_t)bh * g.NK + nc) * g.p * g.r;  // D(n) rows of this chunk
     __syncthreads();
     if (nc + 1 < n1) dda_scan(nc + 1);  // the previous step's d_da
     load_chunk(nc);
-    const f4 v0 = fetch_round(0);
+    const Pieces v0 = fetch_round(0);
     // ---- chunk staging
     if (tid < 64) {
       const int tk = tid & 31;
@@ -551,7 +610,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         if (tk >= off) v += up;
       }
       if (tid < 32) {
-        const int sl = tok_slot(g, tk);  // lane tk is token tk of the chunk
+        const int sl = tok_slot<PO>(tk);  // lane tk is token tk of the chunk
         s_a[sl] = v;
         s_d[sl] = expf(v);
       }
@@ -562,7 +621,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       for (int idx = tid; idx < K * R; idx += NTT) {
         const int k = idx / R, col = idx % R;
         const int j = k / CK, ci = k % CK;
-        const int pos = nc * ELL + slot_tok(g, j);
+        const int pos = nc * ELL + slot_tok<PO>(j);
         bf16 v = (bf16)0.0f;
         if (col < g.r && pos < g.V && ci < g.c)
           v = bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, col)];
@@ -570,9 +629,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         bsY[k * SP + slot_of_col(col)] = v;
       }
       if constexpr (ROT == 1) {
-        for (int idx = tid; idx < ELL * 8 * RT; idx += NTT) {
+        for (int idx = tid; idx < L::RTK * 8 * RT; idx += NTT) {
           const int tk = idx / (8 * RT), a = idx % (8 * RT);
-          const int pos = nc * ELL + slot_tok(g, tk);
+          const int pos = nc * ELL + slot_tok<PO>((PO ? ELL / 2 : 0) + tk);
           float th = 0.0f;
           if (a < g.A && pos < g.V) th = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + a];
           float sv, cv;
@@ -581,9 +640,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           rt[tk * RTP + 2 * a + 1] = sv;
         }
       } else if constexpr (ROT == 3) {
-        for (int idx = tid; idx < ELL * 16 * RT; idx += NTT) {
+        for (int idx = tid; idx < L::RTK * 16 * RT; idx += NTT) {
           const int tk = idx / (16 * RT), e = idx % (16 * RT);
-          const int pos = nc * ELL + slot_tok(g, tk);
+          const int pos = nc * ELL + slot_tok<PO>((PO ? ELL / 2 : 0) + tk);
           float v = (e & 3) == 0 ? 1.0f : 0.0f;
           if ((e >> 2) < g.J && pos < g.V) v = (float)rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e];
           rt[tk * RTP + e] = (RTE)v;
@@ -596,7 +655,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     __syncthreads();
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, tk = idx % ELL;
-      LT[j * LTP + tk] = (slot_tok(g, j) <= slot_tok(g, tk)) ? expf(s_a[tk] - s_a[j]) : 0.0f;
+      LT[j * LTP + tk] = (slot_tok<PO>(j) <= slot_tok<PO>(tk)) ? expf(s_a[tk] - s_a[j]) : 0.0f;
     }
     __syncthreads();
 
@@ -604,21 +663,22 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     const int tv = g.V - nc * ELL;  // valid tokens of this chunk (<= 0: none)
     if (w == 0) {
       // W factors: L[16h+n][j of the slots 32ks+8q..], flattened (h*CK+ks)*(8/CK)+v
+      // (PO: the second half h = 1 only, at entries f - 8)
 #pragma unroll
-      for (int f = 0; f < 16; f++) {
-        const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), v = rest % (8 / CK);
-        reinterpret_cast<float*>(LWt + (f >> 2) * 64 + lane)[f & 3] =
+      for (int f = PO ? 8 : 0; f < 16; f++) {
+        const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), v = rest % (8 / CK), fe = PO ? f - 8 : f;
+        reinterpret_cast<float*>(LWt + (fe >> 2) * 64 + lane)[fe & 3] =
             LT[((32 * ks + 8 * q) / CK + v) * LTP + 16 * hh + n];
       }
-      // d_xhat factors: L[16h+4q+i][j of (j,c) = 16kt+n], entry h*NKT+kt
+      // d_xhat factors: L[16h+4q+i][j of (j,c) = 16kt+n], entry h*NKT+kt (PO: h = 1, entry kt)
 #pragma unroll
-      for (int hh = 0; hh < 2; hh++)
+      for (int hh = PO ? 1 : 0; hh < 2; hh++)
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) {
           f4 v;
 #pragma unroll
           for (int i = 0; i < 4; i++) v[i] = LT[((16 * kt + n) / CK) * LTP + 16 * hh + 4 * q + i];
-          LYt[(hh * NKT + kt) * 64 + lane] = v;
+          LYt[((PO ? 0 : hh) * NKT + kt) * 64 + lane] = v;
         }
     }
     __syncthreads();
@@ -639,7 +699,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     const float dtl = s_d[t];
 
     for (int round = 0; round < nrounds; round++) {
-      const int pr0 = 4 * round;
+      const int pr0 = RR * round;
       const int pblk = pr0 - pr0 % XPB;
       if (round > 0 && pr0 % XPB == 0) {
         __syncthreads();  // the previous round's d_bhat work read the old block
@@ -653,17 +713,17 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
         __syncthreads();
       }
-      const int p = pr0 + u;
-      const f4 pf = fetch_round(pr0 + 4);  // next round's rows
+      const int p = pr0 + rs;
+      const Pieces pf = fetch_round(round + 1);  // next round's rows
       // One state row, all columns, this wave's 16 tokens, in two parts: the
       // states and the packed c^T, then (after a barrier that retires the
       // previous round's reads of the G blocks) everything that writes them.
       // MASK zeroes d_c at tokens >= tv (only the chunk holding valid_len needs
-      // it), and at even tokens when the chain is walked in token pairs.
+      // it; the PO lanes hold odd pair tokens only).
       const int pl = p - pblk;
       u4 cP[KSR];
       u4 hP[ROT == 3 ? KSR : 1];
-      const float* hrow = cst + ((size_t)(round & 1) * 4 + u) * R;
+      const float* hrow = cst + ((size_t)(round & 1) * RR + rs) * R;
       auto row1 = [&]() {
         // ---- W fragment: W[t][(j,c)] = L[t,j] xhat[(j,c)][p] ----------------
         u4 Wf[CK];
@@ -681,7 +741,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           float lw[8];
 #pragma unroll
           for (int e4 = 0; e4 < 2; e4++) {
-            const f4 v = LWt[(2 * tt + e4) * 64 + lane];
+            const f4 v = LWt[((PO ? 0 : 2 * tt) + e4) * 64 + lane];
 #pragma unroll
             for (int i = 0; i < 4; i++) lw[4 * e4 + i] = v[i];
           }
@@ -696,7 +756,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         // ---- states h~^T[col][t] one column tile at a time, then the carry, the
         // de-rotation in the lane and the packed c^T (and h~^T) --------------------
         // tokens 0..15 see j <= 15 only: their last K-steps are all zero
-        const int nks = tt == 0 ? (CK + 1) / 2 : CK;
+        const int nks = tt == 0 && !PO ? (CK + 1) / 2 : CK;
 
         // bhat^T fragments software-pipelined one column tile ahead
         bf8 bn[CK];
@@ -705,7 +765,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
           if (ks < nks) bn[ks] = ld_frag(bsT + n * KP + 32 * ks + 8 * q);
         // carry and rotation rows pipelined one column tile ahead as well
         f4 hvn = *reinterpret_cast<const f4*>(hrow + 4 * q);
-        f4 rtn = RT > 0 ? rt4(t * RTP + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+        f4 rtn = RT > 0 ? rt4(tr * RTP + 4 * q) : f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) {
           __builtin_amdgcn_sched_barrier(0);
@@ -718,7 +778,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             for (int ks = 0; ks < CK; ks++)
               if (ks < nks) bn[ks] = ld_frag(bsT + (16 * (ct + 1) + n) * KP + 32 * ks + 8 * q);
             hvn = *reinterpret_cast<const f4*>(hrow + 16 * (ct + 1) + 4 * q);
-            if (ct + 1 < RT) rtn = rt4(t * RTP + 16 * (ct + 1) + 4 * q);
+            if (ct + 1 < RT) rtn = rt4(tr * RTP + 16 * (ct + 1) + 4 * q);
           }
           __builtin_amdgcn_sched_barrier(0);
           f4 hT = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -755,13 +815,15 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       auto row2 = [&](auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         // ---- d_c^T = S c^T + d_m1, rotation VJP, G, Y = G bhat^T ------------
-        const float* dmrow = cst + (8 + u) * R;
-        const float* dprow = cst + (12 + u) * R;  // D(n+1)[p][:], enters G at the last token
+        const float* dmrow = cst + (2 * RR + rs) * R;
+        const float* dprow = cst + (3 * RR + rs) * R;  // D(n+1)[p][:], enters G at the last token
         const float f31 = t == ELL - 1 ? 1.0f : 0.0f;
         f4 Y[NKT];
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) Y[kt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);  // this lane's piece of its token row
+        // this lane's piece of its slot row in the G block (PO: block u holds rows u
+        // and 4+u of the round at slots 16.. and 0..)
+        bf16* Gw = Gs + ((size_t)u * ELL + gsl) * GTP + 4 * gpiece(q, gsl);
         // S fragments are software-pipelined one column tile ahead: tile ct+1's
         // reads are in flight while tile ct runs its MFMAs and rotation work
         bf8 sn[KSR];
@@ -787,7 +849,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
 #pragma unroll
             for (int ks = 0; ks < KSR; ks++) d = MM<bf16>::mma(sa[ks], as_bf8(cP[ks]), d);
             if constexpr (MASK) {
-              if (ptk >= tv || (g.pair && !(ptk & 1))) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
+              if (ptk >= tv) d = f4{0.0f, 0.0f, 0.0f, 0.0f};
             }
             f4 hc;  // c (complex, none) or h~ (quaternion), from the packed fragments
             {
@@ -801,7 +863,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             f4 G = d;
             if constexpr (ROT == 3) {
               if (ct < RT) {
-                const f4 Q = rt4(t * RTP + 16 * ct + 4 * q);
+                const f4 Q = rt4(tr * RTP + 16 * ct + 4 * q);
                 G[0] = Q[0] * d[0] + Q[1] * d[1] + Q[2] * d[2] + Q[3] * d[3];
                 G[1] = Q[0] * d[1] - Q[1] * d[0] - Q[2] * d[3] + Q[3] * d[2];
                 G[2] = Q[0] * d[2] + Q[1] * d[3] - Q[2] * d[0] - Q[3] * d[1];
@@ -815,7 +877,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             } else {
               if constexpr (ROT == 1) {
                 if (ct < RT) {
-                  const f4 r4 = rt4(t * RTP + 16 * ct + 4 * q);
+                  const f4 r4 = rt4(tr * RTP + 16 * ct + 4 * q);
                   float* ra = racc[ct < RT ? ct : 0];
                   ra[0] += d[0] * hc[1] - d[1] * hc[0];
                   ra[1] += d[2] * hc[3] - d[3] * hc[2];
@@ -826,7 +888,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
                 }
               }
             }
-            if (tt == 1 && has_next) {
+            if ((PO || tt == 1) && has_next) {
               const f4 dp = *reinterpret_cast<const f4*>(dprow + 16 * ct + 4 * q);
 #pragma unroll
               for (int i = 0; i < 4; i++) G[i] += f31 * dp[i];
@@ -856,7 +918,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         float vq = 0.0f;  // the sum of tile kt = q % NKT, which lane group q stores
 #pragma unroll
         for (int kt = 0; kt < NKT; kt++) {
-          const f4 ly = LYt[(tt * NKT + kt) * 64 + lane];
+          const f4 ly = LYt[((PO ? 0 : tt * NKT) + kt) * 64 + lane];
           const float xk = (float)xs[pl * KP + 16 * kt + n];
           f4 e;
 #pragma unroll
@@ -869,36 +931,32 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         }
         part[16 * (q % NKT) + n] = vq;
       };
-      // Walked in token pairs, the first token half holds the even pair tokens:
-      // their d_c vanish, so their states are never needed and their G rows and
-      // d_xhat partials are zero.
-      const bool live = !(g.pair && tt == 0);  // wave-uniform
-      if (p < g.p && live) row1();
+      // (PO: a wave whose row is past p zeroes its G slots, which the d_bhat
+      // contraction reads together with the other row of its block)
+      if (p < g.p) row1();
       __syncthreads();  // the previous round's d_bhat reads of the G blocks are done
-      if (p < g.p) {
-        if (!live) {
-          bf16* Gw = Gs + ((size_t)u * ELL + t) * GTP + 4 * gpiece(q, t);
+      if (PO && p >= g.p) {
+        bf16* Gw = Gs + ((size_t)u * ELL + gsl) * GTP + 4 * gpiece(q, gsl);
 #pragma unroll
-          for (int ky = 0; ky < KSR; ky++) {
-            *reinterpret_cast<unsigned long long*>(Gw + 32 * ky) = 0ull;
-            *reinterpret_cast<unsigned long long*>(Gw + 32 * ky + 16) = 0ull;
-          }
-          dxp[(tt * 4 + u) * K + 16 * (q % NKT) + n] = 0.0f;
-        } else if (tv >= ELL && !g.pair) {
-          row2(std::false_type{});
-        } else {
-          row2(std::true_type{});
+        for (int ky = 0; ky < KSR; ky++) {
+          *reinterpret_cast<unsigned long long*>(Gw + 32 * ky) = 0ull;
+          *reinterpret_cast<unsigned long long*>(Gw + 32 * ky + 16) = 0ull;
         }
+      }
+      if (p < g.p) {
+        if (tv >= ELL) row2(std::false_type{});
+        else row2(std::true_type{});
       }
       store_carry(pf, (round + 1) & 1);  // its buffer was last read two rounds back
       __syncthreads();  // the round's G blocks and d_xhat partials are complete; next carry rows staged
       store_dmdp(pf);   // the round's d_c work, their only reader, is done
-      // ---- d_xhat of the round's rows: the two token halves added ---------------
-      if (tid < 4 * K) {
+      // ---- d_xhat of the round's rows: the two token halves added (PO: each
+      // wave slot tt*4+u holds a whole row, rs = u or 4+u) -----------------------
+      if (tid < RR * K) {
         const int rr = tid / K, k = tid % K;
         const int pp = pr0 + rr;
         if (pp < g.p) {
-          const float v = dxp[rr * K + k] + dxp[(4 + rr) * K + k];
+          const float v = PO ? dxp[(rr < 4 ? 4 + rr : rr - 4) * K + k] : dxp[rr * K + k] + dxp[(4 + rr) * K + k];
           const int pl = pp - pblk;
           dXs[pl * KP + k] = (bf16)v;
           cct += v * (float)xs[pl * KP + k];
@@ -906,88 +964,48 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       }
       // the second token half has the longer row work ahead of it: its waves get
       // issue priority for the d_bhat work, the first half's fills in under their rows
-      if (tt == 1) __builtin_amdgcn_s_setprio(2);
-      // ---- d_bhat[(j,c)][col] += sum_t L[t,j] xhat[(j,c)][p] G[t][col]; local ----
-      float LB[KH][8];  // L[tslot(8q+e)][j of (j,c) = 16(kq*KH+kb)+n]
+      if (!PO && tt == 1) __builtin_amdgcn_s_setprio(2);
+      if constexpr (PO) {
+        // ---- d_bhat and local over the odd pair tokens of two rows per block:
+        // K-slots 8q+e (e < 4) are block slots 4q+e = row 4+rr at token slot
+        // 16+4q+e, K-slots e >= 4 are block slots 16+4q+e-4 = row rr at token
+        // slot 16+4q+e-4; so both halves of a K-step take L at the same tokens.
+        float LB[KH][4];  // L[16+4q+i][j of (j,c) = 16(kq*KH+kb)+n]
 #pragma unroll
-      for (int kb = 0; kb < KH; kb++) {
-        const float* src = LT + ((16 * (kq * KH + kb) + n) / CK) * LTP + 4 * q;
-        const f4 l0 = *reinterpret_cast<const f4*>(src);
-        const f4 l1 = *reinterpret_cast<const f4*>(src + 16);
+        for (int kb = 0; kb < KH; kb++) {
+          const f4 l = *reinterpret_cast<const f4*>(LT + ((16 * (kq * KH + kb) + n) / CK) * LTP + 16 + 4 * q);
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          LB[kb][e] = l0[e];
-          LB[kb][e + 4] = l1[e];
+          for (int i = 0; i < 4; i++) LB[kb][i] = l[i];
         }
-      }
-      bf8 dA;  // A operand of local: rows 0, 4, 8, 12 = d_t over the K-slots, t = tslot(8q+e)
-      {
-        const f4 d0 = *reinterpret_cast<const f4*>(s_d + 4 * q);
-        const f4 d1 = *reinterpret_cast<const f4*>(s_d + 16 + 4 * q);
-        const float on = (n & 3) == 0 ? 1.0f : 0.0f;
+        bf8 dA;  // A operand of local: row 0 = d_t over row rr's K-slots, row 4 over row 4+rr's
+        {
+          const f4 d1 = *reinterpret_cast<const f4*>(s_d + 16 + 4 * q);
+          const float on0 = n == 0 ? 1.0f : 0.0f, on4 = n == 4 ? 1.0f : 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          dA[e] = (bf16)(on * d0[e]);
-          dA[e + 4] = (bf16)(on * d1[e]);
-        }
-      }
-      if (pr0 + 4 <= g.p) {
-        // all four rows present: every G^T fragment of the round is loaded up
-        // front, so one LDS latency covers the whole phase
-        bf8 gbf[4][CH];
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++)
-#pragma unroll
-          for (int cb = 0; cb < CH; cb++)
-            gbf[rr][cb] = ld_tok_frag<GTP>(Gs + (size_t)rr * ELL * GTP, cq * CH + cb, lane);
-        u4 Ab[4][KH];
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++)
-#pragma unroll
-          for (int kb = 0; kb < KH; kb++) {
-            const float xk = (float)xs[(pr0 + rr - pblk) * KP + 16 * (kq * KH + kb) + n];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) Ab[rr][kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
+          for (int e = 0; e < 4; e++) {
+            dA[e] = (bf16)(on4 * d1[e]);
+            dA[e + 4] = (bf16)(on0 * d1[e]);
           }
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++)
-#pragma unroll
-          for (int cb = 0; cb < CH; cb++)
-#pragma unroll
-            for (int kb = 0; kb < KH; kb++)
-              dbacc[kb][cb] = MM<bf16>::mma(as_bf8(Ab[rr][kb]), gbf[rr][cb], dbacc[kb][cb]);
-        // local of the rows rr with rr % KW == kq (each (row, column tile) once):
-        // every lane group holds the row sums (dA repeats d_t in rows 0, 4, 8,
-        // 12), and group q stores column tile q % CH
-#pragma unroll
-        for (int rr = 0; rr < 4; rr++) {
-          if (rr % KW != kq) continue;
-          float* dbrow = dbase + (size_t)(pr0 + rr) * g.r;
-          float lq = 0.0f;
-#pragma unroll
-          for (int cb = 0; cb < CH; cb++) {
-            const f4 lo = MM<bf16>::mma(dA, gbf[rr][cb], f4{0.0f, 0.0f, 0.0f, 0.0f});
-            lq = (q % CH) == cb ? lo[0] : lq;
-          }
-          const int col = 16 * (cq * CH + q % CH) + n;
-          if (q < CH && col < g.r) dbrow[col] = lq;
         }
-      } else {
 #pragma unroll 1
         for (int rr = 0; rr < 4; rr++) {
-          const int pp = pr0 + rr;
-          if (pp >= g.p) break;
-          const int pl = pp - pblk;
+          const int pa = pr0 + rr, pb = pr0 + 4 + rr;  // the rows of block rr
+          if (pa >= g.p) break;                         // then pb >= p as well
+          const bool vb = pb < g.p;
           u4 Ab[KH];
 #pragma unroll
           for (int kb = 0; kb < KH; kb++) {
-            const float xk = (float)xs[pl * KP + 16 * (kq * KH + kb) + n];
+            const int kk = 16 * (kq * KH + kb) + n;
+            const float xa = (float)xs[(pa - pblk) * KP + kk];
+            const float xb = vb ? (float)xs[(pb - pblk) * KP + kk] : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) Ab[kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
+            for (int e = 0; e < 4; e += 2) {
+              Ab[kb][e / 2] = pk_bf16(LB[kb][e] * xb, LB[kb][e + 1] * xb);
+              Ab[kb][2 + e / 2] = pk_bf16(LB[kb][e] * xa, LB[kb][e + 1] * xa);
+            }
           }
           const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
-          float* dbrow = dbase + (size_t)pp * g.r;
-          const bool do_local = kq == (rr % KW);  // each (row, column tile) once
+          const bool do_local = kq == (rr % KW);  // each (block, column tile) once
 #pragma unroll
           for (int cb = 0; cb < CH; cb++) {
             const int ct = cq * CH + cb;
@@ -997,7 +1015,106 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
             if (do_local) {
               const f4 lo = MM<bf16>::mma(dA, gb, f4{0.0f, 0.0f, 0.0f, 0.0f});
               const int col = 16 * ct + n;
-              if (q == 0 && col < g.r) dbrow[col] = lo[0];  // every group holds it; group 0 stores
+              if (col < g.r) {
+                if (q == 0) dbase[(size_t)pa * g.r + col] = lo[0];        // row 0 of the output
+                if (q == 1 && vb) dbase[(size_t)pb * g.r + col] = lo[0];  // row 4
+              }
+            }
+          }
+        }
+      } else {
+        // ---- d_bhat[(j,c)][col] += sum_t L[t,j] xhat[(j,c)][p] G[t][col]; local ----
+        float LB[KH][8];  // L[tslot(8q+e)][j of (j,c) = 16(kq*KH+kb)+n]
+  #pragma unroll
+        for (int kb = 0; kb < KH; kb++) {
+          const float* src = LT + ((16 * (kq * KH + kb) + n) / CK) * LTP + 4 * q;
+          const f4 l0 = *reinterpret_cast<const f4*>(src);
+          const f4 l1 = *reinterpret_cast<const f4*>(src + 16);
+  #pragma unroll
+          for (int e = 0; e < 4; e++) {
+            LB[kb][e] = l0[e];
+            LB[kb][e + 4] = l1[e];
+          }
+        }
+        bf8 dA;  // A operand of local: rows 0, 4, 8, 12 = d_t over the K-slots, t = tslot(8q+e)
+        {
+          const f4 d0 = *reinterpret_cast<const f4*>(s_d + 4 * q);
+          const f4 d1 = *reinterpret_cast<const f4*>(s_d + 16 + 4 * q);
+          const float on = (n & 3) == 0 ? 1.0f : 0.0f;
+  #pragma unroll
+          for (int e = 0; e < 4; e++) {
+            dA[e] = (bf16)(on * d0[e]);
+            dA[e + 4] = (bf16)(on * d1[e]);
+          }
+        }
+        if (pr0 + 4 <= g.p) {
+          // all four rows present: every G^T fragment of the round is loaded up
+          // front, so one LDS latency covers the whole phase
+          bf8 gbf[4][CH];
+  #pragma unroll
+          for (int rr = 0; rr < 4; rr++)
+  #pragma unroll
+            for (int cb = 0; cb < CH; cb++)
+              gbf[rr][cb] = ld_tok_frag<GTP>(Gs + (size_t)rr * ELL * GTP, cq * CH + cb, lane);
+          u4 Ab[4][KH];
+  #pragma unroll
+          for (int rr = 0; rr < 4; rr++)
+  #pragma unroll
+            for (int kb = 0; kb < KH; kb++) {
+              const float xk = (float)xs[(pr0 + rr - pblk) * KP + 16 * (kq * KH + kb) + n];
+  #pragma unroll
+              for (int e = 0; e < 8; e += 2) Ab[rr][kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
+            }
+  #pragma unroll
+          for (int rr = 0; rr < 4; rr++)
+  #pragma unroll
+            for (int cb = 0; cb < CH; cb++)
+  #pragma unroll
+              for (int kb = 0; kb < KH; kb++)
+                dbacc[kb][cb] = MM<bf16>::mma(as_bf8(Ab[rr][kb]), gbf[rr][cb], dbacc[kb][cb]);
+          // local of the rows rr with rr % KW == kq (each (row, column tile) once):
+          // every lane group holds the row sums (dA repeats d_t in rows 0, 4, 8,
+          // 12), and group q stores column tile q % CH
+  #pragma unroll
+          for (int rr = 0; rr < 4; rr++) {
+            if (rr % KW != kq) continue;
+            float* dbrow = dbase + (size_t)(pr0 + rr) * g.r;
+            float lq = 0.0f;
+  #pragma unroll
+            for (int cb = 0; cb < CH; cb++) {
+              const f4 lo = MM<bf16>::mma(dA, gbf[rr][cb], f4{0.0f, 0.0f, 0.0f, 0.0f});
+              lq = (q % CH) == cb ? lo[0] : lq;
+            }
+            const int col = 16 * (cq * CH + q % CH) + n;
+            if (q < CH && col < g.r) dbrow[col] = lq;
+          }
+        } else {
+  #pragma unroll 1
+          for (int rr = 0; rr < 4; rr++) {
+            const int pp = pr0 + rr;
+            if (pp >= g.p) break;
+            const int pl = pp - pblk;
+            u4 Ab[KH];
+  #pragma unroll
+            for (int kb = 0; kb < KH; kb++) {
+              const float xk = (float)xs[pl * KP + 16 * (kq * KH + kb) + n];
+  #pragma unroll
+              for (int e = 0; e < 8; e += 2) Ab[kb][e / 2] = pk_bf16(LB[kb][e] * xk, LB[kb][e + 1] * xk);
+            }
+            const bf16* Gr = Gs + (size_t)rr * ELL * GTP;
+            float* dbrow = dbase + (size_t)pp * g.r;
+            const bool do_local = kq == (rr % KW);  // each (row, column tile) once
+  #pragma unroll
+            for (int cb = 0; cb < CH; cb++) {
+              const int ct = cq * CH + cb;
+              const bf8 gb = ld_tok_frag<GTP>(Gr, ct, lane);
+  #pragma unroll
+              for (int kb = 0; kb < KH; kb++) dbacc[kb][cb] = MM<bf16>::mma(as_bf8(Ab[kb]), gb, dbacc[kb][cb]);
+              if (do_local) {
+                const f4 lo = MM<bf16>::mma(dA, gb, f4{0.0f, 0.0f, 0.0f, 0.0f});
+                const int col = 16 * ct + n;
+                if (q == 0 && col < g.r) dbrow[col] = lo[0];  // every group holds it; group 0 stores
+              }
             }
           }
         }
@@ -1005,7 +1122,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       __builtin_amdgcn_s_setprio(0);
     }
     __syncthreads();  // the last round's d_bhat reads are done
-    flush_dx(nc, (nrounds - 1) * 4 - ((nrounds - 1) * 4) % XPB);
+    flush_dx(nc, (nrounds - 1) * RR - ((nrounds - 1) * RR) % XPB);
 
     // ---- chunk end: d_bhat, the rotation gradient and the d_da partials go
     // through LDS behind one barrier: d_bhat in the G space, the rotation-gradient
@@ -1050,9 +1167,17 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         if (e >= g.RW) continue;
         const int half = tk >> 4;
         float s = 0.0f;
+        if constexpr (PO) {
+          // every wave holds the odd token slots 16..31; the even slots are zero
+          if (half == 1) {
 #pragma unroll
-        for (int uu = 0; uu < 4; uu++) s += RB[((4 * half + uu) * 16 + (tk & 15)) * rwq + el];
-        const int pos = nc * ELL + slot_tok(g, tk);
+            for (int w8 = 0; w8 < NWT; w8++) s += RB[(w8 * 16 + (tk & 15)) * rwq + el];
+          }
+        } else {
+#pragma unroll
+          for (int uu = 0; uu < 4; uu++) s += RB[((4 * half + uu) * 16 + (tk & 15)) * rwq + el];
+        }
+        const int pos = nc * ELL + slot_tok<PO>(tk);
         if (pos < g.s) d_rot[(((size_t)bi * g.s + pos) * g.h + hi) * g.RW + e] = (bf16)s;
       }
     };
@@ -1065,7 +1190,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       const float r = row16_sum(rwa[i]);
       if (n == 0) rwp[w * 16 + 4 * q + i] = r;
     }
-    if (tid < 4 * K) csum[tid] = cct;
+    if (tid < RR * K) csum[tid] = cct;
     // (the d_da partials are scanned at the start of the next step of the walk,
     // behind the barrier there, while the next chunk's loads are in flight)
     __syncthreads();
@@ -1076,7 +1201,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         for (int idx = tid; idx < K * (R / 8); idx += NTT) {
           const int k = idx / (R / 8), c8 = idx % (R / 8);
           const int j = k / CK, ci = k % CK;
-          const int pos = nc * ELL + slot_tok(g, j);
+          const int pos = nc * ELL + slot_tok<PO>(j);
           if (pos < g.s && ci < g.c && 8 * c8 < g.r)
             *reinterpret_cast<u4*>(d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8) =
                 *reinterpret_cast<const u4*>(DBs + k * SP + 8 * c8);
@@ -1085,7 +1210,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         for (int idx = tid; idx < K * g.r; idx += NTT) {
           const int k = idx / g.r, ra = idx - k * g.r;
           const int j = k / CK, ci = k % CK;
-          const int pos = nc * ELL + slot_tok(g, j);
+          const int pos = nc * ELL + slot_tok<PO>(j);
           if (pos < g.s && ci < g.c)
             d_bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + ra] = DBs[k * SP + inv_perm_rc(g, ra)];
         }

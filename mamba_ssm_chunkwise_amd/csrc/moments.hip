@@ -107,6 +107,7 @@ struct Plan {
   // backward over token pairs (bf16, c == 4): workspace regions after the pair
   // plan's own workspace (pair-token da, rot, their gradients, lengths)
   bool pair;
+  bool po;  // ... with every wave on the odd pair tokens (eight state rows a round)
   size_t pr_da2, pr_rot2, pr_dda2, pr_drot2, pr_lens2;
 };
 
@@ -142,13 +143,19 @@ size_t fwd4_lds(const Geo& g, int NT, int CK, bool inc) {
   return 0;
 }
 
-// LDS bytes of k_bwdt for (NT, CK), or 0 when that kernel does not cover the shape.
-size_t bwdt_lds(const Geo& g, int NT, int CK) {
+// LDS bytes of k_bwdt for (NT, CK) (po: the odd-pair-token variant), or 0 when
+// that kernel does not cover the shape.
+size_t bwdt_lds(const Geo& g, int NT, int CK, bool po = false) {
   const int RT = rot_tiles(g);
   auto one = [&](auto lt) -> size_t {
     using LT = typename decltype(lt)::type;
     return LT::fits(g.rot_kind, RT) ? LT::total(RT, g.rot_kind) : 0;
   };
+  if (po) {
+    if (NT == 4 && CK == 2) return one(TT<LdsT<4, 2, true>>{});
+    if (NT == 8 && CK == 2) return one(TT<LdsT<8, 2, true>>{});
+    return 0;
+  }
   if (NT == 4 && CK == 1) return one(TT<LdsT<4, 1>>{});
   if (NT == 4 && CK == 2) return one(TT<LdsT<4, 2>>{});
   if (NT == 8 && CK == 1) return one(TT<LdsT<8, 1>>{});
@@ -171,6 +178,10 @@ int make_pair_plan(const moments_desc* d, Plan* Pv) {
   const int rc = make_plan(&v, Pv);
   if (rc != MOMENTS_OK) return rc;
   Pv->g.pair = 1;
+  // the transposed backward walks token pairs in its odd-pair-token form only
+  const size_t lpo = bwdt_lds(Pv->g, Pv->NT, Pv->CK, true);
+  Pv->po = Pv->bwdt && lpo > 0 && lpo <= kLdsLimit;
+  Pv->bwdt = Pv->po;
   return MOMENTS_OK;
 }
 
@@ -270,6 +281,7 @@ int make_plan(const moments_desc* d, Plan* P) {
     P->fwdt = false;
     P->fwdt_inc = false;
   }
+  P->po = false;
   if (bf && P->CK <= 2) {
     const size_t lb = bwdt_lds(g, P->NT, P->CK);
     P->bwdt = lb > 0 && lb <= kLdsLimit;
@@ -516,6 +528,17 @@ int run_bwd(const Plan& P0, const void* xhat, const void* bhat, const void* da, 
       const int RT = rot_tiles(g);
       auto launch = [&](auto rot_c, auto rt_c) -> int {
         constexpr int RO = decltype(rot_c)::value, RTc = decltype(rt_c)::value;
+        if constexpr (CK == 2) {
+          if (P.po) {  // token pairs: every wave on the odd pair tokens
+            const size_t lds = LdsT<NT, CK, true>::total(RTc, RO);
+            MOM_TRY(set_lds(k_bwdt<NT, RO, CK, RTc, true>, lds));
+            ProfScope ps(KID_BWD, st);
+            hipLaunchKernelGGL((k_bwdt<NT, RO, CK, RTc, true>), dim3(chains * g.NGR), dim3(NTT), lds, st, g, X, B, D,
+                               Rt, (const float*)carry, dm2, (const float*)dm1i, Db, (T*)dx, (T*)db, (T*)dda, (T*)drot);
+            return check_launch();
+          }
+        }
+        if (P.g.pair) return MOMENTS_ENOTSUP;  // token pairs run the odd-pair-token form above
         const size_t lds = LdsT<NT, CK>::total(RTc, RO);
         MOM_TRY(set_lds(k_bwdt<NT, RO, CK, RTc>, lds));
         ProfScope ps(KID_BWD, st);
