@@ -481,13 +481,30 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   struct Pieces {
     f4 v[NPC];
   };
+  int fnc = 0;           // chunk of the walk (PO: the pieces' rows are addressed at each fetch)
+  bool fnext = false;    // ... and whether D(n+1) comes from it
   auto fetch_round = [&](int round) -> Pieces {
     Pieces r;
 #pragma unroll
     for (int k = 0; k < NPC; k++) {
       r.v[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (pc[k].fon && RR * round + pc[k].frr < g.p)
-        r.v[k] = load_cols4(pc[k].frow0 + (size_t)round * pc[k].fstep, pc[k].flim, pc[k].fcol, R);
+      if constexpr (PO) {
+        // two pieces per thread: their row pointers are not held across the round
+        const int farr = __builtin_amdgcn_readfirstlane((w * 64 + k * NTT) / CQA);
+        const int fidx = tid + k * NTT - farr * CQA;
+        const int row = RR * round + fidx / (R / 4), fcol = 4 * (fidx % (R / 4));
+        if (w * 64 + k * NTT < CQ && row < g.p) {
+          if (farr == 0)
+            r.v[k] = load_cols4(carry + (((size_t)bh * g.NK + fnc) * g.p + row) * g.r, g.r, fcol, R);
+          else if (farr == 1)
+            r.v[k] = load_cols4(dm1i + ((size_t)bh * g.p + row) * R, R, fcol, R);
+          else if (fnext)
+            r.v[k] = load_cols4(Db + (((size_t)bh * g.NK + fnc + 1) * g.p + row) * g.r, g.r, fcol, R);
+        }
+      } else {
+        if (pc[k].fon && RR * round + pc[k].frr < g.p)
+          r.v[k] = load_cols4(pc[k].frow0 + (size_t)round * pc[k].fstep, pc[k].flim, pc[k].fcol, R);
+      }
     }
     return r;
   };
@@ -575,8 +592,10 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   for (int nc = n1 - 1; nc >= n0; nc--) {
     asm volatile("" : "+v"(tid));
     const bool has_next = nc + 1 < n1;  // D(n+1) comes from this walk; zero at the group's end
+    fnc = nc;
+    fnext = has_next;
 #pragma unroll
-    for (int k = 0; k < NPC; k++) {
+    for (int k = 0; k < NPC && !PO; k++) {
       RowPiece& f = pc[k];
       if (f.farr == 0) {
         f.frow0 = carry + (((size_t)bh * g.NK + nc) * g.p + f.frr) * g.r;
