@@ -643,6 +643,9 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
   for (int n = n1 - 1; n >= n0 && Q != 0.0f; n--) {
     __syncthreads();
     stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
+    // staging and the <D_B, h_-(n)> sum issue their global loads in batches of
+    // eight per thread (one wait per batch rather than one per element)
+#pragma unroll 8
     for (int idx = threadIdx.x; idx < K * R; idx += NTH) {
       const int k = idx / R, rc = idx % R;
       const int j = k / CK, ci = k % CK;
@@ -651,6 +654,7 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
       if (rc < g.r && ci < g.c) v = to_f(bhat[((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, rc)]);
       bn[k * RP + rc] = to_t<T>(v);
     }
+#pragma unroll 8
     for (int idx = threadIdx.x; idx < K * PK; idx += NTH) {
       const int k = idx / PK, pp = idx % PK;
       const int j = k / CK, ci = k % CK;
@@ -661,12 +665,26 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
     }
     const float* Hn = carry + ((size_t)bh * g.NK + n) * pr;  // h_-(n), entering the chunk
     float hd = 0.0f;
-    for (int e = threadIdx.x; e < pr; e += NTH) hd += Dp[e] * Hn[e];
-    red[threadIdx.x] = hd;
+    {
+      float h8[8];
+#pragma unroll
+      for (int k = 0; k < 8; k++) h8[k] = 0.0f;
+      int e = threadIdx.x;
+      for (; e + 7 * NTH < pr; e += 8 * NTH) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) h8[k] += Dp[e + k * NTH] * Hn[e + k * NTH];
+      }
+      for (; e < pr; e += NTH) h8[0] += Dp[e] * Hn[e];
+      hd = ((h8[0] + h8[1]) + (h8[2] + h8[3])) + ((h8[4] + h8[5]) + (h8[6] + h8[7]));
+    }
+    // fixed-order sum over the workgroup: within each wave, then over the waves
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) hd += __shfl_xor(hd, off, 64);
+    if (lane == 0) red[w] = hd;
     __syncthreads();
     if (threadIdx.x == 0) {
       float s = 0.0f;
-      for (int i = 0; i < NTH; i++) s += red[i];
+      for (int i = 0; i < NW; i++) s += red[i];
       red[0] = s;
     }
     __syncthreads();
