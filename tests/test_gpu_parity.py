@@ -74,6 +74,8 @@ SMALL = [
     (W.ROT_PAIRWISE, "bf16", dict(c=4, p=16, r=32, rope_dim=6, valid_len=90)),
     (W.ROT_NONE, "bf16", dict(c=4, p=37, r=64, valid_len=95)),
     (W.ROT_QUAT, "bf16", dict(c=4, p=128, r=128, quat_blocks=32, valid_len=77, h0_sd=None)),
+    # ... with fewer state rows than one round holds (rows 3..7 of the round idle)
+    (W.ROT_PAIRWISE, "bf16", dict(c=4, p=3, r=24, rope_dim=8, valid_len=45)),
 ]
 
 
@@ -101,6 +103,8 @@ GROUPED = [
     (W.ROT_HALF, dict(b=8, h=64, s=256, valid_len=256, c=1, p=20, r=64, rope_dim=64, da_mu=0.5)),
     # ... with a partial last round of rows (p not a multiple of 4)
     (W.ROT_QUAT, dict(b=8, h=64, s=128, valid_len=120, c=2, p=18, r=64, quat_blocks=16, da_mu=-0.5)),
+    # four channels: the token-pair walk over several groups (group fix-up on pair tokens)
+    (W.ROT_QUAT, dict(b=1, h=4, s=2048, valid_len=2000, c=4, p=16, r=32, quat_blocks=8, da_mu=1.5)),
 ]
 
 
