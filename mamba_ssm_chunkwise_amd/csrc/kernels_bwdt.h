@@ -37,6 +37,13 @@
 // token sum of d_xhat, whose two partials meet in LDS. After a barrier the
 // eight waves accumulate d_bhat for the round's rows, each owning a block of
 // the (j,c) x column tiles.
+//
+// Four channels are walked as token pairs (pair token 2t: channels 0, 1 of token
+// t; 2t+1: channels 2, 3, whose state is token t's). Only odd pair tokens carry
+// moments, so the pair form (PO) puts the even pair tokens in slots 0..15 and
+// the odd ones in 16..31 and gives every wave the odd slots: a round then takes
+// eight state rows (the first half's waves rows 4..7), and each G block holds
+// two rows, one per half of its slots, for the d_bhat contraction.
 #pragma once
 
 #include "kernels.h"

@@ -165,7 +165,7 @@ OPTIONAL = [
     # the transposed bf16 kernels (c <= 2, 128 state columns)
     ("bf16", W.ROT_PAIRWISE, dict(c=2, p=64, r=128, rope_dim=64, valid_len=96)),
     ("bf16", W.ROT_QUAT, dict(c=1, p=40, r=128, quat_blocks=8, valid_len=90)),
-    # the general bf16 kernels (c = 4)
+    # four channels (the transposed backward over odd pair tokens)
     ("bf16", W.ROT_HALF, dict(c=4, p=33, r=128, rope_dim=64, valid_len=100)),
 ]
 WANTS = [("da", "h0"), ("xhat",), ("bhat", "rot"), ("rot",), ()]
