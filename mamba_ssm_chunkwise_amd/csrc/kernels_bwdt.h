@@ -454,9 +454,9 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
   };
   // The carry rows h_-(n)[p][:], the d_m1 rows and the D(n+1) rows of a round
-  // (RR state rows) travel through LDS: every thread fetches its float4 pieces
-  // of them a round ahead and stores them after the round's d_bhat work, off the
-  // rows' critical path. D(n+1) was written by this workgroup one chunk earlier.
+  // (RR state rows) travel through LDS: every thread with a piece loads its float4
+  // pieces of them a round ahead and stores them after the round's row work, off
+  // the rows' critical path. D(n+1) was written by this workgroup one chunk earlier.
   constexpr int CQA = RR * R / 4;          // float4 pieces of one array per round
   constexpr int CQ = 3 * CQA;              // pieces per round
   constexpr int NPC = (CQ + NTT - 1) / NTT;  // pieces per thread
@@ -541,19 +541,21 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
   const int n1 = (n0 + g.G < nkc) ? n0 + g.G : nkc;
   const int nrounds = (g.p + RR - 1) / RR;
   // ---- d_da of chunk ncs: sum_{t>=s} d_t <G[t], h_-> + sum_{s'<s} (C[s'] - Rw[s']),
-  // from the per-wave partials the chunk left in LDS (and its s_d, which the
-  // first wave alone rewrites, after this scan)
+  // from the per-wave partials the chunk left in LDS and its s_d, on the last
+  // wave (the first wave rewrites s_d only after the staging barrier that
+  // follows this scan)
   float* rg = (float*)(smem + L::red);  // [w][q][16] partial <G[t], h_->
   float* rwp = rg + NWT * 4 * 16;       // [w][16] partial row sums Rw
   float* csum = rwp + NWT * 16;         // [rr][(j,c)] partial column sums
   auto dda_scan = [&](int ncs) {
-    if (tid >= 64) return;
+    const int lt = tid - (NTT - 64);  // the last wave's lanes
+    if (lt < 0) return;
     // lane t < 32: x = d_t <G[t], h_->, y = C[t] - Rw[t]; then a suffix scan of x
     // and an exclusive prefix scan of y across the lanes (fixed order)
     const int tvs = g.V - ncs * ELL;
-    const int tk = tid & 31, sl = tok_slot<PO>(tk), half = sl >> 4;
+    const int tk = lt & 31, sl = tok_slot<PO>(tk), half = sl >> 4;
     float x = 0.0f, y = 0.0f;
-    if (tid < ELL) {
+    if (lt < ELL) {
       float gt = 0.0f, rw = 0.0f, cj = 0.0f;
       if constexpr (PO) {
         // every wave's partials are at the odd token slots 16..31; the even ones are zero
@@ -589,10 +591,10 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       if (tk >= off) y += yu;
     }
     const float yex = __shfl_up(y, 1, 32);
-    if (tid < ELL && d_da != nullptr) {
+    if (lt < ELL && d_da != nullptr) {
       const float pre = tk > 0 ? yex : 0.0f;
       // past valid_len every term vanishes; C - Rw cancels there only up to rounding
-      const int pos = ncs * ELL + tid;
+      const int pos = ncs * ELL + lt;
       if (pos < g.s) d_da[((size_t)bi * g.s + pos) * g.h + hi] = (bf16)(tk < tvs ? x + pre : 0.0f);
     }
   };
@@ -627,6 +629,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     load_chunk(nc);
     const Pieces v0 = fetch_round(0);
     // ---- chunk staging
+    float dnew = 0.0f;  // d_t of this chunk, lanes 0..31 of the first wave
     if (tid < 64) {
       const int tk = tid & 31;
       float v = dav;
@@ -636,9 +639,8 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         if (tk >= off) v += up;
       }
       if (tid < 32) {
-        const int sl = tok_slot<PO>(tk);  // lane tk is token tk of the chunk
-        s_a[sl] = v;
-        s_d[sl] = expf(v);
+        s_a[tok_slot<PO>(tk)] = v;  // lane tk is token tk of the chunk
+        dnew = expf(v);
       }
     }
     if (wide) {
@@ -678,34 +680,38 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
     }
     store_carry(v0, 0);
     store_dmdp(v0);
-    __syncthreads();
+    __syncthreads();  // (the last wave's scan of the previous chunk's s_d is done)
+    if (tid < 32) s_d[tok_slot<PO>(tid)] = dnew;
     for (int idx = tid; idx < ELL * ELL; idx += NTT) {
       const int j = idx / ELL, tk = idx % ELL;
       LT[j * LTP + tk] = (slot_tok<PO>(j) <= slot_tok<PO>(tk)) ? expf(s_a[tk] - s_a[j]) : 0.0f;
     }
     __syncthreads();
 
-    // ---- per-lane chunk constants (LDS tables, filled by wave 0's lanes) ----
+    // ---- per-lane chunk constants: LDS tables of entries per wave lane l =
+    // 16 ql + nl, filled by the whole workgroup ----------------------------------
     const int tv = g.V - nc * ELL;  // valid tokens of this chunk (<= 0: none)
-    if (w == 0) {
-      // W factors: L[16h+n][j of the slots 32ks+8q..], flattened (h*CK+ks)*(8/CK)+v
+    {
+      // W factors: L[16h+nl][j of the slots 32ks+8ql..], flattened (h*CK+ks)*(8/CK)+v
       // (PO: the second half h = 1 only, at entries f - 8)
-#pragma unroll
-      for (int f = PO ? 8 : 0; f < 16; f++) {
-        const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), v = rest % (8 / CK), fe = PO ? f - 8 : f;
-        reinterpret_cast<float*>(LWt + (fe >> 2) * 64 + lane)[fe & 3] =
-            LT[((32 * ks + 8 * q) / CK + v) * LTP + 16 * hh + n];
+      constexpr int NLW = PO ? 8 : 16;
+      for (int idx = tid; idx < NLW * 64; idx += NTT) {
+        const int fe = idx >> 6, l = idx & 63, ql = l >> 4, nl = l & 15;
+        const int f = PO ? fe + 8 : fe;
+        const int hh = f / 8, rest = f % 8, ks = rest / (8 / CK), v = rest % (8 / CK);
+        reinterpret_cast<float*>(LWt + (fe >> 2) * 64 + l)[fe & 3] =
+            LT[((32 * ks + 8 * ql) / CK + v) * LTP + 16 * hh + nl];
       }
-      // d_xhat factors: L[16h+4q+i][j of (j,c) = 16kt+n], entry h*NKT+kt (PO: h = 1, entry kt)
+      // d_xhat factors: L[16h+4ql+i][j of (j,c) = 16kt+nl], entry h*NKT+kt (PO: h = 1, entry kt)
+      constexpr int NLY = (PO ? 1 : 2) * NKT;
+      for (int idx = tid; idx < NLY * 64; idx += NTT) {
+        const int e = idx >> 6, l = idx & 63, ql = l >> 4, nl = l & 15;
+        const int hh = PO ? 1 : e / NKT, kt = e % NKT;
+        f4 v;
 #pragma unroll
-      for (int hh = PO ? 1 : 0; hh < 2; hh++)
-#pragma unroll
-        for (int kt = 0; kt < NKT; kt++) {
-          f4 v;
-#pragma unroll
-          for (int i = 0; i < 4; i++) v[i] = LT[((16 * kt + n) / CK) * LTP + 16 * hh + 4 * q + i];
-          LYt[((PO ? 0 : hh) * NKT + kt) * 64 + lane] = v;
-        }
+        for (int i = 0; i < 4; i++) v[i] = LT[((16 * kt + nl) / CK) * LTP + 16 * hh + 4 * ql + i];
+        LYt[e * 64 + l] = v;
+      }
     }
     __syncthreads();
 
