@@ -1,4 +1,9 @@
-"""Build the HIP library libmoments.so for gfx950 (in-tree, under _build/)."""
+"""Build the HIP library libmoments.so for gfx950 (in-tree, under _build/).
+
+Two translation units: moments.hip (the C ABI, the dispatcher and every kernel
+but the lane-pair forward) and fwd4.hip (the lane-pair forward's instances,
+compiled with the ILP machine-scheduling strategy). They are compiled in
+parallel and linked with no undefined symbols allowed."""
 from __future__ import annotations
 
 import os
@@ -7,28 +12,51 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "moments.hip")
+CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(OUT_DIR, "libmoments.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+# translation unit -> extra compiler flags
+UNITS = {
+    "moments.hip": [],
+    "fwd4.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
+def _clean(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if "packed-fp32-ops' is not a recognized" not in l)
 
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    procs = []
+    for unit, extra in UNITS.items():
+        obj = os.path.join(OUT_DIR, unit.replace(".hip", ".o"))
+        cmd = [HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, unit), "-o", obj]
+        procs.append((unit, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    errs = []
+    for unit, obj, p in procs:
+        _, err = p.communicate()
+        err = _clean(err)
+        if p.returncode != 0:
+            errs.append(f"hipcc failed on {unit} ({p.returncode}):\n{err}")
+        elif verbose and err.strip():
+            print(err, file=sys.stderr)
+    if errs:
+        raise RuntimeError("\n".join(errs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), SRC, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Wl,--no-undefined",
+           *[obj for _, obj, _ in procs], "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops' is not a recognized" not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed ({res.returncode}):\n{_clean(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

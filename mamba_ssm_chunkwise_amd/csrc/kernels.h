@@ -445,26 +445,4 @@ __global__ __launch_bounds__(NTH, 1) void k_fwd(Geo g, const T* __restrict__ xha
         m2o[(16 * (wi * NH + a) + 4 * q + i) * R + 16 * (wj * NH + b) + m] = m2acc[a][b][i];
 }
 
-// k_reduce: m2 = sum over the per-workgroup partials, m1 likewise; both
-// written in the caller's column order.
-__global__ __launch_bounds__(NTH) void k_reduce(Geo g, int R, const float* __restrict__ m2part,
-                                                const float* __restrict__ m1part, float* m2,
-                                                float* m1) {
-  const int bh = blockIdx.x;
-  const int e = blockIdx.y * NTH + threadIdx.x;
-  const int n2 = g.r * g.r, n1 = g.p * g.r;
-  if (e < n2) {
-    const int a = inv_perm_rc(g, e / g.r), b = inv_perm_rc(g, e % g.r);
-    float s = 0.0f;
-    for (int gi = 0; gi < g.NGR; gi++) s += m2part[((size_t)bh * g.NGR + gi) * R * R + a * R + b];
-    m2[(size_t)bh * n2 + e] = s;
-  } else if (e < n2 + n1) {
-    const int f = e - n2;
-    const int p0 = f / g.r, rc = inv_perm_rc(g, f % g.r);
-    float s = 0.0f;
-    for (int gi = 0; gi < g.NGR; gi++) s += m1part[((size_t)bh * g.NGR + gi) * g.p * R + p0 * R + rc];
-    m1[(size_t)bh * n1 + f] = s;
-  }
-}
-
 }  // namespace mom

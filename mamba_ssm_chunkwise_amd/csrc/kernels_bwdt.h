@@ -305,16 +305,6 @@ struct WideStage {
   }
 };
 
-// d_m1 in the internal column order, rows padded to R: dm1i[bh][p][R].
-__global__ __launch_bounds__(NTH) void k_prep_dm1(Geo g, int R, const float* __restrict__ dm1, float* dm1i) {
-  const size_t e = (size_t)blockIdx.x * NTH + threadIdx.x;
-  const size_t total = (size_t)g.b * g.h * g.p * R;
-  if (e >= total) return;
-  const int col = (int)(e % R);
-  const size_t row = e / R;
-  dm1i[e] = col < g.r ? dm1[row * g.r + perm_rc(g, col)] : 0.0f;
-}
-
 // Four consecutive internal columns 4q.. of a state row (zero past r).
 __device__ __forceinline__ f4 load_cols4(const float* row, int r, int col, int R) {
   if (r == R) return *reinterpret_cast<const f4*>(row + col);  // every column present

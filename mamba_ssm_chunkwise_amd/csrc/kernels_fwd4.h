@@ -708,30 +708,4 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
       }
 }
 
-// Fixed-order sum of the per-wave, per-group partials of k_fwd4, written in
-// the caller's column order.
-__global__ __launch_bounds__(NTH) void k_reduce4(Geo g, int R, int ord, const float* __restrict__ m2part,
-                                                 const float* __restrict__ m1part, float* m2, float* m1) {
-  const int bh = blockIdx.x;
-  const int e = blockIdx.y * NTH + threadIdx.x;
-  const int nR2 = R * R;
-  if (e < nR2) {
-    const int ia = e / R, ib = e % R;
-    const int a = lp_col(g, ord, ia), b = lp_col(g, ord, ib);
-    if (a < 0 || b < 0) return;
-    float s = 0.0f;
-    const int np = g.NGR * NW4;
-    for (int k = 0; k < np; k++) s += m2part[((size_t)bh * np + k) * nR2 + e];
-    m2[((size_t)bh * g.r + a) * g.r + b] = s;
-  } else if (e < nR2 + g.p * R) {
-    const int e1 = e - nR2;
-    const int pp = e1 / R, ic = e1 % R;
-    const int cc = lp_col(g, ord, ic);
-    if (cc < 0) return;
-    float s = 0.0f;
-    for (int gi = 0; gi < g.NGR; gi++) s += m1part[(((size_t)bh * g.NGR + gi) * g.p + pp) * R + ic];
-    m1[((size_t)bh * g.p + pp) * g.r + cc] = s;
-  }
-}
-
 }  // namespace mom

@@ -16,7 +16,9 @@
 #include "kernels_fwdt.h"
 #include "kernels_cscan.h"
 #include "kernels_fwd4.h"
+#include "kernels_reduce.h"
 #include "kernels_rot.h"
+#include "fwd4_launch.h"
 
 using namespace mom;
 
@@ -417,12 +419,11 @@ int run_fwd(const Plan& P0, const void* xhat, const void* bhat, const void* da, 
             auto go = [&](auto m1t_c, auto inc_c) -> int {
               constexpr int M1 = decltype(m1t_c)::value;
               constexpr int INC = decltype(inc_c)::value;
-              MOM_TRY(set_lds(k_fwd4<NT, RO, CK, RGc, M1, INC>, lds));
               ProfScope ps(KID_FWD, st);
-              hipLaunchKernelGGL((k_fwd4<NT, RO, CK, RGc, M1, INC>), dim3(chains * g.NGR), dim3(NT4), lds, st, g, X, B,
-                                 D, Rt, INC ? nullptr : (const float*)carry, (const T*)h0, m2p, m1p,
-                                 INC == 2 ? carry : nullptr, INC == 2 ? dec : nullptr);
-              return check_launch();
+              const hipError_t e = launch_fwd4<NT, RO, CK, RGc, M1, INC>(
+                  g, lds, (unsigned)(chains * g.NGR), st, X, B, D, Rt, INC ? nullptr : (const float*)carry,
+                  (const T*)h0, m2p, m1p, INC == 2 ? carry : nullptr, INC == 2 ? dec : nullptr);
+              return e == hipSuccess ? 0 : hip_fail(e);
             };
             if (P.fwd4_inc && saved != nullptr) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<2>{}) : go(IC<2>{}, IC<2>{}));
             else if (P.fwd4_inc) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<1>{}) : go(IC<2>{}, IC<1>{}));
