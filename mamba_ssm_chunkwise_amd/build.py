@@ -1,8 +1,9 @@
 """Build the HIP library libmoments.so for gfx950 (in-tree, under _build/).
 
-Two translation units: moments.hip (the C ABI, the dispatcher and every kernel
-but the lane-pair forward) and fwd4.hip (the lane-pair forward's instances,
-compiled with the ILP machine-scheduling strategy). They are compiled in
+Three translation units: moments.hip (the C ABI, the dispatcher and every
+kernel but the lane-pair forward), and fwd4.hip twice, for the lane-pair
+forward's instances that do not save carries (with the ILP machine-scheduling
+strategy) and for those that do (default strategy). They are compiled in
 parallel and linked with no undefined symbols allowed."""
 from __future__ import annotations
 
@@ -22,10 +23,11 @@ FLAGS = [
     # packed fp32 VALU ops are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
-# translation unit -> extra compiler flags
+# object -> (source, extra compiler flags)
 UNITS = {
-    "moments.hip": [],
-    "fwd4.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "moments.o": ("moments.hip", []),
+    "fwd4.o": ("fwd4.hip", ["-DMOM_FWD4_SAVE=0", "-mllvm", "-amdgpu-sched-strategy=max-ilp"]),
+    "fwd4_save.o": ("fwd4.hip", ["-DMOM_FWD4_SAVE=1"]),
 }
 
 
@@ -37,10 +39,10 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include")]
     procs = []
-    for unit, extra in UNITS.items():
-        obj = os.path.join(OUT_DIR, unit.replace(".hip", ".o"))
+    for name, (unit, extra) in UNITS.items():
+        obj = os.path.join(OUT_DIR, name)
         cmd = [HIPCC, *FLAGS, *extra, *inc, "-c", os.path.join(CSRC, unit), "-o", obj]
-        procs.append((unit, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        procs.append((name, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
     errs = []
     for unit, obj, p in procs:
         _, err = p.communicate()

@@ -1,9 +1,16 @@
 // The lane-pair forward's launches and every instance the dispatcher can ask
 // for (the library is linked with no undefined symbols, so a missing instance
-// fails the build). Compiled with the ILP scheduling strategy; see fwd4_launch.h.
+// fails the build). This file is compiled twice: with MOM_FWD4_SAVE = 0, the
+// instances that do not save carries, with the ILP scheduling strategy (see
+// fwd4_launch.h); with MOM_FWD4_SAVE = 1, those that also save the carries
+// (INC = 2), with the default strategy, which measured faster for them.
 #include "fwd4_launch.h"
 
 #include "kernels_fwd4.h"
+
+#ifndef MOM_FWD4_SAVE
+#error "compile with -DMOM_FWD4_SAVE=0 or 1"
+#endif
 
 namespace mom {
 
@@ -27,8 +34,11 @@ hipError_t launch_fwd4(const Geo& g, size_t lds, unsigned grid, hipStream_t st, 
   template hipError_t launch_fwd4<NT, RO, CK, RG, M1, INC>(                                                  \
       const Geo&, size_t, unsigned, hipStream_t, const bf16*, const bf16*, const bf16*, const bf16*,         \
       const float*, const bf16*, float*, float*, float*, float*);
-#define MOM_FWD4_INC(NT, RO, CK, RG, M1) \
-  MOM_FWD4_ONE(NT, RO, CK, RG, M1, 0) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 1) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 2)
+#if MOM_FWD4_SAVE
+#define MOM_FWD4_INC(NT, RO, CK, RG, M1) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 2)
+#else
+#define MOM_FWD4_INC(NT, RO, CK, RG, M1) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 0) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 1)
+#endif
 #define MOM_FWD4_M1(NT, RO, CK, RG) MOM_FWD4_INC(NT, RO, CK, RG, 1) MOM_FWD4_INC(NT, RO, CK, RG, 2)
 #define MOM_FWD4_CK(NT, RO, RG) MOM_FWD4_M1(NT, RO, 1, RG) MOM_FWD4_M1(NT, RO, 2, RG) MOM_FWD4_M1(NT, RO, 4, RG)
 

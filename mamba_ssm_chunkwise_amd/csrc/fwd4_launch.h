@@ -1,9 +1,10 @@
 // Launch of the lane-pair forward kernel k_fwd4. Its instances are compiled in
-// a translation unit of their own (fwd4.hip) with the machine scheduler's ILP
-// strategy: k_fwd4 runs one wave per SIMD, which overlaps its MFMAs with its
-// own VALU work only as far as its instruction stream interleaves them, and
-// that strategy interleaves them better than the default. The backward kernels
-// measured slower with it, so the rest of the library keeps the default.
+// translation units of their own (fwd4.hip), those that do not save carries
+// with the machine scheduler's ILP strategy: k_fwd4 runs one wave per SIMD,
+// which overlaps its MFMAs with its own VALU work only as far as its
+// instruction stream interleaves them, and that strategy interleaves them
+// better than the default. The backward kernels measured slower with it, so
+// the rest of the library keeps the default.
 #pragma once
 
 #include "common.h"
