@@ -324,6 +324,59 @@ __global__ __launch_bounds__(NTH) void k_scan(Geo g, const T* __restrict__ h0, f
   }
 }
 
+// k_scan4: k_scan on four consecutive state elements per thread (p r a multiple
+// of four), 16-byte loads and stores, with the next batch of chunks' U loads in
+// flight while the current batch is stored. Each element takes the same fp32
+// operations in the same order as in k_scan.
+template <typename T>
+__global__ __launch_bounds__(NTH) void k_scan4(Geo g, const T* __restrict__ h0, float* carry,
+                                               const float* __restrict__ dec) {
+  constexpr int B = 8;  // chunks per batch
+  const int bh = blockIdx.x;
+  const int e = 4 * (blockIdx.y * NTH + threadIdx.x);
+  const int pr = g.p * g.r;
+  if (e >= pr) return;
+  f4 h;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int p0 = (e + i) / g.r, rc = (e + i) % g.r;
+    h[i] = h0 ? to_f(h0[((size_t)bh * g.p + p0) * g.r + perm_rc(g, rc)]) : 0.0f;
+  }
+  float* C = carry + (size_t)bh * g.NK * pr + e;
+  const float* D = dec + (size_t)bh * g.NK;
+  const int last = g.NK - 1;
+  f4 u[B];
+  float dd[B];
+  auto load = [&](int n0) {
+#pragma unroll
+    for (int k = 0; k < B; k++) {
+      const int n = n0 + k;
+      u[k] = n < last ? *reinterpret_cast<const f4*>(C + (size_t)n * pr) : f4{0.0f, 0.0f, 0.0f, 0.0f};
+      dd[k] = n < last ? D[n] : 0.0f;
+    }
+  };
+  load(0);
+  for (int n0 = 0; n0 < g.NK; n0 += B) {
+    f4 uc[B];
+    float dc[B];
+#pragma unroll
+    for (int k = 0; k < B; k++) {
+      uc[k] = u[k];
+      dc[k] = dd[k];
+    }
+    if (n0 + B < g.NK) load(n0 + B);  // rows past this batch: not written by it
+#pragma unroll
+    for (int k = 0; k < B; k++) {
+      const int n = n0 + k;
+      if (n < g.NK) {
+        *reinterpret_cast<f4*>(C + (size_t)n * pr) = h;
+#pragma unroll
+        for (int i = 0; i < 4; i++) h[i] = dc[k] * h[i] + uc[k][i];
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_fwd: chunk states, de-rotation, m2 += c^T c and m1 += sum_t c. One workgroup
 // walks G chunks of one (b,h) chain; each round, wave w computes state row

@@ -728,7 +728,7 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
         flush_dx(nc, pblk - XPB);
         __syncthreads();
         if (wide) {
-          wst.load_x(g, xhat, nc, pblk, bi, hi, tid);
+          if constexpr (!PO) wst.load_x(g, xhat, nc, pblk, bi, hi, tid);  // (PO: loaded a round early)
           wst.store_x(xs, tid);
         } else {
           stage_x(nc, pblk);
@@ -972,6 +972,12 @@ __global__ __launch_bounds__(NTT, 1) void k_bwdt(
       store_carry(pf, (round + 1) & 1);  // its buffer was last read two rounds back
       __syncthreads();  // the round's G blocks and d_xhat partials are complete; next carry rows staged
       store_dmdp(pf);   // the round's d_c work, their only reader, is done
+      // (PO: the next xhat block, when the next round starts one, is in flight
+      // during this round's d_bhat work)
+      if constexpr (PO) {
+        if (wide && (RR * (round + 1)) % XPB == 0 && round + 1 < nrounds)
+          wst.load_x(g, xhat, nc, RR * (round + 1), bi, hi, tid);
+      }
       // ---- d_xhat of the round's rows: the two token halves added (PO: each
       // wave slot tt*4+u holds a whole row, rs = u or 4+u) -----------------------
       if (tid < RR * K) {

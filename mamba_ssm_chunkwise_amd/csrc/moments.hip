@@ -377,8 +377,12 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   if (g.NK >= 1) {
     const int pr = g.p * g.r;
     ProfScope ps(KID_SCAN, st);
-    hipLaunchKernelGGL((k_scan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, h0, carry,
-                       dec);
+    if (pr % 4 == 0)
+      hipLaunchKernelGGL((k_scan4<T>), dim3(chains, (pr / 4 + NTH - 1) / NTH), dim3(NTH), 0, st, g, h0, carry,
+                         dec);
+    else
+      hipLaunchKernelGGL((k_scan<T>), dim3(chains, (pr + NTH - 1) / NTH), dim3(NTH), 0, st, g, h0, carry,
+                         dec);
     MOM_TRY(check_launch());
   }
   return 0;
