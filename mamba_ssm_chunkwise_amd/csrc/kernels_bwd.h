@@ -16,6 +16,8 @@
 // exp(a_last(n)) D(n+1) has been scanned (k_dscan).
 #pragma once
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace mom {
@@ -639,14 +641,80 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
   }
   const int n0 = grp * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
+  // The <D_B, h_-(n)> sum of every chunk takes this thread's elements
+  // e = tid + i NTH. Up to NDI of them, the D_B values stay in registers for
+  // the whole walk and each chunk issues all of its h_-(n) loads at once.
+  constexpr int NDI = 64;
+  const bool dreg = pr <= NDI * NTH;
+  float dv[NDI];
+#pragma unroll
+  for (int i = 0; i < NDI; i++) {
+    const int e = threadIdx.x + i * NTH;
+    dv[i] = dreg && e < pr ? Dp[e] : 0.0f;
+  }
+  // bf16 rows of whole 16-byte pieces are staged with 16-byte loads, all issued
+  // before the first LDS store
+  constexpr bool WIDE_T = std::is_same<T, bf16>::value;
+  const bool wide = WIDE_T && g.r % 8 == 0 && g.p % 8 == 0;
   float Q = 1.0f;
   for (int n = n1 - 1; n >= n0 && Q != 0.0f; n--) {
     __syncthreads();
     stage_decay(g, da, bi, hi, n, s_a, s_d, s_L);
+    if constexpr (WIDE_T) {
+      if (wide) {
+        // items (k, piece of 8): bhat rows K x R/8, then xhat rows K x PK/8
+        constexpr int NBU = K * R / 8, NBL = (NBU + NTH - 1) / NTH;
+        u4 bv[NBL];
+#pragma unroll
+        for (int i = 0; i < NBL; i++) {
+          const int idx = threadIdx.x + i * NTH;
+          const int k = idx / (R / 8), c8 = idx % (R / 8);
+          const int j = k / CK, ci = k % CK, pos = n * ELL + j;
+          bv[i] = u4{0u, 0u, 0u, 0u};
+          if (idx < NBU && 8 * c8 < g.r && ci < g.c)
+            bv[i] = *reinterpret_cast<const u4*>(bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + 8 * c8);
+        }
+        const int NXU = K * PK / 8;
+        for (int idx0 = 0; idx0 < NXU; idx0 += 4 * NTH) {
+          u4 xv[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int idx = idx0 + threadIdx.x + i * NTH;
+            const int k = idx / (PK / 8), p8 = idx % (PK / 8);
+            const int j = k / CK, ci = k % CK, pos = n * ELL + j;
+            xv[i] = u4{0u, 0u, 0u, 0u};
+            if (idx < NXU && 8 * p8 < g.p && ci < g.c)
+              xv[i] = *reinterpret_cast<const u4*>(xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + 8 * p8);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int idx = idx0 + threadIdx.x + i * NTH;
+            if (idx < NXU) {
+              const int k = idx / (PK / 8), p8 = idx % (PK / 8);
+              *reinterpret_cast<u4*>(xn + k * PP + 8 * p8) = xv[i];
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NBL; i++) {
+          const int idx = threadIdx.x + i * NTH;
+          if (idx >= NBU) continue;
+          const int k = idx / (R / 8), c8 = idx % (R / 8);
+          const T* v = reinterpret_cast<const T*>(&bv[i]);
+          // caller columns 8c8.. sit at internal columns inv_perm_rc(..) < r;
+          // internal columns >= r are zero
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const int cc = 8 * c8 + e;
+            bn[k * RP + (cc < g.r ? inv_perm_rc(g, cc) : cc)] = v[e];
+          }
+        }
+      }
+    }
     // staging and the <D_B, h_-(n)> sum issue their global loads in batches of
     // eight per thread (one wait per batch rather than one per element)
 #pragma unroll 8
-    for (int idx = threadIdx.x; idx < K * R; idx += NTH) {
+    for (int idx = threadIdx.x; idx < K * R && !wide; idx += NTH) {
       const int k = idx / R, rc = idx % R;
       const int j = k / CK, ci = k % CK;
       const int pos = n * ELL + j;
@@ -655,7 +723,7 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
       bn[k * RP + rc] = to_t<T>(v);
     }
 #pragma unroll 8
-    for (int idx = threadIdx.x; idx < K * PK; idx += NTH) {
+    for (int idx = threadIdx.x; idx < K * PK && !wide; idx += NTH) {
       const int k = idx / PK, pp = idx % PK;
       const int j = k / CK, ci = k % CK;
       const int pos = n * ELL + j;
@@ -666,15 +734,36 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
     const float* Hn = carry + ((size_t)bh * g.NK + n) * pr;  // h_-(n), entering the chunk
     float hd = 0.0f;
     {
+      // elements e = tid + i NTH: i in blocks of eight while a whole block is
+      // below pr, the rest into h8[0] (the same sums in both forms)
       float h8[8];
 #pragma unroll
       for (int k = 0; k < 8; k++) h8[k] = 0.0f;
-      int e = threadIdx.x;
-      for (; e + 7 * NTH < pr; e += 8 * NTH) {
+      if (dreg) {
+        float hv[NDI];
 #pragma unroll
-        for (int k = 0; k < 8; k++) h8[k] += Dp[e + k * NTH] * Hn[e + k * NTH];
+        for (int i = 0; i < NDI; i++) {
+          const int e = threadIdx.x + i * NTH;
+          hv[i] = e < pr ? Hn[e] : 0.0f;
+        }
+        const int nb = threadIdx.x + 7 * NTH < pr ? (pr - threadIdx.x - 7 * NTH + 8 * NTH - 1) / (8 * NTH) : 0;
+#pragma unroll
+        for (int b = 0; b < NDI / 8; b++)
+          if (b < nb) {
+#pragma unroll
+            for (int k = 0; k < 8; k++) h8[k] += dv[8 * b + k] * hv[8 * b + k];
+          }
+#pragma unroll
+        for (int i = 0; i < NDI; i++)
+          if (i >= 8 * nb && threadIdx.x + i * NTH < pr) h8[0] += dv[i] * hv[i];
+      } else {
+        int e = threadIdx.x;
+        for (; e + 7 * NTH < pr; e += 8 * NTH) {
+#pragma unroll
+          for (int k = 0; k < 8; k++) h8[k] += Dp[e + k * NTH] * Hn[e + k * NTH];
+        }
+        for (; e < pr; e += NTH) h8[0] += Dp[e] * Hn[e];
       }
-      for (; e < pr; e += NTH) h8[0] += Dp[e] * Hn[e];
       hd = ((h8[0] + h8[1]) + (h8[2] + h8[3])) + ((h8[4] + h8[5]) + (h8[6] + h8[7]));
     }
     // fixed-order sum over the workgroup: within each wave, then over the waves
@@ -697,22 +786,47 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
       const int pos = n * ELL + j;
       const float lj = Q * ll[j];
       float xsum = 0.0f;
-      for (int mt = 0; mt < PK / 16; mt++) {
-        f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int ks = 0; ks < R / KS; ks++) {
-          const int k0 = ks * KS + E * q;
-          acc = MM<T>::mma(ld_frag(dp + (16 * mt + m) * RP + k0), ld_frag(bn + (16 * nt + m) * RP + k0), acc);
-        }
+      // row tiles in batches of eight: the d_xhat loads of a batch are issued
+      // together, then its stores
+      constexpr int MB = 8;
+      const int MT = PK / 16;
+      for (int mt0 = 0; mt0 < MT; mt0 += MB) {
+        f4 acc[MB];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const int pp = 16 * mt + 4 * q + i;
-          if (pp < g.p && ci < g.c) {
-            xsum += to_f(xn[k * PP + pp]) * acc[i];
-            if (d_xhat != nullptr) {
-              T* dst = d_xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p + pp;
-              *dst = to_t<T>(to_f(*dst) + lj * acc[i]);
+        for (int u = 0; u < MB; u++) {
+          acc[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+          if (mt0 + u < MT) {
+            for (int ks = 0; ks < R / KS; ks++) {
+              const int k0 = ks * KS + E * q;
+              acc[u] = MM<T>::mma(ld_frag(dp + (16 * (mt0 + u) + m) * RP + k0), ld_frag(bn + (16 * nt + m) * RP + k0),
+                                  acc[u]);
             }
           }
+        }
+#pragma unroll
+        for (int u = 0; u < MB; u++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int pp = 16 * (mt0 + u) + 4 * q + i;
+            if (mt0 + u < MT && pp < g.p && ci < g.c) xsum += to_f(xn[k * PP + pp]) * acc[u][i];
+          }
+        if (d_xhat != nullptr && ci < g.c) {
+          T* xrow = d_xhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.p;
+          T old[MB][4];
+#pragma unroll
+          for (int u = 0; u < MB; u++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int pp = 16 * (mt0 + u) + 4 * q + i;
+              old[u][i] = mt0 + u < MT && pp < g.p ? xrow[pp] : to_t<T>(0.0f);
+            }
+#pragma unroll
+          for (int u = 0; u < MB; u++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int pp = 16 * (mt0 + u) + 4 * q + i;
+              if (mt0 + u < MT && pp < g.p) xrow[pp] = to_t<T>(to_f(old[u][i]) + lj * acc[u][i]);
+            }
         }
       }
       xsum = col4_sum(xsum);
@@ -724,20 +838,33 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
         const int j = k / CK, ci = k % CK;
         const int pos = n * ELL + j;
         const float lj = Q * ll[j];
+        // all NT column tiles first, then their d_bhat loads together, then the stores
+        f4 acc[NT];
+#pragma unroll
         for (int mt = 0; mt < NT; mt++) {
-          f4 acc = f4{0.0f, 0.0f, 0.0f, 0.0f};
+          acc[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
           for (int ks = 0; ks < PK / KS; ks++) {
             const int k0 = ks * KS + E * q;
-            acc = MM<T>::mma(ld_frag(dpt + (16 * mt + m) * PP + k0), ld_frag(xn + (16 * nt + m) * PP + k0), acc);
+            acc[mt] = MM<T>::mma(ld_frag(dpt + (16 * mt + m) * PP + k0), ld_frag(xn + (16 * nt + m) * PP + k0), acc[mt]);
           }
+        }
+        if (ci < g.c) {
+          T* brow = d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r;
+          T old[NT][4];
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int rc = 16 * mt + 4 * q + i;
-            if (rc < g.r && ci < g.c) {
-              T* dst = d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r + perm_rc(g, rc);
-              *dst = to_t<T>(to_f(*dst) + lj * acc[i]);
+          for (int mt = 0; mt < NT; mt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int rc = 16 * mt + 4 * q + i;
+              old[mt][i] = rc < g.r ? brow[perm_rc(g, rc)] : to_t<T>(0.0f);
             }
-          }
+#pragma unroll
+          for (int mt = 0; mt < NT; mt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int rc = 16 * mt + 4 * q + i;
+              if (rc < g.r) brow[perm_rc(g, rc)] = to_t<T>(to_f(old[mt][i]) + lj * acc[mt][i]);
+            }
         }
       }
     }
