@@ -604,8 +604,9 @@ __global__ __launch_bounds__(NTH) void k_gscan(Geo g, const float* __restrict__ 
 //   d_da_s += d_{l-1} <D+, h_-(n)> + sum_{j<s} L[l-1,j] sum_c <xhat[j,c], v[:, (j,c)]>
 // (d_da in its direct form, as in k_bwdt).
 // Once Q underflows to zero every later term is exactly zero, so the walk stops.
+// (Two workgroups per CU where LDS allows: the register budget that sets.)
 template <typename T, int NT, int CK>
-__global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restrict__ xhat,
+__global__ __launch_bounds__(NTH, 2) void k_gfix(Geo g, int PK, const T* __restrict__ xhat,
                                                   const T* __restrict__ bhat, const T* __restrict__ da,
                                                   const float* __restrict__ carry, const float* __restrict__ dec,
                                                   const float* __restrict__ DB, T* d_xhat, T* d_bhat, T* d_da) {
@@ -641,17 +642,6 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
   }
   const int n0 = grp * g.G;
   const int n1 = (n0 + g.G < g.NK) ? n0 + g.G : g.NK;
-  // The <D_B, h_-(n)> sum of every chunk takes this thread's elements
-  // e = tid + i NTH. Up to NDI of them, the D_B values stay in registers for
-  // the whole walk and each chunk issues all of its h_-(n) loads at once.
-  constexpr int NDI = 64;
-  const bool dreg = pr <= NDI * NTH;
-  float dv[NDI];
-#pragma unroll
-  for (int i = 0; i < NDI; i++) {
-    const int e = threadIdx.x + i * NTH;
-    dv[i] = dreg && e < pr ? Dp[e] : 0.0f;
-  }
   // bf16 rows of whole 16-byte pieces are staged with 16-byte loads, all issued
   // before the first LDS store
   constexpr bool WIDE_T = std::is_same<T, bf16>::value;
@@ -734,36 +724,28 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
     const float* Hn = carry + ((size_t)bh * g.NK + n) * pr;  // h_-(n), entering the chunk
     float hd = 0.0f;
     {
-      // elements e = tid + i NTH: i in blocks of eight while a whole block is
-      // below pr, the rest into h8[0] (the same sums in both forms)
+      // elements e = tid + i NTH, in blocks of eight (h8[k] takes element k of
+      // each block) while a whole block is below pr, the rest into h8[0]; the
+      // loads of two blocks are issued together
       float h8[8];
 #pragma unroll
       for (int k = 0; k < 8; k++) h8[k] = 0.0f;
-      if (dreg) {
-        float hv[NDI];
+      int e = threadIdx.x;
+      for (; e + 15 * NTH < pr; e += 16 * NTH) {
+        float dv[16], hv[16];
 #pragma unroll
-        for (int i = 0; i < NDI; i++) {
-          const int e = threadIdx.x + i * NTH;
-          hv[i] = e < pr ? Hn[e] : 0.0f;
+        for (int k = 0; k < 16; k++) {
+          dv[k] = Dp[e + k * NTH];
+          hv[k] = Hn[e + k * NTH];
         }
-        const int nb = threadIdx.x + 7 * NTH < pr ? (pr - threadIdx.x - 7 * NTH + 8 * NTH - 1) / (8 * NTH) : 0;
 #pragma unroll
-        for (int b = 0; b < NDI / 8; b++)
-          if (b < nb) {
-#pragma unroll
-            for (int k = 0; k < 8; k++) h8[k] += dv[8 * b + k] * hv[8 * b + k];
-          }
-#pragma unroll
-        for (int i = 0; i < NDI; i++)
-          if (i >= 8 * nb && threadIdx.x + i * NTH < pr) h8[0] += dv[i] * hv[i];
-      } else {
-        int e = threadIdx.x;
-        for (; e + 7 * NTH < pr; e += 8 * NTH) {
-#pragma unroll
-          for (int k = 0; k < 8; k++) h8[k] += Dp[e + k * NTH] * Hn[e + k * NTH];
-        }
-        for (; e < pr; e += NTH) h8[0] += Dp[e] * Hn[e];
+        for (int k = 0; k < 16; k++) h8[k & 7] += dv[k] * hv[k];
       }
+      for (; e + 7 * NTH < pr; e += 8 * NTH) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) h8[k] += Dp[e + k * NTH] * Hn[e + k * NTH];
+      }
+      for (; e < pr; e += NTH) h8[0] += Dp[e] * Hn[e];
       hd = ((h8[0] + h8[1]) + (h8[2] + h8[3])) + ((h8[4] + h8[5]) + (h8[6] + h8[7]));
     }
     // fixed-order sum over the workgroup: within each wave, then over the waves
@@ -786,9 +768,9 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
       const int pos = n * ELL + j;
       const float lj = Q * ll[j];
       float xsum = 0.0f;
-      // row tiles in batches of eight: the d_xhat loads of a batch are issued
+      // row tiles in batches of four: the d_xhat loads of a batch are issued
       // together, then its stores
-      constexpr int MB = 8;
+      constexpr int MB = 4;
       const int MT = PK / 16;
       for (int mt0 = 0; mt0 < MT; mt0 += MB) {
         f4 acc[MB];
@@ -838,33 +820,39 @@ __global__ __launch_bounds__(NTH, 1) void k_gfix(Geo g, int PK, const T* __restr
         const int j = k / CK, ci = k % CK;
         const int pos = n * ELL + j;
         const float lj = Q * ll[j];
-        // all NT column tiles first, then their d_bhat loads together, then the stores
-        f4 acc[NT];
+        // column tiles in batches of four: the d_bhat loads of a batch are
+        // issued together, then its stores
+        constexpr int CB = NT < 4 ? NT : 4;
 #pragma unroll
-        for (int mt = 0; mt < NT; mt++) {
-          acc[mt] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-          for (int ks = 0; ks < PK / KS; ks++) {
-            const int k0 = ks * KS + E * q;
-            acc[mt] = MM<T>::mma(ld_frag(dpt + (16 * mt + m) * PP + k0), ld_frag(xn + (16 * nt + m) * PP + k0), acc[mt]);
+        for (int mt0 = 0; mt0 < NT; mt0 += CB) {
+          f4 acc[CB];
+#pragma unroll
+          for (int u = 0; u < CB; u++) {
+            acc[u] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int ks = 0; ks < PK / KS; ks++) {
+              const int k0 = ks * KS + E * q;
+              acc[u] = MM<T>::mma(ld_frag(dpt + (16 * (mt0 + u) + m) * PP + k0), ld_frag(xn + (16 * nt + m) * PP + k0),
+                                  acc[u]);
+            }
           }
-        }
-        if (ci < g.c) {
-          T* brow = d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r;
-          T old[NT][4];
+          if (ci < g.c) {
+            T* brow = d_bhat + ((((size_t)bi * g.s + pos) * g.c + ci) * g.h + hi) * g.r;
+            T old[CB][4];
 #pragma unroll
-          for (int mt = 0; mt < NT; mt++)
+            for (int u = 0; u < CB; u++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const int rc = 16 * mt + 4 * q + i;
-              old[mt][i] = rc < g.r ? brow[perm_rc(g, rc)] : to_t<T>(0.0f);
-            }
+              for (int i = 0; i < 4; i++) {
+                const int rc = 16 * (mt0 + u) + 4 * q + i;
+                old[u][i] = rc < g.r ? brow[perm_rc(g, rc)] : to_t<T>(0.0f);
+              }
 #pragma unroll
-          for (int mt = 0; mt < NT; mt++)
+            for (int u = 0; u < CB; u++)
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const int rc = 16 * mt + 4 * q + i;
-              if (rc < g.r) brow[perm_rc(g, rc)] = to_t<T>(to_f(old[mt][i]) + lj * acc[mt][i]);
-            }
+              for (int i = 0; i < 4; i++) {
+                const int rc = 16 * (mt0 + u) + 4 * q + i;
+                if (rc < g.r) brow[perm_rc(g, rc)] = to_t<T>(to_f(old[u][i]) + lj * acc[u][i]);
+              }
+          }
         }
       }
     }
