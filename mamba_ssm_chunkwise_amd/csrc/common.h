@@ -159,6 +159,9 @@ struct Geo {
   int pair;         // backward over token pairs: only odd tokens carry moments (see moments.hip)
   int skip;         // with per-sequence lengths: chunks past a sequence's length are not walked
                     // (set only when every kernel of the call skips them the same way)
+  int cstride;      // the carry pass stores the state entering chunk n only for n % cstride == 0
+                    // (1: every chunk; a forward that carries its state through each group of
+                    // cstride chunks reads only the states entering the groups)
 };
 
 // Kernel chunks a sequence walks: all NK, or with `skip` only those holding a

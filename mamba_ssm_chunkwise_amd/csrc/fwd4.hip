@@ -29,7 +29,8 @@ hipError_t launch_fwd4(const Geo& g, size_t lds, unsigned grid, hipStream_t st, 
 // Instances: column tiles NT in {4, 8}; (rotation, rotated column groups) with
 // RG * (2 for complex pairs, 4 for quaternions) <= NT; channel steps CK in
 // {1, 2, 4}; m1 row tiles M1T in {1, 2}; INC 0 (carries from the carry pass),
-// 1 (carried in LDS), 2 (carried in LDS and saved).
+// 1 (carried in LDS), 2 (carried in LDS and saved), 3 (carried in LDS through
+// each group from the carry pass's group-entry state).
 #define MOM_FWD4_ONE(NT, RO, CK, RG, M1, INC)                                                                \
   template hipError_t launch_fwd4<NT, RO, CK, RG, M1, INC>(                                                  \
       const Geo&, size_t, unsigned, hipStream_t, const bf16*, const bf16*, const bf16*, const bf16*,         \
@@ -37,7 +38,8 @@ hipError_t launch_fwd4(const Geo& g, size_t lds, unsigned grid, hipStream_t st, 
 #if MOM_FWD4_SAVE
 #define MOM_FWD4_INC(NT, RO, CK, RG, M1) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 2)
 #else
-#define MOM_FWD4_INC(NT, RO, CK, RG, M1) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 0) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 1)
+#define MOM_FWD4_INC(NT, RO, CK, RG, M1) \
+  MOM_FWD4_ONE(NT, RO, CK, RG, M1, 0) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 1) MOM_FWD4_ONE(NT, RO, CK, RG, M1, 3)
 #endif
 #define MOM_FWD4_M1(NT, RO, CK, RG) MOM_FWD4_INC(NT, RO, CK, RG, 1) MOM_FWD4_INC(NT, RO, CK, RG, 2)
 #define MOM_FWD4_CK(NT, RO, RG) MOM_FWD4_M1(NT, RO, 1, RG) MOM_FWD4_M1(NT, RO, 2, RG) MOM_FWD4_M1(NT, RO, 4, RG)

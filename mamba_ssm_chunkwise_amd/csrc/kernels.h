@@ -292,7 +292,8 @@ __global__ __launch_bounds__(NTH, 1) void k_carry(Geo g, int PK, const T* __rest
   if (threadIdx.x == 0) dec[(size_t)bh * g.NK + n] = s_d[ELL - 1];
 }
 
-// k_scan: h_-(0) = h0, h_-(n+1) = dec_n h_-(n) + U_n, written in place over U.
+// k_scan: h_-(0) = h0, h_-(n+1) = dec_n h_-(n) + U_n, written in place over U
+// (rows n % cstride == 0; the others keep U).
 template <typename T>
 __global__ __launch_bounds__(NTH) void k_scan(Geo g, const T* __restrict__ h0, float* carry,
                                               const float* __restrict__ dec) {
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(NTH) void k_scan(Geo g, const T* __restrict__ h0, f
     for (int k = 0; k < 8; k++) {
       const int n = n0 + k;
       if (n < g.NK) {
-        C[(size_t)n * pr] = h;
+        if (n % g.cstride == 0) C[(size_t)n * pr] = h;
         h = dd[k] * h + u[k];
       }
     }
@@ -369,7 +370,7 @@ __global__ __launch_bounds__(NTH) void k_scan4(Geo g, const T* __restrict__ h0, 
     for (int k = 0; k < B; k++) {
       const int n = n0 + k;
       if (n < g.NK) {
-        *reinterpret_cast<f4*>(C + (size_t)n * pr) = h;
+        if (n % g.cstride == 0) *reinterpret_cast<f4*>(C + (size_t)n * pr) = h;
 #pragma unroll
         for (int i = 0; i < 4; i++) h[i] = dc[k] * h[i] + uc[k][i];
       }

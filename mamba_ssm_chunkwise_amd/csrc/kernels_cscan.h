@@ -174,7 +174,7 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
 #pragma unroll
     for (int mi = 0; mi < MTW; mi++) {
       const int mt = w + CSW * mi;
-      if (mt >= MT) break;
+      if (mt >= MT || nc % g.cstride != 0) break;
 #pragma unroll
       for (int nt = 0; nt < NT; nt++) {
         if (16 * nt + m >= g.r) continue;

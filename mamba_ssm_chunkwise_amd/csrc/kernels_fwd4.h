@@ -265,7 +265,9 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
   const int nrow = (g.p - w + 3) / 4;  // rows of this wave: p = w + 4k
 
   // INC 0: entering states from the carry pass; 1: carried in LDS (carry ==
-  // nullptr); 2: carried, and also written to `save` / `save_dec`
+  // nullptr); 2: carried, and also written to `save` / `save_dec`; 3: carried in
+  // LDS through the group, from the carry pass's state entering its first chunk
+  // (the only one of the group's states that carry pass stores)
   constexpr bool inc = INC != 0;
   // index of this lane's columns in the carry-pass rows (their column order
   // interleaves half-split pairs), -1 for padding
@@ -283,10 +285,16 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
     sic[u] = INC == 2 && col < g.r ? lp_ic(g, ORD, perm_rc(g, col)) : -1;
   }
   if (inc) {
+    const float* c0 = INC == 3 ? carry + ((size_t)bh * g.NK + (size_t)gi * g.G) * g.p * g.r : nullptr;
     for (int idx = tid; idx < g.p * R; idx += NT4) {
       const int pp = idx / R, ic = idx % R;
       const int cc = lp_col(g, ORD, ic);
-      const float v = (h0 != nullptr && cc >= 0) ? (float)h0[((size_t)bh * g.p + pp) * g.r + cc] : 0.0f;
+      float v = 0.0f;
+      if (INC == 3) {
+        if (cc >= 0) v = c0[(size_t)pp * g.r + inv_perm_rc(g, cc)];  // carry-pass column order
+      } else if (h0 != nullptr && cc >= 0) {
+        v = (float)h0[((size_t)bh * g.p + pp) * g.r + cc];
+      }
       carryL[idx] = v;
     }
   }

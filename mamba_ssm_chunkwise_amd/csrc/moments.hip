@@ -222,6 +222,7 @@ int make_plan(const moments_desc* d, Plan* P) {
   g.b = (int)d->b; g.s = (int)d->s; g.c = (int)d->c; g.h = (int)d->h; g.p = (int)d->p; g.r = (int)d->r;
   g.V = (int)(d->valid_len < d->s ? d->valid_len : d->s);
   g.NK = (g.V + ELL - 1) / ELL;
+  g.cstride = 1;
   P->bf = bf;
   P->CK = g.c <= 1 ? 1 : g.c <= 2 ? 2 : 4;
   g.K = ELL * P->CK;
@@ -411,26 +412,37 @@ int run_fwd(const Plan& P0, const void* xhat, const void* bhat, const void* da, 
   const int chains = g.b * g.h;
   if constexpr (std::is_same<T, bf16>::value) {
     if (P.fwd4) {
-      if (!P.fwd4_inc) MOM_TRY((launch_carry_scan<T, NT, CK>(P, X, B, D, (const T*)h0, carry, dec, st)));
+      // A forward over several groups per chain, with no saved buffer, carries
+      // its state rows through each group in LDS when they fit there; its carry
+      // pass then stores only the states entering the groups.
+      const bool grp_inc =
+          !P.fwd4_inc && saved == nullptr && g.NGR > 1 && fwd4_lds(g, P.NT, P.CK, true) <= kLdsLimit;
+      if (!P.fwd4_inc) {
+        Plan Pc = P;
+        if (grp_inc) Pc.g.cstride = g.G;
+        MOM_TRY((launch_carry_scan<T, NT, CK>(Pc, X, B, D, (const T*)h0, carry, dec, st)));
+      }
       const int RG = rot_groups(g);
       auto launch = [&](auto rot_c, auto rg_c) -> int {
         constexpr int RO = decltype(rot_c)::value, RGc = decltype(rg_c)::value;
         if constexpr (RGc * (RO == 3 ? 4 : 2) > NT) {
           return MOMENTS_ENOTSUP;
         } else {
-          const size_t lds = fwd4_lds(g, NT, CK, P.fwd4_inc);
+          const size_t lds = fwd4_lds(g, NT, CK, P.fwd4_inc || grp_inc);
           if (g.NK >= 1) {
             auto go = [&](auto m1t_c, auto inc_c) -> int {
               constexpr int M1 = decltype(m1t_c)::value;
               constexpr int INC = decltype(inc_c)::value;
               ProfScope ps(KID_FWD, st);
               const hipError_t e = launch_fwd4<NT, RO, CK, RGc, M1, INC>(
-                  g, lds, (unsigned)(chains * g.NGR), st, X, B, D, Rt, INC ? nullptr : (const float*)carry,
+                  g, lds, (unsigned)(chains * g.NGR), st, X, B, D, Rt,
+                  INC == 0 || INC == 3 ? (const float*)carry : nullptr,
                   (const T*)h0, m2p, m1p, INC == 2 ? carry : nullptr, INC == 2 ? dec : nullptr);
               return e == hipSuccess ? 0 : hip_fail(e);
             };
             if (P.fwd4_inc && saved != nullptr) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<2>{}) : go(IC<2>{}, IC<2>{}));
             else if (P.fwd4_inc) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<1>{}) : go(IC<2>{}, IC<1>{}));
+            else if (grp_inc) MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<3>{}) : go(IC<2>{}, IC<3>{}));
             else MOM_TRY(g.p <= 64 ? go(IC<1>{}, IC<0>{}) : go(IC<2>{}, IC<0>{}));
           }
           const int nout = P.R * P.R + g.p * P.R;
