@@ -91,13 +91,14 @@ struct LdsF4 {
   __host__ __device__ static size_t carryL(int pp, int rot_kind, int RG) {
     return al16(rot(pp) + (RG > 0 ? (size_t)ELL * rpitch(rot_kind, RG) * 4 : 0));
   }
-  // scratch rows for the carry stores of lanes that do not hold the last token
+  // a scratch slot per lane (and wave) for the carry stores of lanes that do
+  // not hold the last token: their values are discarded
   __host__ __device__ static size_t dummy(int pp, int rot_kind, int RG, bool inc) {
     return carryL(pp, rot_kind, RG) + (inc ? (size_t)pp * R * 4 : 0);
   }
   // total: with the state rows carried in LDS ([p][R] fp32) or not
   __host__ __device__ static size_t total(int pp, int rot_kind, int RG, bool inc) {
-    return dummy(pp, rot_kind, RG, inc) + (inc ? (size_t)NW4 * NT * 64 * 4 : 0);
+    return dummy(pp, rot_kind, RG, inc) + (inc ? (size_t)NW4 * 64 * 4 : 0);
   }
 };
 
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
   // The row work of one chunk (see the software pipeline at its call). Tokens
   // past valid_len have zero W factors and decays, so their states, and c,
   // come out as exact zeros.
-  float* dummyL = (float*)(smem + L::dummy(PP, ROT, RG, inc)) + (size_t)w * NT * 64;
+  float* dummyL = (float*)(smem + L::dummy(PP, ROT, RG, inc)) + (size_t)w * 64;
   auto rows = [&](const float (&dtok)[2][4], const float (&lw)[2][CK][8 / CK]) {
     if (nrow == 0) return;
     using RV = typename std::conditional<ROT == 3, f4, fl2>::type;
@@ -390,9 +391,9 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
           for (int i = 0; i < 4; i++) h[tt][ct][i] += dtok[tt][i] * hv[ct];
       if constexpr (inc) {
         // the state at the chunk's last token (lanes q = 3) enters the next chunk;
-        // the other lanes, and repeated rows, store to a scratch row instead
+        // the other lanes, and repeated rows, store to their scratch slot instead
         float* dst = (q == 3 && real) ? carryL + pr * R + n : dummyL + lane;
-        const int step = (q == 3 && real) ? 16 : 64;
+        const int step = (q == 3 && real) ? 16 : 0;
 #pragma unroll
         for (int ct = 0; ct < NT; ct++) dst[ct * step] = h[1][ct][3];
       }
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(NT4, 1) void k_fwd4(Geo g, const bf16* __restrict__
           for (int i = 0; i < 4; i++) h[tt][gr * GS + u][i] += dtok[tt][i] * hv[gr * GS + u];
       if constexpr (inc) {
         float* dst = (q == 3 && real) ? carryL + pr * R + n : dummyL + lane;
-        const int stp = (q == 3 && real) ? 16 : 64;
+        const int stp = (q == 3 && real) ? 16 : 0;
 #pragma unroll
         for (int u = 0; u < GS; u++) dst[(gr * GS + u) * stp] = h[1][gr * GS + u][3];
       }
