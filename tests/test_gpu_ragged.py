@@ -102,6 +102,10 @@ CASES = [
     # 512 chains: one workgroup per chain, the forward carries its own state
     (_small("rg_bf16_pair_carried", "bf16", W.ROT_PAIRWISE, b=4, h=128, p=8, r=32, s=64, valid_len=64),
      [64, 33, 1, 50], [0, 77, 127]),
+    # 16 chains of 64 chunks: groups of two chunks, the forward carries its state through each
+    # group from the group-entry states its carry pass stores; one sequence ends mid-group
+    (_small("rg_bf16_quat_grouped", "bf16", W.ROT_QUAT, b=2, h=8, c=2, p=16, r=32, quat_blocks=8, s=2048,
+            valid_len=2048, chunk_len=64), [1500, 2048], [0, 7]),
 ]
 
 
