@@ -48,7 +48,13 @@ __device__ __forceinline__ bf8 ld_kx_frag(const bf16* blk, int P, int ks, int x0
 }
 
 // MTW: row tiles per wave (1: state rows <= 64, 2: <= 128).
-template <int NT, int CK, int MTW>
+// GS: group summaries instead of carries. Workgroup (chain, group gi) walks the
+// group's G chunks from a zero state and leaves Z, the state after the group,
+// in the carry rows of chunk gi G + 1 and the product D of its chunk decays in
+// dec at that chunk (slots a forward that carries its state through each group
+// never reads); k_gentry then forms the states entering the groups. The last
+// group of a chain passes nothing on and returns at once.
+template <int NT, int CK, int MTW, bool GS = false>
 __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __restrict__ xhat,
                                                const bf16* __restrict__ bhat, const bf16* __restrict__ da,
                                                const bf16* __restrict__ h0, float* carry, float* dec) {
@@ -63,7 +69,8 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
   bf16* bs = (bf16*)(smem + L::bs(PK));
   float* wv = (float*)(smem + L::wv(PK));  // per buffer: exp(a_last - a_j), j < ELL; then dec
 
-  const int bh = blockIdx.x, bi = bh / g.h, hi = bh % g.h;
+  const int bh = GS ? blockIdx.x / g.NGR : blockIdx.x, bi = bh / g.h, hi = bh % g.h;
+  const int gi = GS ? blockIdx.x % g.NGR : 0;
   g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, q = lane >> 4;
   const int MT = PK / 16;
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int row = 16 * (w + CSW * mi) + 4 * q + i, col = 16 * nt + m;
-        acc[mi][nt][i] = (h0 != nullptr && row < g.p && col < g.r)
+        acc[mi][nt][i] = (!GS && h0 != nullptr && row < g.p && col < g.r)
                              ? (float)h0[((size_t)bh * g.p + row) * g.r + col] : 0.0f;
       }
   // internal position of this lane's columns (half-split interleaves the halves)
@@ -164,17 +171,23 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
   for (int nt = 0; nt < NT; nt++) icol[nt] = 16 * nt + m < g.r ? inv_perm_rc(g, 16 * nt + m) : 0;
 
   const int nkc = chain_nk(g);  // chunks walked (carries past them are not written)
-  if (nkc > 1) store(fetch(0), 0);
+  // chunks n0 .. n1-1: the whole walk, or a group none of whose chunks is the last
+  const int n0 = GS ? gi * g.G : 0;
+  const int n1 = GS ? (n0 + g.G < nkc ? n0 + g.G : nkc) : nkc;
+  if (GS && n1 >= nkc) return;
+  if (GS || nkc > 1) store(fetch(n0), 0);
   __syncthreads();
-  for (int nc = 0; nc < nkc; nc++) {
-    const bool more = nc + 2 < nkc;  // chunk nc+1 contributes U only if it is not the last
+  float dprod = 1.0f;  // GS: product of the group's chunk decays
+  for (int nc = n0; nc < n1; nc++) {
+    // chunk nc+1 contributes U only if it is not the last (in a group it never is)
+    const bool more = GS ? nc + 1 < n1 : nc + 2 < nkc;
     Pf pf;
     if (more) pf = fetch(nc + 1);
     float* out = carry + ((size_t)bh * g.NK + nc) * pr;
 #pragma unroll
     for (int mi = 0; mi < MTW; mi++) {
       const int mt = w + CSW * mi;
-      if (mt >= MT || nc % g.cstride != 0) break;
+      if (GS || mt >= MT || nc % g.cstride != 0) break;
 #pragma unroll
       for (int nt = 0; nt < NT; nt++) {
         if (16 * nt + m >= g.r) continue;
@@ -185,11 +198,12 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
         }
       }
     }
-    if (nc + 1 < nkc) {
-      const int b = nc & 1;
+    if (GS || nc + 1 < nkc) {
+      const int b = (nc - n0) & 1;
       const float* wb = wv + b * (ELL + 4);
       const float dn = wb[ELL];
-      if (tid == 0) dec[(size_t)bh * g.NK + nc] = dn;
+      if (GS) dprod *= dn;
+      else if (tid == 0) dec[(size_t)bh * g.NK + nc] = dn;
       const bf16* xb = xs + (size_t)b * K * XP;
       const bf16* bb = bs + (size_t)b * K * BP;
 #pragma unroll
@@ -216,8 +230,49 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
         }
       }
     }
-    if (more) store(pf, (nc + 1) & 1);
+    if (more) store(pf, (nc + 1 - n0) & 1);
     __syncthreads();
+  }
+  if constexpr (GS) {
+    float* out = carry + ((size_t)bh * g.NK + n0 + 1) * pr;
+#pragma unroll
+    for (int mi = 0; mi < MTW; mi++) {
+      const int mt = w + CSW * mi;
+      if (mt >= MT) break;
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++) {
+        if (16 * nt + m >= g.r) continue;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int row = 16 * mt + 4 * q + i;
+          if (row < g.p) out[(size_t)row * g.r + icol[nt]] = acc[mi][nt][i];
+        }
+      }
+    }
+    if (tid == 0) dec[(size_t)bh * g.NK + n0 + 1] = dprod;
+  }
+}
+
+// States entering the groups from the group summaries of k_cscan<.., true>:
+// E_0 = h0 and E_{g+1} = D_g E_g + Z_g, element by element, written to the carry
+// rows of each group's first chunk (carry layout: internal column order).
+__global__ __launch_bounds__(NTH) void k_gentry(Geo g, const bf16* __restrict__ h0, float* carry,
+                                                const float* __restrict__ dec) {
+  const int bh = blockIdx.x, bi = bh / g.h;
+  const size_t pr = (size_t)g.p * g.r;
+  const size_t e = (size_t)blockIdx.y * NTH + threadIdx.x;
+  if (e >= pr) return;
+  g.V = chain_len(g, bi);
+  const int nkc = chain_nk(g);
+  const int row = (int)(e / g.r), ic = (int)(e % g.r);
+  float E = h0 != nullptr ? (float)h0[((size_t)bh * g.p + row) * g.r + perm_rc(g, ic)] : 0.0f;
+  for (int gi = 0; gi < g.NGR; gi++) {
+    const int n0 = gi * g.G;
+    if (n0 >= nkc) break;
+    carry[((size_t)bh * g.NK + n0) * pr + e] = E;
+    if (n0 + g.G >= nkc) break;  // the last group's summary is not formed
+    const size_t zs = (size_t)bh * g.NK + n0 + 1;
+    E = dec[zs] * E + carry[zs * pr + e];
   }
 }
 

@@ -37,12 +37,12 @@ constexpr size_t kLdsLimit = 160 * 1024;
 // ---- optional per-kernel event timing (moments_profile_*) -------------------
 enum KernelId {
   KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_PREP, KID_GSCAN, KID_GFIX,
-  KID_CSCAN, KID_ROTSEG, KID_ROTCARRY, KID_ROTAPPLY, KID_PAIR, KID_N
+  KID_CSCAN, KID_ROTSEG, KID_ROTCARRY, KID_ROTAPPLY, KID_PAIR, KID_GENTRY, KID_N
 };
 const char* const kKernelNames[KID_N] = {"k_carry", "k_scan",      "k_fwd",      "k_reduce", "k_bwd",  "k_dscan",
                                          "k_fix",   "k_zero_tail", "k_prep_dm1", "k_gscan",  "k_gfix",
                                          "k_cscan", "k_rot_seg",   "k_rot_carry", "k_rot_apply",
-                                         "k_pair"};
+                                         "k_pair",  "k_gentry"};
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -389,6 +389,34 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   return 0;
 }
 
+// The states entering each group (and only those) for a forward that carries
+// its state through each group: per-group walks from a zero state (k_cscan in
+// its group-summary form, in parallel over the groups) and a scan over the
+// groups (k_gentry). Needs groups of two chunks or more; returns
+// MOMENTS_ENOTSUP when k_cscan does not cover the shape.
+template <int NT, int CK>
+int launch_group_entries(const Plan& P, const bf16* xhat, const bf16* bhat, const bf16* da, const bf16* h0,
+                         float* carry, float* dec, hipStream_t st) {
+  const Geo& g = P.g;
+  const int chains = g.b * g.h;
+  const size_t lds = LdsC<NT, CK>::total(P.PK);
+  if (g.G < 2 || g.NGR < 2 || P.PK > 16 * CSW * CMT || lds > kLdsLimit) return MOMENTS_ENOTSUP;
+  auto launch = [&](auto mtw_c) -> int {
+    constexpr int MTW = decltype(mtw_c)::value;
+    MOM_TRY(set_lds(k_cscan<NT, CK, MTW, true>, lds));
+    ProfScope ps(KID_CSCAN, st);
+    hipLaunchKernelGGL((k_cscan<NT, CK, MTW, true>), dim3(chains * g.NGR), dim3(CST), lds, st, g, P.PK, xhat, bhat,
+                       da, h0, carry, dec);
+    return check_launch();
+  };
+  MOM_TRY(P.PK <= 16 * CSW ? launch(IC<1>{}) : launch(IC<2>{}));
+  const size_t pr = (size_t)g.p * g.r;
+  ProfScope ps(KID_GENTRY, st);
+  hipLaunchKernelGGL(k_gentry, dim3(chains, (unsigned)((pr + NTH - 1) / NTH)), dim3(NTH), 0, st, g, h0, carry,
+                     (const float*)dec);
+  return check_launch();
+}
+
 // saved != nullptr: also leave the carries and chunk decays in the caller's
 // buffer (the carrying kernels write them; otherwise the carry pass writes there).
 template <typename T, int NT, int ROT, int CK>
@@ -418,9 +446,17 @@ int run_fwd(const Plan& P0, const void* xhat, const void* bhat, const void* da, 
       const bool grp_inc =
           !P.fwd4_inc && saved == nullptr && g.NGR > 1 && fwd4_lds(g, P.NT, P.CK, true) <= kLdsLimit;
       if (!P.fwd4_inc) {
-        Plan Pc = P;
-        if (grp_inc) Pc.g.cstride = g.G;
-        MOM_TRY((launch_carry_scan<T, NT, CK>(Pc, X, B, D, (const T*)h0, carry, dec, st)));
+        // the group entries from per-group summaries where they apply, else a
+        // carry pass that stores only those entries (or, without grp_inc, all)
+        const int rc = grp_inc ? launch_group_entries<NT, CK>(P, X, B, D, (const T*)h0, carry, dec, st)
+                               : MOMENTS_ENOTSUP;
+        if (rc == MOMENTS_ENOTSUP) {
+          Plan Pc = P;
+          if (grp_inc) Pc.g.cstride = g.G;
+          MOM_TRY((launch_carry_scan<T, NT, CK>(Pc, X, B, D, (const T*)h0, carry, dec, st)));
+        } else {
+          MOM_TRY(rc);
+        }
       }
       const int RG = rot_groups(g);
       auto launch = [&](auto rot_c, auto rg_c) -> int {
