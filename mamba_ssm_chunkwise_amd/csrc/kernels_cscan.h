@@ -48,13 +48,15 @@ __device__ __forceinline__ bf8 ld_kx_frag(const bf16* blk, int P, int ks, int x0
 }
 
 // MTW: row tiles per wave (1: state rows <= 64, 2: <= 128).
-// GS: group summaries instead of carries. Workgroup (chain, group gi) walks the
-// group's G chunks from a zero state and leaves Z, the state after the group,
-// in the carry rows of chunk gi G + 1 and the product D of its chunk decays in
-// dec at that chunk (slots a forward that carries its state through each group
-// never reads); k_gentry then forms the states entering the groups. The last
-// group of a chain passes nothing on and returns at once.
-template <int NT, int CK, int MTW, bool GS = false>
+// GM: 0 walks each chain from h0 and stores every carry. 1 (group summaries):
+// workgroup (chain, group gi) walks the group's G chunks from a zero state and
+// leaves Z, the state after the group, in the carry rows of chunk gi G + 1 and
+// the product D of its chunk decays in dec at that chunk (slots a forward that
+// carries its state through each group never reads); k_gentry then forms the
+// states entering the groups, and the last group of a chain returns at once.
+// 2 (group carries): each group is walked from the state k_gentry left in its
+// first chunk's carry rows, storing every carry and decay of the group.
+template <int NT, int CK, int MTW, int GM = 0>
 __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __restrict__ xhat,
                                                const bf16* __restrict__ bhat, const bf16* __restrict__ da,
                                                const bf16* __restrict__ h0, float* carry, float* dec) {
@@ -69,8 +71,9 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
   bf16* bs = (bf16*)(smem + L::bs(PK));
   float* wv = (float*)(smem + L::wv(PK));  // per buffer: exp(a_last - a_j), j < ELL; then dec
 
-  const int bh = GS ? blockIdx.x / g.NGR : blockIdx.x, bi = bh / g.h, hi = bh % g.h;
-  const int gi = GS ? blockIdx.x % g.NGR : 0;
+  constexpr bool GS = GM == 1;  // group summaries
+  const int bh = GM ? blockIdx.x / g.NGR : blockIdx.x, bi = bh / g.h, hi = bh % g.h;
+  const int gi = GM ? blockIdx.x % g.NGR : 0;
   g.V = chain_len(g, bi);  // this sequence's valid length (per-sequence lengths)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, m = lane & 15, q = lane >> 4;
   const int MT = PK / 16;
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int row = 16 * (w + CSW * mi) + 4 * q + i, col = 16 * nt + m;
-        acc[mi][nt][i] = (!GS && h0 != nullptr && row < g.p && col < g.r)
+        acc[mi][nt][i] = (GM == 0 && h0 != nullptr && row < g.p && col < g.r)
                              ? (float)h0[((size_t)bh * g.p + row) * g.r + col] : 0.0f;
       }
   // internal position of this lane's columns (half-split interleaves the halves)
@@ -171,16 +174,32 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
   for (int nt = 0; nt < NT; nt++) icol[nt] = 16 * nt + m < g.r ? inv_perm_rc(g, 16 * nt + m) : 0;
 
   const int nkc = chain_nk(g);  // chunks walked (carries past them are not written)
-  // chunks n0 .. n1-1: the whole walk, or a group none of whose chunks is the last
-  const int n0 = GS ? gi * g.G : 0;
-  const int n1 = GS ? (n0 + g.G < nkc ? n0 + g.G : nkc) : nkc;
+  // chunks n0 .. n1-1: the whole walk, or a group (for summaries, one none of
+  // whose chunks is the last)
+  const int n0 = GM ? gi * g.G : 0;
+  const int n1 = GM ? (n0 + g.G < nkc ? n0 + g.G : nkc) : nkc;
+  if (GM && n0 >= nkc) return;
   if (GS && n1 >= nkc) return;
-  if (GS || nkc > 1) store(fetch(n0), 0);
+  if constexpr (GM == 2) {
+    // the state entering the group, in the carry layout (internal column order)
+    const float* in = carry + ((size_t)bh * g.NK + n0) * pr;
+#pragma unroll
+    for (int mi = 0; mi < MTW; mi++)
+#pragma unroll
+      for (int nt = 0; nt < NT; nt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int row = 16 * (w + CSW * mi) + 4 * q + i;
+          acc[mi][nt][i] = row < g.p && 16 * nt + m < g.r ? in[(size_t)row * g.r + icol[nt]] : 0.0f;
+        }
+  }
+  if (GS || (GM == 2 ? n0 + 1 < nkc : nkc > 1)) store(fetch(n0), 0);
   __syncthreads();
   float dprod = 1.0f;  // GS: product of the group's chunk decays
   for (int nc = n0; nc < n1; nc++) {
-    // chunk nc+1 contributes U only if it is not the last (in a group it never is)
-    const bool more = GS ? nc + 1 < n1 : nc + 2 < nkc;
+    // chunk nc+1 contributes U only if it is not the last (in a summarized
+    // group it never is)
+    const bool more = GS ? nc + 1 < n1 : (nc + 2 < nkc && nc + 1 < n1);
     Pf pf;
     if (more) pf = fetch(nc + 1);
     float* out = carry + ((size_t)bh * g.NK + nc) * pr;

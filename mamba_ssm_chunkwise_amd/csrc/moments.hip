@@ -344,6 +344,33 @@ int check_launch() {
     if (_rc != 0) return _rc; \
   } while (0)
 
+// The states entering each group: per-group walks from a zero state (k_cscan
+// in its group-summary form, in parallel over the groups) and a scan over the
+// groups (k_gentry), into each group's first carry rows. Needs groups of two
+// chunks or more; returns MOMENTS_ENOTSUP when k_cscan does not cover the shape.
+template <int NT, int CK>
+int launch_group_entries(const Plan& P, const bf16* xhat, const bf16* bhat, const bf16* da, const bf16* h0,
+                         float* carry, float* dec, hipStream_t st) {
+  const Geo& g = P.g;
+  const int chains = g.b * g.h;
+  const size_t lds = LdsC<NT, CK>::total(P.PK);
+  if (g.G < 2 || g.NGR < 2 || P.PK > 16 * CSW * CMT || lds > kLdsLimit) return MOMENTS_ENOTSUP;
+  auto launch = [&](auto mtw_c) -> int {
+    constexpr int MTW = decltype(mtw_c)::value;
+    MOM_TRY(set_lds(k_cscan<NT, CK, MTW, 1>, lds));
+    ProfScope ps(KID_CSCAN, st);
+    hipLaunchKernelGGL((k_cscan<NT, CK, MTW, 1>), dim3(chains * g.NGR), dim3(CST), lds, st, g, P.PK, xhat, bhat,
+                       da, h0, carry, dec);
+    return check_launch();
+  };
+  MOM_TRY(P.PK <= 16 * CSW ? launch(IC<1>{}) : launch(IC<2>{}));
+  const size_t pr = (size_t)g.p * g.r;
+  ProfScope ps(KID_GENTRY, st);
+  hipLaunchKernelGGL(k_gentry, dim3(chains, (unsigned)((pr + NTH - 1) / NTH)), dim3(NTH), 0, st, g, h0, carry,
+                     (const float*)dec);
+  return check_launch();
+}
+
 // The carry pass: states entering every kernel chunk (carry) and chunk decays
 // (dec), into the workspace or the caller's saved-carry buffer.
 template <typename T, int NT, int CK>
@@ -352,9 +379,26 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   const Geo& g = P.g;
   const int chains = g.b * g.h;
   if constexpr (std::is_same<T, bf16>::value) {
+    const size_t lds = LdsC<NT, CK>::total(P.PK);
+    // with groups of two chunks or more: the states entering the groups, then
+    // every group walked from its entering state, in parallel over the groups
+    if (g.cstride == 1 && g.NK >= 1) {
+      const int rc = launch_group_entries<NT, CK>(P, xhat, bhat, da, h0, carry, dec, st);
+      if (rc != MOMENTS_ENOTSUP) {
+        MOM_TRY(rc);
+        auto launch = [&](auto mtw_c) -> int {
+          constexpr int MTW = decltype(mtw_c)::value;
+          MOM_TRY(set_lds(k_cscan<NT, CK, MTW, 2>, lds));
+          ProfScope ps(KID_CSCAN, st);
+          hipLaunchKernelGGL((k_cscan<NT, CK, MTW, 2>), dim3(chains * g.NGR), dim3(CST), lds, st, g, P.PK, xhat,
+                             bhat, da, h0, carry, dec);
+          return check_launch();
+        };
+        return P.PK <= 16 * CSW ? launch(IC<1>{}) : launch(IC<2>{});
+      }
+    }
     // one sequential walk per chain when there are enough chains to fill the
     // chip (or the chains are short); otherwise the chunk-parallel pair below
-    const size_t lds = LdsC<NT, CK>::total(P.PK);
     if (g.NK >= 1 && P.PK <= 16 * CSW * CMT && lds <= kLdsLimit && (chains >= 64 || g.NK <= 32)) {
       auto launch = [&](auto mtw_c) -> int {
         constexpr int MTW = decltype(mtw_c)::value;
@@ -387,34 +431,6 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
     MOM_TRY(check_launch());
   }
   return 0;
-}
-
-// The states entering each group (and only those) for a forward that carries
-// its state through each group: per-group walks from a zero state (k_cscan in
-// its group-summary form, in parallel over the groups) and a scan over the
-// groups (k_gentry). Needs groups of two chunks or more; returns
-// MOMENTS_ENOTSUP when k_cscan does not cover the shape.
-template <int NT, int CK>
-int launch_group_entries(const Plan& P, const bf16* xhat, const bf16* bhat, const bf16* da, const bf16* h0,
-                         float* carry, float* dec, hipStream_t st) {
-  const Geo& g = P.g;
-  const int chains = g.b * g.h;
-  const size_t lds = LdsC<NT, CK>::total(P.PK);
-  if (g.G < 2 || g.NGR < 2 || P.PK > 16 * CSW * CMT || lds > kLdsLimit) return MOMENTS_ENOTSUP;
-  auto launch = [&](auto mtw_c) -> int {
-    constexpr int MTW = decltype(mtw_c)::value;
-    MOM_TRY(set_lds(k_cscan<NT, CK, MTW, true>, lds));
-    ProfScope ps(KID_CSCAN, st);
-    hipLaunchKernelGGL((k_cscan<NT, CK, MTW, true>), dim3(chains * g.NGR), dim3(CST), lds, st, g, P.PK, xhat, bhat,
-                       da, h0, carry, dec);
-    return check_launch();
-  };
-  MOM_TRY(P.PK <= 16 * CSW ? launch(IC<1>{}) : launch(IC<2>{}));
-  const size_t pr = (size_t)g.p * g.r;
-  ProfScope ps(KID_GENTRY, st);
-  hipLaunchKernelGGL(k_gentry, dim3(chains, (unsigned)((pr + NTH - 1) / NTH)), dim3(NTH), 0, st, g, h0, carry,
-                     (const float*)dec);
-  return check_launch();
 }
 
 // saved != nullptr: also leave the carries and chunk decays in the caller's
