@@ -54,6 +54,11 @@ def algorithmic(w, ell, l=None):
         "k_scan": dict(flops=0, bytes=2 * carry_b),
         # one sequential walk per chain: inputs read once, carries written once
         "k_cscan": dict(flops=th * 2 * c * p * r, bytes=th * (c * p + c * r + 1) * e + carry_b),
+        # its group forms: summaries read the inputs (all but each chain's last
+        # group, counted whole here) and store almost nothing; the group walks
+        # read the inputs and write every carry
+        "k_cscan_sum": dict(flops=th * 2 * c * p * r, bytes=th * (c * p + c * r + 1) * e),
+        "k_cscan_grp": dict(flops=th * 2 * c * p * r, bytes=th * (c * p + c * r + 1) * e + carry_b),
         "step": dict(flops=th * (2 * states + 2 * gram + 2 * dw), bytes=fwd_b + bwd_b),
     }
 

@@ -37,12 +37,12 @@ constexpr size_t kLdsLimit = 160 * 1024;
 // ---- optional per-kernel event timing (moments_profile_*) -------------------
 enum KernelId {
   KID_CARRY, KID_SCAN, KID_FWD, KID_REDUCE, KID_BWD, KID_DSCAN, KID_FIX, KID_ZERO, KID_PREP, KID_GSCAN, KID_GFIX,
-  KID_CSCAN, KID_ROTSEG, KID_ROTCARRY, KID_ROTAPPLY, KID_PAIR, KID_GENTRY, KID_N
+  KID_CSCAN, KID_ROTSEG, KID_ROTCARRY, KID_ROTAPPLY, KID_PAIR, KID_GENTRY, KID_CSUM, KID_CGRP, KID_N
 };
 const char* const kKernelNames[KID_N] = {"k_carry", "k_scan",      "k_fwd",      "k_reduce", "k_bwd",  "k_dscan",
                                          "k_fix",   "k_zero_tail", "k_prep_dm1", "k_gscan",  "k_gfix",
                                          "k_cscan", "k_rot_seg",   "k_rot_carry", "k_rot_apply",
-                                         "k_pair",  "k_gentry"};
+                                         "k_pair",  "k_gentry",    "k_cscan_sum", "k_cscan_grp"};
 struct Prof {
   std::mutex mu;
   bool on = false;
@@ -358,7 +358,7 @@ int launch_group_entries(const Plan& P, const bf16* xhat, const bf16* bhat, cons
   auto launch = [&](auto mtw_c) -> int {
     constexpr int MTW = decltype(mtw_c)::value;
     MOM_TRY(set_lds(k_cscan<NT, CK, MTW, 1>, lds));
-    ProfScope ps(KID_CSCAN, st);
+    ProfScope ps(KID_CSUM, st);
     hipLaunchKernelGGL((k_cscan<NT, CK, MTW, 1>), dim3(chains * g.NGR), dim3(CST), lds, st, g, P.PK, xhat, bhat,
                        da, h0, carry, dec);
     return check_launch();
@@ -389,7 +389,7 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
         auto launch = [&](auto mtw_c) -> int {
           constexpr int MTW = decltype(mtw_c)::value;
           MOM_TRY(set_lds(k_cscan<NT, CK, MTW, 2>, lds));
-          ProfScope ps(KID_CSCAN, st);
+          ProfScope ps(KID_CGRP, st);
           hipLaunchKernelGGL((k_cscan<NT, CK, MTW, 2>), dim3(chains * g.NGR), dim3(CST), lds, st, g, P.PK, xhat,
                              bhat, da, h0, carry, dec);
           return check_launch();
