@@ -1,16 +1,18 @@
-// Boundary carries in one pass per (b,h) chain (bf16 inputs).
+// Boundary carries: one walk per (b,h) chain, or per group of its chunks
+// (bf16 inputs).
 //
 // Source: burn-mamba "backward.rs" source page, boundary_carries: the state
 // entering chunk n is h_-(0) = h0 and h_-(n+1) = dec_n h_-(n) + U_n, where
 // dec_n = exp(a_last) and U_n[p][col] = sum_{(j,c)} exp(a_last - a_j)
 // xhat[j,c,p] bhat[j,c,col] is the chunk's decay-to-chunk-end product.
 //
-// One workgroup walks one chain from the first chunk to the last. The state
-// rows stay in MFMA accumulators for the whole walk (wave w owns row tiles
-// w, w+4): per chunk the wave stores h_-(n), scales by dec_n and accumulates
-// U_n on MFMA. Each chunk's xhat and bhat are fetched one chunk ahead into
-// registers and stored to LDS in their global layouts ([(j,c)][p] and
-// [(j,c)][col]); transposing LDS reads build both MFMA operands from there.
+// One workgroup walks one chain from the first chunk to the last (or, in the
+// group forms below, one group of chunks). The state rows stay in MFMA
+// accumulators for the whole walk (wave w owns row tiles w, w+4): per chunk the
+// wave stores h_-(n), scales by dec_n and accumulates U_n on MFMA. Each chunk's
+// xhat and bhat are fetched one chunk ahead into registers and stored to LDS in
+// their global layouts ([(j,c)][p] and [(j,c)][col]); transposing LDS reads
+// build both MFMA operands from there.
 // The states are kept in the caller's column order and written to the
 // internal order on store.
 #pragma once
