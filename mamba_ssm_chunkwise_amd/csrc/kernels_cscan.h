@@ -49,6 +49,25 @@ __device__ __forceinline__ bf8 ld_kx_frag(const bf16* blk, int P, int ks, int x0
   return __builtin_bit_cast(bf8, v);
 }
 
+// 4x4 transpose within each quad of lanes: lane j's v[i] becomes lane i's
+// v[j] (two exchanges, lanes j ^ 2 then j ^ 1, through DPP quad permutes).
+__device__ __forceinline__ void quad_transpose(f4& v, int j) {
+  auto xch = [](float x, int ctrl) {
+    return __builtin_bit_cast(float, ctrl == 0x4E ? __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false)
+                                                  : __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  };
+  {  // 2x2 blocks: lanes 0-1 registers 2-3 <-> lanes 2-3 registers 0-1
+    const bool hi = j & 2;
+    const float r0 = xch(hi ? v[0] : v[2], 0x4E), r1 = xch(hi ? v[1] : v[3], 0x4E);
+    if (hi) { v[0] = r0; v[1] = r1; } else { v[2] = r0; v[3] = r1; }
+  }
+  {  // within each 2x2 block
+    const bool od = j & 1;
+    const float r0 = xch(od ? v[0] : v[1], 0xB1), r1 = xch(od ? v[2] : v[3], 0xB1);
+    if (od) { v[0] = r0; v[2] = r1; } else { v[1] = r0; v[3] = r1; }
+  }
+}
+
 // MTW: row tiles per wave (1: state rows <= 64, 2: <= 128).
 // GM: 0 walks each chain from h0 and stores every carry. 1 (group summaries):
 // workgroup (chain, group gi) walks the group's G chunks from a zero state and
@@ -170,6 +189,9 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
         acc[mi][nt][i] = (GM == 0 && h0 != nullptr && row < g.p && col < g.r)
                              ? (float)h0[((size_t)bh * g.p + row) * g.r + col] : 0.0f;
       }
+  // 16-byte stores of four consecutive columns when the internal column order
+  // is the caller's and the rows hold whole column tiles
+  const bool vec_store = !g.half && g.r % 16 == 0;
   // internal position of this lane's columns (half-split interleaves the halves)
   int icol[NT];
 #pragma unroll
@@ -209,6 +231,19 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
     for (int mi = 0; mi < MTW; mi++) {
       const int mt = w + CSW * mi;
       if (GS || mt >= MT || nc % g.cstride != 0) break;
+      if (vec_store) {
+        // after a quad transpose lane (q, m) holds columns 16nt + 4(m / 4) ..
+        // + 3 of row 16mt + 4q + m % 4: one 16-byte store per tile
+        const int row = 16 * mt + 4 * q + (m & 3);
+#pragma unroll
+        for (int nt = 0; nt < NT; nt++) {
+          f4 v = acc[mi][nt];
+          quad_transpose(v, m & 3);
+          if (row < g.p && 16 * nt < g.r)
+            *reinterpret_cast<f4*>(out + (size_t)row * g.r + 16 * nt + 4 * (m >> 2)) = v;
+        }
+        continue;
+      }
 #pragma unroll
       for (int nt = 0; nt < NT; nt++) {
         if (16 * nt + m >= g.r) continue;
