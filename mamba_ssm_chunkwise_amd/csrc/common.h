@@ -162,6 +162,9 @@ struct Geo {
   int cstride;      // the carry pass stores the state entering chunk n only for n % cstride == 0
                     // (1: every chunk; a forward that carries its state through each group of
                     // cstride chunks reads only the states entering the groups)
+  int cnb;          // chunk staging buffers of the carry walk: 2 (the next chunk is staged
+                    // while the current one is read), or 1 (one barrier more per chunk, half
+                    // the LDS, so that two workgroups share a CU)
 };
 
 // Kernel chunks a sequence walks: all NK, or with `skip` only those holding a

@@ -32,10 +32,11 @@ __host__ __device__ __forceinline__ int cscan_xp(int PK) { return PK + (((PK >> 
 template <int NT, int CK>
 struct LdsC {
   static constexpr int R = 16 * NT, K = ELL * CK, BP = R + 16;
-  __host__ __device__ static size_t xs(int) { return 0; }                                  // [2][K][XP]
-  __host__ __device__ static size_t bs(int PK) { return (size_t)2 * K * cscan_xp(PK) * 2; }  // [2][K][BP]
-  __host__ __device__ static size_t wv(int PK) { return bs(PK) + (size_t)2 * K * BP * 2; }  // [2][ELL+1]
-  __host__ __device__ static size_t total(int PK) { return wv(PK) + (size_t)2 * (ELL + 4) * 4; }
+  // nb staging buffers (Geo::cnb)
+  __host__ __device__ static size_t xs(int, int) { return 0; }                                     // [nb][K][XP]
+  __host__ __device__ static size_t bs(int PK, int nb) { return (size_t)nb * K * cscan_xp(PK) * 2; }  // [nb][K][BP]
+  __host__ __device__ static size_t wv(int PK, int nb) { return bs(PK, nb) + (size_t)nb * K * BP * 2; }  // [nb][ELL+4]
+  __host__ __device__ static size_t total(int PK, int nb) { return wv(PK, nb) + (size_t)nb * (ELL + 4) * 4; }
 };
 
 // Operand over K-step ks of a [(j,c)][x] block (pitch P): lane (q, m) gets x =
@@ -77,6 +78,9 @@ __device__ __forceinline__ void quad_transpose(f4& v, int j) {
 // states entering the groups, and the last group of a chain returns at once.
 // 2 (group carries): each group is walked from the state k_gentry left in its
 // first chunk's carry rows, storing every carry and decay of the group.
+// Staging: chunk nc+1's inputs are loaded during chunk nc's work and go into
+// the other of two LDS buffers, or (Geo::cnb = 1) into the one buffer once
+// every wave has read chunk nc from it.
 template <int NT, int CK, int MTW, int GM = 0>
 __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __restrict__ xhat,
                                                const bf16* __restrict__ bhat, const bf16* __restrict__ da,
@@ -88,9 +92,10 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
   using L = LdsC<NT, CK>;
   const int XP = cscan_xp(PK);
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16* xs = (bf16*)(smem + L::xs(PK));
-  bf16* bs = (bf16*)(smem + L::bs(PK));
-  float* wv = (float*)(smem + L::wv(PK));  // per buffer: exp(a_last - a_j), j < ELL; then dec
+  bf16* xs = (bf16*)(smem + L::xs(PK, g.cnb));
+  bf16* bs = (bf16*)(smem + L::bs(PK, g.cnb));
+  float* wv = (float*)(smem + L::wv(PK, g.cnb));  // per buffer: exp(a_last - a_j), j < ELL; then dec
+  const int bmask = g.cnb - 1;                   // buffer of the chunk nc: (nc - n0) & bmask
 
   constexpr bool GS = GM == 1;  // group summaries
   const int bh = GM ? blockIdx.x / g.NGR : blockIdx.x, bi = bh / g.h, hi = bh % g.h;
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
       }
     }
     if (GS || nc + 1 < nkc) {
-      const int b = (nc - n0) & 1;
+      const int b = (nc - n0) & bmask;
       const float* wb = wv + b * (ELL + 4);
       const float dn = wb[ELL];
       if (GS) dprod *= dn;
@@ -286,7 +291,9 @@ __global__ __launch_bounds__(CST, 2) void k_cscan(Geo g, int PK, const bf16* __r
         }
       }
     }
-    if (more) store(pf, (nc + 1 - n0) & 1);
+    // one buffer: every wave is done reading it before the next chunk goes in
+    if (bmask == 0 && more) __syncthreads();
+    if (more) store(pf, (nc + 1 - n0) & bmask);
     __syncthreads();
   }
   if constexpr (GS) {

@@ -33,6 +33,7 @@ namespace {
 std::atomic<int> g_last_hip{0};
 
 constexpr size_t kLdsLimit = 160 * 1024;
+constexpr long kCUs = 256;  // compute units of the part (MI355X)
 
 // ---- optional per-kernel event timing (moments_profile_*) -------------------
 enum KernelId {
@@ -223,6 +224,7 @@ int make_plan(const moments_desc* d, Plan* P) {
   g.V = (int)(d->valid_len < d->s ? d->valid_len : d->s);
   g.NK = (g.V + ELL - 1) / ELL;
   g.cstride = 1;
+  g.cnb = 2;
   P->bf = bf;
   P->CK = g.c <= 1 ? 1 : g.c <= 2 ? 2 : 4;
   g.K = ELL * P->CK;
@@ -344,6 +346,18 @@ int check_launch() {
     if (_rc != 0) return _rc; \
   } while (0)
 
+// The carry walk's group forms with `grid` workgroups: one staging buffer when
+// that lets two workgroups share a CU where two double-buffered ones would not
+// fit, and the grid has more workgroups than one per CU (the long-context shape:
+// 148 KB double-buffered, 74 KB single).
+template <int NT, int CK>
+Geo cscan_geo(const Plan& P, long grid) {
+  Geo g = P.g;
+  const size_t l2 = LdsC<NT, CK>::total(P.PK, 2), l1 = LdsC<NT, CK>::total(P.PK, 1);
+  g.cnb = (2 * l2 > kLdsLimit && 2 * l1 <= kLdsLimit && grid > kCUs) ? 1 : 2;
+  return g;
+}
+
 // The states entering each group: per-group walks from a zero state (k_cscan
 // in its group-summary form, in parallel over the groups) and a scan over the
 // groups (k_gentry), into each group's first carry rows. Needs groups of two
@@ -351,9 +365,9 @@ int check_launch() {
 template <int NT, int CK>
 int launch_group_entries(const Plan& P, const bf16* xhat, const bf16* bhat, const bf16* da, const bf16* h0,
                          float* carry, float* dec, hipStream_t st) {
-  const Geo& g = P.g;
-  const int chains = g.b * g.h;
-  const size_t lds = LdsC<NT, CK>::total(P.PK);
+  const int chains = P.g.b * P.g.h;
+  const Geo g = cscan_geo<NT, CK>(P, (long)chains * P.g.NGR);
+  const size_t lds = LdsC<NT, CK>::total(P.PK, g.cnb);
   if (g.G < 2 || g.NGR < 2 || P.PK > 16 * CSW * CMT || lds > kLdsLimit) return MOMENTS_ENOTSUP;
   auto launch = [&](auto mtw_c) -> int {
     constexpr int MTW = decltype(mtw_c)::value;
@@ -379,18 +393,20 @@ int launch_carry_scan(const Plan& P, const T* xhat, const T* bhat, const T* da, 
   const Geo& g = P.g;
   const int chains = g.b * g.h;
   if constexpr (std::is_same<T, bf16>::value) {
-    const size_t lds = LdsC<NT, CK>::total(P.PK);
+    const size_t lds = LdsC<NT, CK>::total(P.PK, g.cnb);
     // with groups of two chunks or more: the states entering the groups, then
     // every group walked from its entering state, in parallel over the groups
     if (g.cstride == 1 && g.NK >= 1) {
       const int rc = launch_group_entries<NT, CK>(P, xhat, bhat, da, h0, carry, dec, st);
       if (rc != MOMENTS_ENOTSUP) {
         MOM_TRY(rc);
+        const Geo gg = cscan_geo<NT, CK>(P, (long)chains * g.NGR);
+        const size_t lg = LdsC<NT, CK>::total(P.PK, gg.cnb);
         auto launch = [&](auto mtw_c) -> int {
           constexpr int MTW = decltype(mtw_c)::value;
-          MOM_TRY(set_lds(k_cscan<NT, CK, MTW, 2>, lds));
+          MOM_TRY(set_lds(k_cscan<NT, CK, MTW, 2>, lg));
           ProfScope ps(KID_CGRP, st);
-          hipLaunchKernelGGL((k_cscan<NT, CK, MTW, 2>), dim3(chains * g.NGR), dim3(CST), lds, st, g, P.PK, xhat,
+          hipLaunchKernelGGL((k_cscan<NT, CK, MTW, 2>), dim3(chains * g.NGR), dim3(CST), lg, st, gg, P.PK, xhat,
                              bhat, da, h0, carry, dec);
           return check_launch();
         };

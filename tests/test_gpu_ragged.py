@@ -106,6 +106,10 @@ CASES = [
     # group from the group-entry states its carry pass stores; one sequence ends mid-group
     (_small("rg_bf16_quat_grouped", "bf16", W.ROT_QUAT, b=2, h=8, c=2, p=16, r=32, quat_blocks=8, s=2048,
             valid_len=2048, chunk_len=64), [1500, 2048], [0, 7]),
+    # four channels and 128 columns over 512 group workgroups: the carry walk's group forms
+    # stage each chunk in one LDS buffer, so that two workgroups share a CU
+    (_small("rg_bf16_quat_c4_grouped", "bf16", W.ROT_QUAT, b=2, h=8, c=4, p=32, r=128, quat_blocks=32,
+            s=2048, valid_len=2048, chunk_len=64), [2048, 1200], [0, 7]),
 ]
 
 
